@@ -1,0 +1,218 @@
+/*
+ * mla.h -- C ABI of an MI355X (gfx950) library for Multi-head Latent Attention
+ * (MLA) decode with weight absorption.
+ *
+ * One decode step over a compressed latent cache is four calls:
+ *
+ *   mla_cache_append  write the new tokens' latent c_kv and rotated RoPE key
+ *                     k_pe into the cache (contiguous or 64-token pages; an
+ *                     FP4 latent cache is quantised on the way in)
+ *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
+ *   mla_decode_attn   scores q_lat.c + q_pe.k_pe, scale, causal mask, softmax,
+ *                     latent-weighted sum x (split over the tokens when that
+ *                     helps, merged with a log-sum-exp combine)
+ *   mla_up_proj_v     out = W_UV x per head
+ *
+ * Sources of the operations: the "MLA decode step" exercise page (6547.cn):
+ * the prose on the two score streams, scaling, masking and the low-rank
+ * result, and the five steps of mla_decode_step with its shape comments; the
+ * DeepSeek-V3 architecture deep-dive page (neuronix): absorption of W_UK on
+ * the query side (comment in forward_inference) and the latent/RoPE slot pool
+ * (LatentKVCachePool::allocate_slot); the "hands-on MLA projection
+ * absorption" page: the CacheCompressed form storing compressed_kv split as
+ * [kv_lora_rank | qk_rope_head_dim]; the DeepSeek-V4.1-Flash MLA course page,
+ * block 4A: a 512-dim FP4 latent with E4M3 scales per 16 channels, 288 B per
+ * entry.
+ *
+ * Conventions shared by every call
+ *  - Shapes are row-major. B = dims.batch, H = dims.heads, Q = dims.q_len
+ *    (new tokens per sequence), Dn = d_nope, Dr = d_rope, Vd = d_v,
+ *    Ckv = d_latent. A query row is (h, q) with q fastest.
+ *  - wkv_b is [H, Dn+Vd, Ckv]: for head h, rows 0..Dn-1 are W_UK[h] and rows
+ *    Dn..Dn+Vd-1 are W_UV[h] (layout of the exercise page).
+ *  - Every pointer argument is a DEVICE pointer unless said otherwise, and
+ *    16-byte aligned. The caller owns all memory, including the workspace;
+ *    the library never allocates or frees device memory and keeps no state
+ *    besides a per-device cache of the compute-unit count.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work; no call synchronises the host. Buffers must stay valid until the
+ *    stream has finished the work.
+ *  - Every call returns MLA_OK or a negative status. Arguments are checked on
+ *    the host before anything is enqueued; on an error nothing is enqueued.
+ *    Device-resident data (seq_lens, page tables) cannot be checked on the
+ *    host: kernels clamp lengths to the cache capacity and treat a page index
+ *    outside the cache as an error of that sequence (its outputs become NaN)
+ *    instead of reading out of bounds.
+ *  - Supported shapes: Dn = 128, Dr = 64, Vd = 128, Ckv = 512 for the bf16 /
+ *    FP4 paths; any positive sizes for the fp32 path (d_latent and d_rope
+ *    multiples of 4). H*Q <= 1024, Q <= 16 for the attention call.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_API __attribute__((visibility("default")))
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1) /* null pointer, misalignment, non-positive size */
+#define MLA_ERR_UNSUPPORTED (-2) /* shape / dtype combination this library does not run */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define MLA_ERR_HIP (-4)         /* a HIP runtime call or launch failed */
+
+/* Element types. */
+#define MLA_F32 0
+#define MLA_BF16 1
+#define MLA_FP4_E2M1_E4M3X16 2 /* latent only: 4-bit E2M1 codes + one E4M3 scale per 16 channels */
+
+typedef struct mla_dims {
+  int32_t batch;    /* B */
+  int32_t heads;    /* H */
+  int32_t q_len;    /* Q: new tokens per sequence (decode: 1; multi-token: 2..) */
+  int32_t d_nope;   /* Dn: non-RoPE query/key width per head */
+  int32_t d_rope;   /* Dr: decoupled RoPE width (shared key) */
+  int32_t d_v;      /* Vd: value width per head */
+  int32_t d_latent; /* Ckv: compressed latent width */
+} mla_dims;
+
+/*
+ * Latent cache descriptor. The cache holds one row per token, shared by all
+ * heads: Ckv latent channels and Dr RoPE channels (the RoPE key is stored
+ * already rotated). Physical row r of the cache lives at
+ *     latent + r*latent_stride, rope + r*rope_stride (+ latent_scale +
+ *     r*scale_stride for FP4),
+ * strides in bytes. A combined [latent | rope] row (the CacheCompressed
+ * layout) is rope = latent + Ckv*sizeof(elem) with equal strides.
+ *
+ * Logical token t of sequence b maps to physical row
+ *     contiguous (page_size == 0):  b*capacity + t
+ *     paged (page_size == 64):      page_table[b*page_table_stride + t/64]*64 + t%64
+ * (the slot arithmetic of the latent slot pool on the deep-dive page, with
+ * pages). `capacity` is the most tokens a sequence may hold; num_rows is the
+ * number of physical rows the buffers hold.
+ *
+ * FP4 latent rows: byte i of a row holds channel 2i in its low nibble and
+ * channel 2i+1 in its high nibble (E2M1: sign, 2 exponent bits, 1 mantissa
+ * bit); the scale row holds Ckv/16 E4M3 ("FN") bytes in channel-group order.
+ */
+typedef struct mla_kv_cache {
+  int32_t latent_dtype; /* MLA_F32, MLA_BF16 or MLA_FP4_E2M1_E4M3X16 */
+  int32_t rope_dtype;   /* MLA_F32 or MLA_BF16 */
+  void* latent;
+  void* latent_scale; /* FP4 only, else NULL */
+  void* rope;
+  int64_t latent_stride;
+  int64_t scale_stride;
+  int64_t rope_stride;
+  int64_t num_rows;
+  int32_t page_size; /* 0 or 64 */
+  int32_t capacity;
+  const int32_t* page_table; /* paged only: device int32 [B, page_table_stride] */
+  int32_t page_table_stride;
+  int32_t reserved;
+} mla_kv_cache;
+
+/* Optional tuning of mla_decode_attn; pass NULL for the library's choice. */
+typedef struct mla_decode_opts {
+  /* Workgroups that share the token axis of one block of 128 query rows.
+   * 0 = chosen from the compute-unit count. The tokens of all sequences are
+   * dealt to them in equal contiguous runs of 64-token tiles. */
+  int32_t workgroups;
+  int32_t reserved[3];
+} mla_decode_opts;
+
+/*
+ * mla_absorb_q -- q_lat[b,h,q,:] = sum_d q_nope[b,h,q,d] * W_UK[h,d,:].
+ * Absorbs W_UK into the query so scores are taken against the latent
+ * directly (deep-dive page, forward_inference comment; exercise page step 1).
+ *   dtype   MLA_F32 (all fp32) or MLA_BF16 (bf16 in/out, fp32 accumulation)
+ *   q_nope  [B, H, Q, Dn]
+ *   wkv_b   [H, Dn+Vd, Ckv]
+ *   q_lat   [B, H, Q, Ckv] output
+ */
+MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope,
+                         const void* wkv_b, void* q_lat, void* stream);
+
+/*
+ * Bytes of workspace mla_decode_attn needs for these arguments on the
+ * current device (0 if none). Returns 0 and sets *bytes on success.
+ */
+MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32_t max_seq_len,
+                                      const mla_decode_opts* opts, size_t* bytes);
+
+/*
+ * mla_decode_attn -- absorbed attention over the latent cache (exercise page
+ * prose and steps 2-4 and the x einsum; the two score streams of the
+ * deep-dive comment).
+ *   For query row (b, h, q) with L = seq_lens[b] (cache length including the
+ *   Q new tokens), the visible positions are t = 0 .. L-Q+q and
+ *     s_t   = softmax_scale * (q_lat[b,h,q,:] . c_t + q_pe[b,h,q,:] . k_pe_t)
+ *     x     = sum_t softmax(s)_t * c_t          -> x_lat[b,h,q,:]
+ *     lse   = log sum_t exp(s_t) (natural log)  -> lse[b,h,q]
+ *   A row with no visible position gets x = 0 and lse = -inf.
+ *   dtype        MLA_F32: q_lat/q_pe/x_lat fp32, cache latent and rope fp32.
+ *                MLA_BF16: q_lat/q_pe/x_lat bf16, cache latent bf16 or FP4,
+ *                rope bf16; products on bf16 matrix cores, fp32 accumulation,
+ *                probabilities rounded to bf16 before the weighted sum.
+ *   q_lat        [B, H, Q, Ckv];  q_pe [B, H, Q, Dr]
+ *   seq_lens     device int32 [B]
+ *   max_seq_len  host upper bound of seq_lens (sizes the token split)
+ *   x_lat        [B, H, Q, Ckv] output;  lse: float [B, H, Q] output or NULL
+ *   workspace    device scratch of mla_decode_workspace_size() bytes (its
+ *                contents need no initialisation and are not preserved)
+ */
+MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat,
+                            const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
+                            int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
+                            void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
+                            void* stream);
+
+/*
+ * mla_up_proj_v -- out[b,h,q,v] = sum_c W_UV[h,v,c] * x_lat[b,h,q,c]
+ * (exercise page step 5: map the latent result back to each head's values).
+ *   dtype  MLA_F32 or MLA_BF16 (bf16 in/out, fp32 accumulation)
+ *   x_lat  [B, H, Q, Ckv];  wkv_b [H, Dn+Vd, Ckv];  out [B, H, Q, Vd]
+ */
+MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat,
+                          const void* wkv_b, void* out, void* stream);
+
+/*
+ * mla_cache_append -- store the Q new tokens of every sequence.
+ *   Token j (0 <= j < Q) of sequence b goes to logical position
+ *   seq_lens[b] - Q + j (seq_lens counts the new tokens); positions outside
+ *   [0, capacity) are skipped. (Deep-dive page: compress the current token
+ *   and store it; slot address = token position times the row width.)
+ *   src_dtype  dtype of c_kv_new: MLA_F32 or MLA_BF16. It must equal the
+ *              latent dtype of an fp32/bf16 cache; an FP4 cache quantises it
+ *              (scale = E4M3 round-to-nearest-even of fp32(amax/6) per 16
+ *              channels, element = nearest E2M1 value of x/scale, ties to the
+ *              even code, saturating; scale 0 -> all-zero codes).
+ *   c_kv_new   [B, Q, Ckv];  k_pe_new [B, Q, Dr] in the cache's rope dtype
+ */
+MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
+                             const void* k_pe_new, const mla_kv_cache* cache,
+                             const int32_t* seq_lens, void* stream);
+
+/*
+ * mla_dequant_rows -- inspection aid: the latent of `n` physical cache rows
+ * (device int32 rows[n]) as fp32 [n, Ckv], decoded by the same device code
+ * the attention kernel uses (FP4: E2M1 value times E4M3 scale; bf16/fp32:
+ * widened). Lets a caller check the stored cache bit for bit.
+ */
+MLA_API int mla_dequant_rows(const mla_kv_cache* cache, int32_t d_latent, const int32_t* rows,
+                             int32_t n, float* out, void* stream);
+
+/* Static description of a status code. */
+MLA_API const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

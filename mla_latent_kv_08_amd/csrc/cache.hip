@@ -1,0 +1,120 @@
+// Latent cache writes and reads outside the attention kernel.
+//
+// Append: the Q new tokens of each sequence go to logical positions
+// len-Q .. len-1, through the page table when the cache is paged (DeepSeek-V3
+// deep-dive page: compress the current token, store it in the latent/RoPE
+// slot pool at token_pos times the row width; here with bounds checks).
+// An FP4 latent cache is quantised on the way in: per 16 channels an E4M3
+// scale = RNE(fp32(amax / 6)), each channel the nearest E2M1 value of x/scale
+// with ties to the even code (DeepSeek-V4.1-Flash course page, block 4A: FP4
+// latent with an E4M3 scale per 16 channels).
+#include "internal.h"
+#include "mla.h"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ float load_src(const void* base, int64_t idx, int dtype) {
+  if (dtype == MLA_F32) return reinterpret_cast<const float*>(base)[idx];
+  return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+
+// grid (B * Qn); one 64-lane wave per new token.
+__global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / p.Qn;
+  const int j = blockIdx.x % p.Qn;
+  const int len = p.seq_lens[b];
+  const int pos = len - p.Qn + j;
+  if (pos < 0 || pos >= p.cache.capacity) return;
+  bool bad = false;
+  const int64_t r = phys_row(p.cache, b, pos, bad);
+  if (bad) return;
+  const int64_t src_row = (int64_t)b * p.Qn + j;
+  const CacheView& c = p.cache;
+
+  // RoPE part: same dtype in and out.
+  const int rb = p.rope_dtype == MLA_F32 ? 4 : 2;
+  {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.k_pe) + src_row * p.Dr * rb;
+    uint8_t* dst = const_cast<uint8_t*>(c.rope) + r * c.rope_stride;
+    for (int i = lane * 4; i < p.Dr * rb; i += 64 * 4) {
+      *reinterpret_cast<uint32_t*>(dst + i) = *reinterpret_cast<const uint32_t*>(src + i);
+    }
+  }
+
+  uint8_t* lat = const_cast<uint8_t*>(c.latent) + r * c.latent_stride;
+  if (p.latent_dtype != MLA_FP4_E2M1_E4M3X16) {
+    const int eb = p.latent_dtype == MLA_F32 ? 4 : 2;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.c_kv) + src_row * p.Ckv * eb;
+    for (int i = lane * 4; i < p.Ckv * eb; i += 64 * 4) {
+      *reinterpret_cast<uint32_t*>(lat + i) = *reinterpret_cast<const uint32_t*>(src + i);
+    }
+    return;
+  }
+
+  // FP4: a pair of lanes per 16-channel group, 8 channels per lane.
+  uint8_t* scl = const_cast<uint8_t*>(c.scale) + r * c.scale_stride;
+  for (int c0 = lane * 8; c0 < p.Ckv; c0 += 64 * 8) {
+    float v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = load_src(p.c_kv, src_row * p.Ckv + c0 + e, p.src_dtype);
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    const uint32_t sc = e4m3_encode_rne(__fdiv_rn(amax, 6.0f));  // correctly rounded fp32 division
+    const float s = e4m3_to_f32(sc);
+    uint32_t word = 0;
+    if (s > 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= e2m1_encode(v[e], s) << (4 * e);
+    }
+    *reinterpret_cast<uint32_t*>(lat + c0 / 2) = word;
+    if ((lane & 1) == 0) scl[c0 / 16] = (uint8_t)sc;
+  }
+}
+
+// grid (n); latent of physical row rows[i] as fp32.
+__global__ void __launch_bounds__(256) dequant_kernel(CacheView c, int latent_dtype, int Ckv,
+                                                      const int32_t* rows, float* out) {
+  const int i = blockIdx.x;
+  const int64_t r = rows[i];
+  const bool ok = r >= 0 && r < c.num_rows;
+  const uint8_t* lat = c.latent + (ok ? r : 0) * c.latent_stride;
+  for (int ch = threadIdx.x; ch < Ckv; ch += 256) {
+    float v;
+    if (!ok) {
+      v = __uint_as_float(0x7fc00000u);
+    } else if (latent_dtype == MLA_F32) {
+      v = reinterpret_cast<const float*>(lat)[ch];
+    } else if (latent_dtype == MLA_BF16) {
+      v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(lat)[ch]);
+    } else {
+      const uint32_t byte = lat[ch >> 1];
+      const uint32_t code = (ch & 1) ? (byte >> 4) : (byte & 0xfu);
+      const float s = e4m3_to_f32(c.scale[(ok ? r : 0) * c.scale_stride + (ch >> 4)]);
+      v = __uint_as_float(e2m1_f32_bits(code)) * s;
+    }
+    out[(int64_t)i * Ckv + ch] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.B * p.Qn;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)n), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const CacheView& c, int latent_dtype, int Ckv, const int32_t* rows,
+                               int n, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_kernel, dim3(n), dim3(256), 0, s, c, latent_dtype, Ckv, rows, out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

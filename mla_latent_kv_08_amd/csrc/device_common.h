@@ -1,0 +1,141 @@
+// Device-side helpers shared by the MLA decode kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 latent codec: E2M1 codes with one E4M3 ("FN") scale per 16 channels.
+// ---------------------------------------------------------------------------
+
+// fp32 bit pattern of an E2M1 code: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ uint32_t e2m1_f32_bits(uint32_t code) {
+  const uint32_t k = code & 7u;
+  uint32_t mag;
+  if (k < 2u) {
+    mag = k ? 0x3f000000u : 0u;  // 0.5 or 0
+  } else {
+    mag = (((k >> 1) + 126u) << 23) | ((k & 1u) << 22);
+  }
+  return mag | ((code & 8u) << 28);
+}
+
+// Value of an E4M3 ("FN") byte.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 0xfu;
+  const uint32_t m = byte & 7u;
+  float v;
+  if (e == 0u) {
+    v = (float)m * 0.001953125f;  // m * 2^-9
+  } else if (e == 15u && m == 7u) {
+    v = __uint_as_float(0x7fc00000u);
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return (byte & 0x80u) ? -v : v;
+}
+
+// E4M3 code nearest to r >= 0 (fp32), ties to the even code, saturating to 448.
+__device__ __forceinline__ uint32_t e4m3_encode_rne(float r) {
+  if (!(r < 448.0f)) return 0x7eu;  // also catches +inf
+  const uint32_t bits = __float_as_uint(r);
+  const int e = (int)((bits >> 23) & 0xffu) - 127;
+  if (e < -6) {
+    // Subnormal E4M3 range: multiples of 2^-9; 8 * 2^-9 is the smallest normal.
+    return (uint32_t)__builtin_rintf(r * 512.0f);
+  }
+  uint32_t keep = (bits >> 20) & 7u;
+  const uint32_t rem = bits & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep += 1u;
+  uint32_t E = (uint32_t)(e + 7);
+  if (keep == 8u) {
+    keep = 0u;
+    E += 1u;
+  }
+  uint32_t code = (E << 3) | keep;
+  return code > 0x7eu ? 0x7eu : code;
+}
+
+// E2M1 code of x under scale s > 0: nearest magnitude to |x|/s with ties to
+// the even code. Thresholds s*midpoint are exact in fp32, so comparing |x|
+// with them decides the real-valued rounding exactly.
+__device__ __forceinline__ uint32_t e2m1_encode(float x, float s) {
+  const float ax = fabsf(x);
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t k = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float t = s * mids[j];
+    k += (ax > t) ? 1u : 0u;
+  }
+  // A tie sits exactly on midpoint k (between codes k and k+1): choose the even one.
+  if (k < 7u) {
+    const float t = s * (k == 0 ? 0.25f : k == 1 ? 0.75f : k == 2 ? 1.25f : k == 3 ? 1.75f
+                          : k == 4 ? 2.5f : k == 5 ? 3.5f : 5.0f);
+    if (ax == t && (k & 1u)) k += 1u;
+  }
+  if (k == 0u) return 0u;
+  return k | ((x < 0.0f) ? 8u : 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Cache addressing
+// ---------------------------------------------------------------------------
+struct CacheView {
+  const uint8_t* latent;
+  const uint8_t* scale;
+  const uint8_t* rope;
+  int64_t latent_stride;
+  int64_t scale_stride;
+  int64_t rope_stride;
+  int64_t num_rows;
+  const int32_t* page_table;
+  int32_t page_size;  // 0 or 64
+  int32_t capacity;
+  int32_t pt_stride;
+};
+
+// Sequence length clamped to what the cache can hold.
+__device__ __forceinline__ int clamp_len(int len, int capacity) {
+  return len < 0 ? 0 : (len > capacity ? capacity : len);
+}
+
+// Physical row of logical token t of sequence b; sets bad (and returns 0)
+// when a page index points outside the cache.
+__device__ __forceinline__ int64_t phys_row(const CacheView& c, int b, int t, bool& bad) {
+  if (c.page_size == 0) return (int64_t)b * c.capacity + t;
+  const int page = c.page_table[(int64_t)b * c.pt_stride + (t >> 6)];
+  const int64_t r = (int64_t)page * 64 + (t & 63);
+  if (page < 0 || r >= c.num_rows) {
+    bad = true;
+    return 0;
+  }
+  return r;
+}
+
+}  // namespace mla

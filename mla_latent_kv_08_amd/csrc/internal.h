@@ -1,0 +1,59 @@
+// Host-side declarations shared between the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace mla {
+
+// Rows of query (h, q) handled by one attention workgroup on the matrix-core path.
+constexpr int kRowsPerGroup = 128;
+constexpr int kTileTokens = 64;
+
+struct AttnParams {
+  const void* q_lat;  // [B, HQ, Ckv]
+  const void* q_pe;   // [B, HQ, Dr]
+  CacheView cache;
+  const int32_t* seq_lens;
+  void* x_lat;   // [B, HQ, Ckv]
+  float* lse;    // [B, HQ] or null
+  float* part_x;    // [G, 2W, 128, Ckv] fp32 partial results
+  float* part_lse;  // [G, 2W, 128]
+  int B, H, Q, HQ, Ckv, Dr;
+  int groups;      // G = ceil(HQ / 128)
+  int workgroups;  // W per row group
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s);
+
+struct ProjParams {
+  const void* in;   // absorb: q_nope [B,H,Q,Dn]; up: x [B,H,Q,Ckv]
+  const void* w;    // wkv_b [H, Dn+Vd, Ckv]
+  void* out;        // absorb: q_lat [B,H,Q,Ckv]; up: out [B,H,Q,Vd]
+  int B, H, Q, Dn, Vd, Ckv;
+};
+
+hipError_t launch_absorb(const ProjParams& p, bool bf16, hipStream_t s);
+hipError_t launch_up_proj(const ProjParams& p, bool bf16, hipStream_t s);
+
+struct AppendParams {
+  const void* c_kv;  // [B, Qn, Ckv]
+  const void* k_pe;  // [B, Qn, Dr]
+  CacheView cache;
+  const int32_t* seq_lens;
+  int B, Qn, Ckv, Dr;
+  int src_dtype;     // MLA_F32 / MLA_BF16
+  int latent_dtype;  // cache latent dtype
+  int rope_dtype;
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_dequant_rows(const CacheView& c, int latent_dtype, int Ckv, const int32_t* rows,
+                               int n, float* out, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,308 @@
+// C ABI of the MLA decode library: argument checks, the token-split policy,
+// workspace sizing and kernel dispatch. Every check runs on the host before
+// any HIP call, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "internal.h"
+#include "mla.h"
+
+namespace {
+
+using mla::kRowsPerGroup;
+using mla::kTileTokens;
+
+constexpr int kMaxDevices = 64;
+
+int num_cus(int* out) {
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::call_once(once[dev], [dev]() {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+    cus[dev] = v;
+  });
+  if (cus[dev] <= 0) return MLA_ERR_HIP;
+  *out = cus[dev];
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const mla_dims* d) {
+  if (d == nullptr) return MLA_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->heads <= 0 || d->q_len <= 0 || d->d_nope <= 0 || d->d_rope <= 0 ||
+      d->d_v <= 0 || d->d_latent <= 0) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  return MLA_OK;
+}
+
+bool deepseek_dims(const mla_dims* d) {
+  return d->d_nope == 128 && d->d_rope == 64 && d->d_v == 128 && d->d_latent == 512;
+}
+
+int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t batch) {
+  if (c == nullptr || c->latent == nullptr || c->rope == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c->latent) || !aligned16(c->rope)) return MLA_ERR_INVALID_ARG;
+  if (c->latent_stride <= 0 || c->rope_stride <= 0 || (c->latent_stride & 15) ||
+      (c->rope_stride & 15)) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (c->capacity < 0 || c->num_rows < 0) return MLA_ERR_INVALID_ARG;
+  int64_t lat_bytes;
+  if (c->latent_dtype == MLA_F32) {
+    lat_bytes = (int64_t)d_latent * 4;
+  } else if (c->latent_dtype == MLA_BF16) {
+    lat_bytes = (int64_t)d_latent * 2;
+  } else if (c->latent_dtype == MLA_FP4_E2M1_E4M3X16) {
+    lat_bytes = d_latent / 2;
+    if (c->latent_scale == nullptr || c->scale_stride < d_latent / 16) return MLA_ERR_INVALID_ARG;
+    if (d_latent % 32) return MLA_ERR_UNSUPPORTED;
+  } else {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (c->rope_dtype != MLA_F32 && c->rope_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  const int64_t rope_bytes = (int64_t)d_rope * (c->rope_dtype == MLA_F32 ? 4 : 2);
+  if (c->latent_stride < lat_bytes || c->rope_stride < rope_bytes) return MLA_ERR_INVALID_ARG;
+  if (c->page_size == 0) {
+    if (c->page_table != nullptr) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)batch * c->capacity > c->num_rows) return MLA_ERR_INVALID_ARG;
+  } else if (c->page_size == kTileTokens) {
+    if (c->page_table == nullptr || c->page_table_stride <= 0) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)c->page_table_stride * kTileTokens < c->capacity) return MLA_ERR_INVALID_ARG;
+  } else {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  return MLA_OK;
+}
+
+mla::CacheView view_of(const mla_kv_cache* c) {
+  mla::CacheView v;
+  v.latent = static_cast<const uint8_t*>(c->latent);
+  v.scale = static_cast<const uint8_t*>(c->latent_scale);
+  v.rope = static_cast<const uint8_t*>(c->rope);
+  v.latent_stride = c->latent_stride;
+  v.scale_stride = c->scale_stride;
+  v.rope_stride = c->rope_stride;
+  v.num_rows = c->num_rows;
+  v.page_table = c->page_table;
+  v.page_size = c->page_size;
+  v.capacity = c->capacity;
+  v.pt_stride = c->page_table_stride;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Token-split policy of the matrix-core attention path: how many workgroups
+// share the tiles of one block of 128 query rows.
+int attn_workgroups(const mla_dims* d, int32_t max_seq_len, const mla_decode_opts* opts, int cus) {
+  const int64_t hq = (int64_t)d->heads * d->q_len;
+  const int groups = (int)((hq + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int64_t max_tiles = (int64_t)d->batch * ((std::max(max_seq_len, 0) + kTileTokens - 1) / kTileTokens);
+  if (opts != nullptr && opts->workgroups > 0) return opts->workgroups;
+  // One workgroup per compute unit over all row groups, but at least 4 tiles each.
+  int64_t w = std::max<int64_t>(1, cus / groups);
+  w = std::min<int64_t>(w, std::max<int64_t>(1, max_tiles / 4));
+  return (int)w;
+}
+
+int check_attn(const mla_dims* dims, int32_t dtype, const mla_kv_cache* cache, int32_t max_seq_len,
+               const mla_decode_opts* opts) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (max_seq_len < 0) return MLA_ERR_INVALID_ARG;
+  if (opts != nullptr && opts->workgroups < 0) return MLA_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)dims->heads * dims->q_len;
+  if (hq > 1024 || dims->q_len > 16) return MLA_ERR_UNSUPPORTED;
+  if (dtype == MLA_F32) {
+    if (dims->d_latent % 4 || dims->d_rope % 4 || dims->d_latent > 2048) return MLA_ERR_UNSUPPORTED;
+    if (cache != nullptr && (cache->latent_dtype != MLA_F32 || cache->rope_dtype != MLA_F32)) {
+      return MLA_ERR_UNSUPPORTED;
+    }
+  } else if (dtype == MLA_BF16) {
+    if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
+    if (cache != nullptr && ((cache->latent_dtype != MLA_BF16 &&
+                              cache->latent_dtype != MLA_FP4_E2M1_E4M3X16) ||
+                             cache->rope_dtype != MLA_BF16)) {
+      return MLA_ERR_UNSUPPORTED;
+    }
+  } else {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  return MLA_OK;
+}
+
+size_t attn_workspace_bytes(const mla_dims* d, int32_t dtype, int w) {
+  if (dtype != MLA_BF16) return 0;
+  const int64_t hq = (int64_t)d->heads * d->q_len;
+  const int64_t groups = (hq + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int64_t rows = groups * 2 * w * kRowsPerGroup;
+  return (size_t)(rows * d->d_latent * 4 + rows * 4 + 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+MLA_API const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b,
+                         void* q_lat, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (q_nope == nullptr || wkv_b == nullptr || q_lat == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
+  if (dtype == MLA_BF16) {
+    if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
+  } else if (dtype != MLA_F32) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return MLA_OK;
+  mla::ProjParams p{q_nope, wkv_b, q_lat, dims->batch, dims->heads, dims->q_len,
+                    dims->d_nope, dims->d_v, dims->d_latent};
+  return hip_status(mla::launch_absorb(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat, const void* wkv_b,
+                          void* out, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (x_lat == nullptr || wkv_b == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x_lat) || !aligned16(wkv_b) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (dtype == MLA_BF16) {
+    if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
+  } else if (dtype != MLA_F32) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return MLA_OK;
+  mla::ProjParams p{x_lat, wkv_b, out, dims->batch, dims->heads, dims->q_len,
+                    dims->d_nope, dims->d_v, dims->d_latent};
+  return hip_status(mla::launch_up_proj(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32_t max_seq_len,
+                                      const mla_decode_opts* opts, size_t* bytes) {
+  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+  int st = check_attn(dims, dtype, nullptr, max_seq_len, opts);
+  if (st) return st;
+  if (dtype != MLA_BF16) {
+    *bytes = 0;
+    return MLA_OK;
+  }
+  int cus = 0;
+  st = num_cus(&cus);
+  if (st) return st;
+  *bytes = attn_workspace_bytes(dims, dtype, attn_workgroups(dims, max_seq_len, opts, cus));
+  return MLA_OK;
+}
+
+MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+                            const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                            float softmax_scale, void* x_lat, float* lse, void* workspace,
+                            size_t workspace_bytes, const mla_decode_opts* opts, void* stream) {
+  int st = check_attn(dims, dtype, cache, max_seq_len, opts);
+  if (st) return st;
+  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
+  if (st) return st;
+  if (q_lat == nullptr || q_pe == nullptr || seq_lens == nullptr || x_lat == nullptr) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(x_lat)) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return MLA_OK;
+
+  mla::AttnParams p{};
+  p.q_lat = q_lat;
+  p.q_pe = q_pe;
+  p.cache = view_of(cache);
+  p.seq_lens = seq_lens;
+  p.x_lat = x_lat;
+  p.lse = lse;
+  p.B = dims->batch;
+  p.H = dims->heads;
+  p.Q = dims->q_len;
+  p.HQ = dims->heads * dims->q_len;
+  p.Ckv = dims->d_latent;
+  p.Dr = dims->d_rope;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MLA_F32) {
+    p.groups = 1;
+    p.workgroups = 1;
+    return hip_status(mla::launch_attn_f32(p, s));
+  }
+  int cus = 0;
+  st = num_cus(&cus);
+  if (st) return st;
+  const int w = attn_workgroups(dims, max_seq_len, opts, cus);
+  const size_t need = attn_workspace_bytes(dims, dtype, w);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  p.groups = (p.HQ + kRowsPerGroup - 1) / kRowsPerGroup;
+  p.workgroups = w;
+  const int64_t part_rows = (int64_t)p.groups * 2 * w * kRowsPerGroup;
+  p.part_x = static_cast<float*>(workspace);
+  p.part_lse = p.part_x + part_rows * p.Ckv;
+  return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, s));
+}
+
+MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
+                             const void* k_pe_new, const mla_kv_cache* cache,
+                             const int32_t* seq_lens, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
+  if (st) return st;
+  if (c_kv_new == nullptr || k_pe_new == nullptr || seq_lens == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c_kv_new) || !aligned16(k_pe_new)) return MLA_ERR_INVALID_ARG;
+  if (src_dtype != MLA_F32 && src_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (cache->latent_dtype == MLA_FP4_E2M1_E4M3X16) {
+    if (dims->d_latent != 512) return MLA_ERR_UNSUPPORTED;
+  } else if (cache->latent_dtype != src_dtype) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (dims->d_latent % 8 || dims->d_rope % 8) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)dims->batch * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return MLA_OK;
+  mla::AppendParams p{};
+  p.c_kv = c_kv_new;
+  p.k_pe = k_pe_new;
+  p.cache = view_of(cache);
+  p.seq_lens = seq_lens;
+  p.B = dims->batch;
+  p.Qn = dims->q_len;
+  p.Ckv = dims->d_latent;
+  p.Dr = dims->d_rope;
+  p.src_dtype = src_dtype;
+  p.latent_dtype = cache->latent_dtype;
+  p.rope_dtype = cache->rope_dtype;
+  return hip_status(mla::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+MLA_API int mla_dequant_rows(const mla_kv_cache* cache, int32_t d_latent, const int32_t* rows,
+                             int32_t n, float* out, void* stream) {
+  if (d_latent <= 0 || n < 0) return MLA_ERR_INVALID_ARG;
+  int st = check_cache(cache, d_latent, 1, 0);
+  if (st) return st;
+  if (rows == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  return hip_status(mla::launch_dequant_rows(view_of(cache), cache->latent_dtype, d_latent, rows, n,
+                                             out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -128,9 +128,9 @@ def decode_nonabsorbed(q_nope, q_pe, kv_rows: Sequence, pe_rows: Sequence, wkv_b
             t1 = min(n_all, t0 + token_block)
             c = _f64(kv_rows[b][t0:t1])  # [T, Ckv]
             kpe = _f64(pe_rows[b][t0:t1])  # [T, Dr]
-            k_nope = np.einsum("hdc,tc->htd", w_uk, c)  # [Hs, T, Dn]
-            s_nope = np.einsum("hqd,htd->hqt", qn_b, k_nope)
-            s_pe = np.einsum("hqr,tr->hqt", qp_b, kpe)
+            k_nope = np.matmul(w_uk, c.T)  # [Hs, Dn, T]: K_nope[t,h,:] = W_UK[h] c_t
+            s_nope = np.matmul(qn_b, k_nope)  # [Hs, Q, T]
+            s_pe = np.matmul(qp_b, kpe.T)  # [Hs, Q, T]
             scores[:, :, t0:t1] = softmax_scale * (s_nope + s_pe)
         # Softmax over each query's own visible prefix.
         p_full = np.zeros((Hs, Q, n_all))
@@ -148,10 +148,10 @@ def decode_nonabsorbed(q_nope, q_pe, kv_rows: Sequence, pe_rows: Sequence, wkv_b
         for t0 in range(0, n_all, token_block):
             t1 = min(n_all, t0 + token_block)
             c = _f64(kv_rows[b][t0:t1])
-            v = np.einsum("hvc,tc->htv", w_uv, c)  # [Hs, T, Vd]
-            pblk = p_full[:, :, t0:t1]
-            out[b] += np.einsum("hqt,htv->hqv", pblk, v)
-            x[b] += np.einsum("hqt,tc->hqc", pblk, c)
+            v = np.matmul(w_uv, c.T)  # [Hs, Vd, T]: V[t,h,:] = W_UV[h] c_t
+            pblk = p_full[:, :, t0:t1]  # [Hs, Q, T]
+            out[b] += np.matmul(pblk, v.transpose(0, 2, 1))
+            x[b] += np.matmul(pblk, c)
         if return_probs:
             probs.append(pb)
     res = {"out": out, "x": x, "lse": lse}

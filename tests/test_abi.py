@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects
+invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mla_latent_kv_08_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    syms = _header_symbols()
+    assert len(syms) >= 7, syms
+    assert sorted(_lib.EXPORTS) == syms
+    for s in syms:
+        assert getattr(lib, s) is not None
+
+
+def test_only_c_abi_is_exported(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    names = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    assert set(_header_symbols()) <= names
+    assert all(n.startswith("mla_") or n.startswith("_") for n in names), names
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(-99) == b"unknown status"
+
+
+def _dims(**kw):
+    d = dict(batch=2, heads=128, q_len=1, d_nope=128, d_rope=64, d_v=128, d_latent=512)
+    d.update(kw)
+    return _lib.MlaDims(**d)
+
+
+def _cache(**kw):
+    c = dict(latent_dtype=_lib.MLA_BF16, rope_dtype=_lib.MLA_BF16, latent=0x10000, latent_scale=None,
+             rope=0x10400, latent_stride=1152, scale_stride=0, rope_stride=1152, num_rows=2 * 4096,
+             page_size=0, capacity=4096, page_table=None, page_table_stride=0, reserved=0)
+    c.update(kw)
+    return _lib.MlaKvCache(**c)
+
+
+P = 0x20000  # a 16-byte aligned fake device address; never dereferenced on these paths
+
+
+def test_absorb_validation(lib):
+    byref = ctypes.byref
+    assert lib.mla_absorb_q(None, 1, P, P, P, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims()), 1, None, P, P, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims()), 1, P + 2, P, P, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims(heads=0)), 1, P, P, P, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims(d_nope=64)), 1, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(byref(_dims()), 7, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
+    # An empty batch is a valid no-op.
+    assert lib.mla_absorb_q(byref(_dims(batch=0)), 1, P, P, P, None) == _lib.MLA_OK
+    assert lib.mla_up_proj_v(byref(_dims(d_v=64)), 1, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_up_proj_v(byref(_dims()), 1, P, None, P, None) == _lib.MLA_ERR_INVALID_ARG
+
+
+def _attn(lib, dims=None, dtype=1, cache=None, seq=P, max_len=4096, ws=P, ws_bytes=1 << 30, opts=None,
+          q=P):
+    dims = dims or _dims()
+    cache = cache or _cache()
+    return lib.mla_decode_attn(ctypes.byref(dims), dtype, q, P, ctypes.byref(cache), seq, max_len,
+                               0.072, P, P, ws, ws_bytes, ctypes.byref(opts) if opts else None, None)
+
+
+def test_attn_validation(lib):
+    E = _lib
+    assert _attn(lib, q=None) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, seq=None) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, max_len=-1) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, dims=_dims(q_len=17)) == E.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, dims=_dims(heads=2048)) == E.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, dims=_dims(d_latent=256)) == E.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, cache=_cache(latent_stride=1000)) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, cache=_cache(latent_stride=512)) == E.MLA_ERR_INVALID_ARG  # row too short
+    assert _attn(lib, cache=_cache(num_rows=100)) == E.MLA_ERR_INVALID_ARG  # B*capacity rows missing
+    assert _attn(lib, cache=_cache(page_size=32)) == E.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, cache=_cache(page_size=64)) == E.MLA_ERR_INVALID_ARG  # no page table
+    assert _attn(lib, cache=_cache(latent_dtype=E.MLA_F32)) == E.MLA_ERR_UNSUPPORTED  # bf16 q, f32 cache
+    assert _attn(lib, cache=_cache(latent_dtype=E.MLA_FP4_E2M1_E4M3X16)) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, dtype=E.MLA_F32) == E.MLA_ERR_UNSUPPORTED  # fp32 q, bf16 cache
+    assert _attn(lib, opts=_lib.MlaDecodeOpts(-1)) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, dims=_dims(batch=0)) == E.MLA_OK
+
+
+def test_append_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+    c = _cache()
+    assert lib.mla_cache_append(byref(_dims()), E.MLA_F32, P, P, byref(c), P, None) == E.MLA_ERR_UNSUPPORTED
+    assert lib.mla_cache_append(byref(_dims()), E.MLA_BF16, None, P, byref(c), P, None) == E.MLA_ERR_INVALID_ARG
+    fp4 = _cache(latent_dtype=E.MLA_FP4_E2M1_E4M3X16, latent_scale=0x10100, scale_stride=416,
+                 latent_stride=416, rope_stride=416)
+    assert lib.mla_cache_append(byref(_dims(d_latent=256)), E.MLA_F32, P, P, byref(fp4), P,
+                                None) == E.MLA_ERR_UNSUPPORTED
+    assert lib.mla_cache_append(byref(_dims(batch=0)), E.MLA_F32, P, P, byref(fp4), P, None) == E.MLA_OK
+    assert lib.mla_dequant_rows(byref(c), 512, None, 4, P, None) == E.MLA_ERR_INVALID_ARG

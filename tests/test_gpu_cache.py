@@ -1,0 +1,111 @@
+"""GPU checks of mla_cache_append (bf16 copy, FP4 quantisation) and mla_dequant_rows.
+
+Integer and byte results must be bit-exact against the oracle's codec.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import fp4_ref
+from tests import mla_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+
+def _adversarial_rows(n, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    x[1] = 0.0
+    x[2, :16] = np.float32(1e-12)      # scale rounds to zero
+    x[3] *= np.float32(1e3)            # large values -> saturated scales
+    x[4] *= np.float32(1e-3)           # small, subnormal-scale range
+    # exact ties: s = 1 (amax 6) and elements on every midpoint
+    x[5, :16] = np.array([6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, -.25, -.75, -1.25, -1.75, -2.5, -3.5, -5, 0],
+                         dtype=np.float32)
+    x[6, :16] = np.float32(-0.0)
+    x[7] = np.float32(448 * 6 * 2)     # amax/6 above the E4M3 maximum
+    x[8] = rng.choice(fp4_ref.E2M1_TABLE, size=512).astype(np.float32) * np.float32(0.125)
+    return x
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp4_append_bytes_bit_exact(paged):
+    n_tok = 257
+    x = _adversarial_rows(n_tok)
+    rope = torch.randn(n_tok, 64).to(torch.bfloat16)
+    w = W.Workload("app", B=1, H=1, Q=1, Dn=128, Dr=64, Vd=128, Ckv=512, dtype="fp4", seed=0,
+                   lens=(n_tok,), paged=paged)
+    inp = W.generate(w)
+    inp.latent = torch.from_numpy(x)
+    inp.rope = rope
+    g = T.GpuCase(inp, poison=True)
+    torch.cuda.synchronize()
+    buf = g.buf.cpu().numpy()
+    rows = g.pl.rows.numpy()
+    codes_ref, scales_ref = fp4_ref.quantize_rows(x)
+    assert np.array_equal(buf[rows, :256], codes_ref)
+    assert np.array_equal(buf[rows, 256:288], scales_ref)
+    assert np.array_equal(buf[rows, 288:416].view(np.int16), rope.view(torch.int16).numpy())
+    # Decoded values, through the same device decode the attention kernel uses.
+    out = torch.empty(n_tok, 512, dtype=torch.float32, device="cuda")
+    T.ops().mla_dequant_rows(g.cache, torch.from_numpy(rows.astype(np.int32)).cuda(), out)
+    torch.cuda.synchronize()
+    deq = out.cpu().numpy().astype(np.float64)
+    ref = fp4_ref.dequantize_rows(codes_ref, scales_ref)
+    assert np.array_equal(deq.view(np.int64), ref.view(np.int64))
+
+
+def test_fp4_append_many_random_rows():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((4096, 512)) * np.exp(rng.uniform(-8, 8, (4096, 1)))).astype(np.float32)
+    w = W.Workload("app", B=4, H=1, Q=1, Dn=128, Dr=64, Vd=128, Ckv=512, dtype="fp4", seed=1,
+                   lens=(1024, 1024, 1024, 1024))
+    inp = W.generate(w)
+    inp.latent = torch.from_numpy(x)
+    g = T.GpuCase(inp, poison=False)
+    torch.cuda.synchronize()
+    buf = g.buf.cpu().numpy()
+    rows = g.pl.rows.numpy()
+    codes_ref, scales_ref = fp4_ref.quantize_rows_fast(x)
+    assert np.array_equal(buf[rows, :256], codes_ref)
+    assert np.array_equal(buf[rows, 256:288], scales_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_plain_append_bit_exact_and_positions(dtype):
+    w = W.reduced(W.WORKLOADS["dsv3_bf16"], 3, [5, 64, 70]).with_(dtype=dtype, paged=True)
+    inp = W.generate(w)
+    g = T.GpuCase(inp, poison=True)
+    # Append Q=2 new tokens per sequence at positions len..len+1 (lengths grow by 2).
+    o = T.ops()
+    new_lens = inp.seq_lens + 2
+    sd = W.storage_dtype(w)
+    c = torch.randn(3, 2, 512).to(sd)
+    r = torch.randn(3, 2, 64).to(sd)
+    before = g.buf.clone()
+    # Capacity: pages exist for the new positions only where the last page has room.
+    o.mla_cache_append(c.cuda(), r.cuda(), g.cache, new_lens.cuda().to(torch.int32))
+    torch.cuda.synchronize()
+    after = g.buf.cpu()
+    table = g.pl.page_table
+    changed = set()
+    for b in range(3):
+        for j in range(2):
+            pos = int(new_lens[b]) - 2 + j
+            page_idx = pos // 64
+            if pos >= g.pl.capacity or page_idx >= table.shape[1]:
+                continue
+            pr = int(table[b, page_idx]) * 64 + pos % 64
+            if pr >= after.shape[0]:
+                continue
+            changed.add(pr)
+            assert torch.equal(after[pr, :512].float(), c[b, j].float())
+            assert torch.equal(after[pr, 512:].float(), r[b, j].float())
+    mask = torch.ones(after.shape[0], dtype=torch.bool)
+    for pr in changed:
+        mask[pr] = False
+    a = after[mask].float()
+    bb = before.cpu()[mask].float()
+    assert torch.equal(torch.isnan(a), torch.isnan(bb))
+    assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(bb))
