@@ -31,7 +31,7 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 WORKLOAD = "dsv3_bf16"
 METRIC = "MLA decode tokens/s + KV GB/s & MFMA TFLOP/s as % of MI355X roofline"
-ATTN_KERNEL_SOURCES = ("attn_bf16.hip", "device_common.h", "internal.h")
+ATTN_KERNEL_SOURCES = ("attn_mfma.hip", "device_common.h", "internal.h")
 
 
 def kernel_source_hash() -> str:

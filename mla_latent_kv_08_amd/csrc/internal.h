@@ -10,7 +10,7 @@
 namespace mla {
 
 // Rows of query (h, q) handled by one attention workgroup on the matrix-core path.
-constexpr int kRowsPerGroup = 128;
+constexpr int kRowsPerGroup = 64;
 constexpr int kTileTokens = 64;
 
 struct AttnParams {
@@ -20,10 +20,10 @@ struct AttnParams {
   const int32_t* seq_lens;
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
-  float* part_x;    // [G, 2W, 128, Ckv] fp32 partial results
-  float* part_lse;  // [G, 2W, 128]
+  float* part_x;    // [G, 2W, 64, Ckv] fp32 partial results
+  float* part_lse;  // [G, 2W, 64]
   int B, H, Q, HQ, Ckv, Dr;
-  int groups;      // G = ceil(HQ / 128)
+  int groups;      // G = ceil(HQ / 64)
   int workgroups;  // W per row group
   float scale_log2;  // softmax_scale * log2(e)
 };
