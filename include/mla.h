@@ -87,7 +87,8 @@ typedef struct mla_dims {
  * already rotated). Physical row r of the cache lives at
  *     latent + r*latent_stride, rope + r*rope_stride (+ latent_scale +
  *     r*scale_stride for FP4),
- * strides in bytes. A combined [latent | rope] row (the CacheCompressed
+ * strides in bytes (multiples of 16, at most 2^24; a larger stride returns
+ * MLA_ERR_UNSUPPORTED). A combined [latent | rope] row (the CacheCompressed
  * layout) is rope = latent + Ckv*sizeof(elem) with equal strides.
  *
  * Logical token t of sequence b maps to physical row
@@ -120,7 +121,7 @@ typedef struct mla_kv_cache {
 
 /* Optional tuning of mla_decode_attn; pass NULL for the library's choice. */
 typedef struct mla_decode_opts {
-  /* Workgroups that share the token axis of one block of 128 query rows.
+  /* Workgroups that share the token axis of one block of 64 query rows.
    * 0 = chosen from the compute-unit count. The tokens of all sequences are
    * dealt to them in equal contiguous runs of 64-token tiles. */
   int32_t workgroups;

@@ -21,6 +21,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # Keep the compiler from forming packed fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-op accumulators in VGPRs: the attention kernel's O accumulators
+    # then stay put across the tile loop (no AGPR<->VGPR copies each tile),
+    # and its query fragments sit in AGPRs, which the matrix ops read directly.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -11,16 +11,18 @@
 //   O^T[c, r] += sum_t C^T[c, t] P^T[t, r]        c over the 512 latent
 //
 // Both contractions are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-// Wave w = (rh, ch): rows 32*rh..+31 of the block; it scores tokens 32*ch..+31
-// of each 64-token tile and accumulates latent channels 256*ch..+255. The two
+// Wave w = (rh, th): rows 32*rh..+31 of the block; it scores tokens 32*th..+31
+// of each 64-token tile and accumulates latent channels 256*th..+255. The two
 // waves of a row half swap their bf16 probabilities (and row max / sum)
 // through LDS, so each accumulates P.V over all 64 tokens for its channels.
 // Per wave: Q fragments 144 VGPRs, O^T 8 x 16 fp32 accumulators.
 //
 // Tiles of 64 tokens (one cache page) are double buffered in LDS: the loads
-// of tile i+1 are issued into registers when tile i starts and written to
-// the other buffer after tile i's P.V (an FP4 tile is decoded to bf16 on that
-// write). The P.V operand (tokens along the contraction) is read with
+// of tile i+1 are issued when tile i starts. bf16 rows go straight to the
+// other buffer by buffer loads with an LDS destination; an FP4 tile is loaded
+// into registers and decoded to bf16 when written to the other buffer after
+// tile i's P.V.
+// The P.V operand (tokens along the contraction) is read with
 // ds_read_b64_tr_b16 from the same row-major tile the score contraction reads.
 //
 // Tokens are split across workgroups (flash-decoding): the tiles of all
@@ -105,68 +107,58 @@ __device__ __forceinline__ int64_t tile_row0(const CacheView& c, int b, int tile
   return r0;
 }
 
-// 64-bit select without control flow.
-__device__ __forceinline__ const uint8_t* pick(bool c, const uint8_t* a, const uint8_t* b) {
-  const uint64_t m = 0ull - (uint64_t)c;
-  return reinterpret_cast<const uint8_t*>((reinterpret_cast<uint64_t>(a) & m) |
-                                          (reinterpret_cast<uint64_t>(b) & ~m));
+// bf16 tiles go to LDS by direct buffer loads: one load instruction per
+// token moves its 1 KiB latent row (64 lanes x 16 B) to the token's LDS row,
+// and one with 8 active lanes moves its 128 B RoPE key behind it. Each buffer
+// descriptor spans exactly the tile's valid rows, so rows at or past `valid`
+// read as zero without touching memory, and no load can leave the tile. The
+// loads of tile i+1 are issued right after the barrier that opens tile i, and
+// each wave waits for its own loads before the barrier that opens tile i+1.
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(int32x4_t rsrc, lds_void* lds, int size,
+                                                           int voffset, int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer descriptor: base, stride 0, num_records bytes (loads at or past
+// it return zero).
+__device__ __forceinline__ int32x4_t buffer_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
 }
 
-// Tile staging through registers: the loads of tile i+1 are issued right
-// after the barrier that opens tile i and are written to LDS after tile i's
-// P.V, so they stay in flight for a whole tile of compute.
-//
-// bf16 tiles: 64 tokens x 72 chunks of 16 B = 18 chunks per thread; thread
-// tid takes chunks s = tid + 256*n, i.e. token s / 72, chunk s % 72 (0..63
-// latent, 64..71 RoPE), advancing by (3, 40) per step. Tokens at or past
-// `valid` re-read the last valid row: they are masked out of the softmax and
-// their (finite) values meet zero probabilities.
-constexpr int kBf16Regs = kTileTokens * 72 / kThreads;  // 18
-
-struct Bf16Stage {
-  uint4 v[kBf16Regs];
-};
+struct Bf16Stage {};  // nothing passes through registers
 
 __device__ __forceinline__ void load_tile_bf16(const CacheView& c, int64_t row0, int valid, int tid,
-                                               Bf16Stage& st) {
-  // Opaque thread id: keeps the compiler from hoisting all 18 addresses out
-  // of the tile loop (they would not fit in registers).
-  asm volatile("" : "+v"(tid));
-  const uint8_t* lat0 = c.latent + row0 * c.latent_stride;
-  const uint8_t* rope0 = c.rope + row0 * c.rope_stride;
-  const uint32_t ls = (uint32_t)c.latent_stride, rs = (uint32_t)c.rope_stride;
-  int t = tid / 72;
-  int cc = tid - t * 72;
+                                               uint8_t* dst, Bf16Stage&) {
+  // The wave index is uniform; saying so keeps the offsets in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
+  const uint32_t rs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.rope_stride);
+  const int32x4_t lat = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * ls);
+  const int32x4_t rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * rs);
 #pragma unroll
-  for (int n = 0; n < kBf16Regs; ++n) {
-    const uint32_t tt = (uint32_t)min(t, valid - 1);
-    const bool lat = cc < 64;
-    const uint32_t off = tt * (lat ? ls : rs) + (uint32_t)(lat ? cc : cc - 64) * 16u;
-    st.v[n] = *reinterpret_cast<const uint4*>(pick(lat, lat0, rope0) + off);
-    cc += 40;
-    t += 3;
-    if (cc >= 72) {
-      cc -= 72;
-      t += 1;
+  for (int n = 0; n < kTileTokens / 4; ++n) {
+    const int t = wave * (kTileTokens / 4) + n;
+    llvm_amdgcn_raw_buffer_load_lds(lat, (lds_void*)(dst + t * kRowBytes), 16, lane * 16,
+                                    (int)(t * ls), 0, 0);
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int n = 0; n < kTileTokens / 4; ++n) {
+      const int t = wave * (kTileTokens / 4) + n;
+      llvm_amdgcn_raw_buffer_load_lds(rope, (lds_void*)(dst + t * kRowBytes + 1024), 16, lane * 16,
+                                      (int)(t * rs), 0, 0);
     }
   }
 }
 
-__device__ __forceinline__ void store_tile_bf16(uint8_t* dst, int tid, const Bf16Stage& st) {
-  asm volatile("" : "+v"(tid));
-  int t = tid / 72;
-  int cc = tid - t * 72;
-#pragma unroll
-  for (int n = 0; n < kBf16Regs; ++n) {
-    *reinterpret_cast<uint4*>(dst + t * kRowBytes + cc * 16) = st.v[n];
-    cc += 40;
-    t += 3;
-    if (cc >= 72) {
-      cc -= 72;
-      t += 1;
-    }
-  }
-}
+__device__ __forceinline__ void store_tile_bf16(uint8_t*, int, const Bf16Stage&) {}
 
 // FP4 tiles: per token 16 code chunks (32 channels each) with their 2 scale
 // bytes, and 8 RoPE chunks. Thread tid takes code chunks s = tid + 256*k
@@ -228,6 +220,18 @@ __device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int tid, const Fp4S
   }
 }
 
+// Both halves of a wave64 register combined lane-wise: lanes l and l ^ 32
+// get the same op(x_l, x_l^32) (operands in the same order), via
+// v_permlane32_swap instead of an LDS permute.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <bool kFp4>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
@@ -236,10 +240,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
-  const int rh = wave & 1;
-  const int ch = wave >> 1;
+  const int rh = wave & 1;   // row half of the block (32 rows)
+  const int th = wave >> 1;  // token half of a tile for S, channel half of O
 
   // Block -> (run wg, row block g). Consecutive block ids go to the 8 XCDs in
   // turn; the G row blocks of one run share an XCD (and its L2), and are
@@ -279,19 +283,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  uint8_t* tiles = smem;  // two bf16 tiles: tile i lives in buffer i & 1
+  uint8_t* tiles = smem;  // two bf16 tiles: tile i of the run lives in buffer i & 1
   Xchg* xc = reinterpret_cast<Xchg*>(smem + 2 * kTileBytes);
 
   const int row_local = rh * 32 + (lane & 31);
   const int row = g * 64 + row_local;
   const bool row_ok = row < p.HQ;
-  const int qi = row_ok ? row % p.Q : 0;
+  const int row_c = row_ok ? row : 0;  // rows past HQ compute on row 0's query, never stored
+  const int qi = row_c % p.Q;
   const int slots = 2 * p.workgroups;
   const int count = end - start;
 
-  // Current tile (b, tile) and the next one to prefetch (nb, ntile).
-  int b = s_start[0];
-  int tile = s_start[1];
+  // Current tile (b, tile) and the prefetch cursor (nb, ntile).
+  int b = __builtin_amdgcn_readfirstlane(s_start[0]);
+  int tile = __builtin_amdgcn_readfirstlane(s_start[1]);
   int L = seq_len(p, b);
   int nb = b, ntile = tile, nL = L;
   auto advance = [&](int& bb, int& tt, int& LL) {
@@ -304,208 +309,226 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       LL = bb < p.B ? seq_len(p, bb) : 0;
     }
   };
+  using Stage = typename std::conditional<kFp4, Fp4Stage, Bf16Stage>::type;
+  auto stage_load = [&](int bb, int tt, int LL, uint8_t* dst, Stage& st, bool& bad) {
+    const int64_t r0 = tile_row0(p.cache, bb, tt, bad);
+    const int valid = bad ? 1 : min(kTileTokens, LL - tt * kTileTokens);
+    if constexpr (kFp4) {
+      (void)dst;
+      load_tile_fp4(p.cache, r0, valid, tid, st);
+    } else {
+      load_tile_bf16(p.cache, r0, valid, tid, dst, st);
+    }
+  };
+  auto stage_store = [&](uint8_t* dst, const Stage& st) {
+    if constexpr (kFp4) {
+      store_tile_fp4(dst, tid, st);
+    } else {
+      store_tile_bf16(dst, tid, st);
+    }
+  };
 
   // Stage tile 0 of the run into buffer 0 (visible after the first barrier).
   bool bad_cur = false;
   {
-    const int64_t r0 = tile_row0(p.cache, b, tile, bad_cur);
-    const int valid = bad_cur ? 1 : min(kTileTokens, L - tile * kTileTokens);
-    if constexpr (kFp4) {
-      Fp4Stage st;
-      load_tile_fp4(p.cache, r0, valid, tid, st);
-      store_tile_fp4(tiles, tid, st);
-    } else {
-      Bf16Stage st;
-      load_tile_bf16(p.cache, r0, valid, tid, st);
-      store_tile_bf16(tiles, tid, st);
-    }
+    Stage st;
+    stage_load(b, tile, L, tiles, st, bad_cur);
+    stage_store(tiles, st);
   }
 
-  bf16x8 qf[36];
-  floatx16 o[8];
-  float m = -INFINITY, l = 0.0f;
-  int seg_bad = 0;
-  int seg_lo = tile;
+  int it = 0;
   bool first_seg = true;
+  while (it < count) {
+    // ---- one segment: tiles [seg_lo, seg_lo + seg_n) of sequence seg_b ----
+    const int seg_b = b;
+    const int seg_L = L;
+    const int nt = tiles_of(seg_L);
+    const int seg_lo = tile;
+    const int seg_n = min(count - it, nt - seg_lo);
+    const int vis = seg_L - p.Q + qi + 1;  // this row sees tokens t < vis
 
-  for (int it = 0; it < count; ++it) {
-    const int nt = tiles_of(L);
-    if (it == 0 || tile == 0) {
-      // New segment: Q fragments of this sequence (B operand of S^T = K Qcat^T):
-      // row `row`, channels 16*ks + 8*hi .. +7 of [q_lat | q_pe].
-      const int64_t grow = (int64_t)b * p.HQ + (row_ok ? row : 0);
-      const uint16_t* ql = reinterpret_cast<const uint16_t*>(p.q_lat) + grow * 512;
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_pe) + grow * 64;
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(ql + 16 * ks + 8 * hi) : bf16x8{};
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        qf[32 + ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * hi) : bf16x8{};
-      }
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) o[cb] = floatx16{};
-      m = -INFINITY;
-      l = 0.0f;
-      seg_bad = 0;
-      seg_lo = tile;
-    }
-    seg_bad |= bad_cur ? 1 : 0;
-
-    // Tile `it` is in LDS for every wave, and every wave is done with tile
-    // it-1, whose buffer receives tile it+1 below.
-    __syncthreads();
-
-    // Prefetch the next tile of the run into registers.
-    bool bad_nxt = false;
-    const bool has_next = it + 1 < count;
-    using Stage = typename std::conditional<kFp4, Fp4Stage, Bf16Stage>::type;
-    Stage st;
-    if (has_next) {
-      advance(nb, ntile, nL);
-      const int64_t r0 = tile_row0(p.cache, nb, ntile, bad_nxt);
-      const int valid = bad_nxt ? 1 : min(kTileTokens, nL - ntile * kTileTokens);
-      if constexpr (kFp4) {
-        load_tile_fp4(p.cache, r0, valid, tid, st);
-      } else {
-        load_tile_bf16(p.cache, r0, valid, tid, st);
-      }
-    }
-    const uint8_t* tb = tiles + (it & 1) * kTileBytes;
-
-    // ---- S^T block: tokens 32*ch .. +31 of the tile x rows 32*rh .. +31 ----
-    floatx16 s = floatx16{};
+    // Q fragments (B operand of S^T = K Qcat^T): row `row_c`, channels
+    // 16*ks + 8*hi .. +7 of [q_lat | q_pe].
+    bf16x8 qf[36];
     {
-      const uint8_t* kb = tb + (32 * ch + (lane & 31)) * kRowBytes + hi * 16;
+      const int64_t grow = (int64_t)seg_b * p.HQ + row_c;
+      const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) + grow * 512 + 8 * hi);
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) + grow * 64 + 8 * hi);
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + ks * 32);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
+      // Park the fragments in AGPRs (the matrix ops read them there), which
+      // leaves the VGPRs to the accumulators and the LDS read pipelines.
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) asm volatile("" : "+a"(qf[ks]));
     }
+    floatx16 o[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) o[cb] = floatx16{};
+    float m = -INFINITY, l = 0.0f;
+    int seg_bad = 0;
 
-    // ---- online softmax in the log2 domain; lane holds row `row` ----
-    const int vis = L - p.Q + qi + 1;  // this row sees tokens t < vis
-    const int tok0 = tile * kTileTokens + 32 * ch + 4 * hi;
-    float own_mx = -INFINITY;
+    for (int j = 0; j < seg_n; ++j, ++it) {
+      seg_bad |= bad_cur ? 1 : 0;
+      const int cur_tile = seg_lo + j;
+
+      // Tile `it` is in LDS for every wave (each wave's own loads have
+      // landed), and every wave is done with tile it-1, whose buffer
+      // receives tile it+1 below.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+
+      bool bad_nxt = false;
+      const bool has_next = it + 1 < count;
+      Stage st;
+      if (has_next) {
+        advance(nb, ntile, nL);
+        stage_load(nb, ntile, nL, tiles + ((it + 1) & 1) * kTileBytes, st, bad_nxt);
+      }
+      const uint8_t* tb = tiles + (it & 1) * kTileBytes;
+
+      // ---- S^T block: tokens 32*th .. +31 of the tile x rows 32*rh .. +31 ----
+      // K fragments run four reads ahead of the matrix ops; the k-steps
+      // chain on one accumulator.
+      floatx16 s;
+      {
+        const uint8_t* kb = tb + (32 * th + (lane & 31)) * kRowBytes + hi * 16;
+        bf16x8 ka[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = tok0 + 8 * (i >> 2) + (i & 3);
-      const float v = tok < vis ? s[i] * p.scale_log2 : -INFINITY;
-      s[i] = v;
-      own_mx = fmaxf(own_mx, v);
-    }
-    own_mx = fmaxf(own_mx, __shfl_xor(own_mx, 32, 64));
-    // The reference m moves only when a row max exceeds it by > kRescaleLog2,
-    // so O is rarely rescaled and every probability stays <= 2^kRescaleLog2.
-    const bool ovf = own_mx > m + kRescaleLog2;
-    float m_use = m == -INFINITY ? 0.0f : m;
-    float own_sum = 0.0f;
-    bf16x8 pf[2];
+        for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kb + u * 32);
+        s = floatx16{};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = exp2f(s[i] - m_use);
-      own_sum += e;
-      pf[i >> 3][i & 7] = (__bf16)e;
-    }
-    own_sum += __shfl_xor(own_sum, 32, 64);
-    const int pw = wave ^ 2;  // the other token half of this row half
-    *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][0]) = pf[0];
-    *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][1]) = pf[1];
-    if (hi == 0) {
-      xc->mx[wave][lane] = own_mx;
-      xc->sum[wave][lane] = own_sum;
-    }
-    const bool wave_ovf = __any(ovf);
-    if (lane == 0) xc->flag[wave] = wave_ovf ? 1 : 0;
-    __syncthreads();
-    const int any_ovf = xc->flag[0] | xc->flag[1] | xc->flag[2] | xc->flag[3];
-    if (any_ovf) {
-      // A row max rose: move the reference to the new max (both token halves
-      // agree on it), recompute this wave's probabilities, rescale O and l.
-      const float mx = fmaxf(own_mx, xc->mx[pw][lane & 31]);
-      const bool upd = mx > m + kRescaleLog2;
-      const float m_new = upd ? mx : m;
-      const float alpha = upd ? exp2f(m - m_new) : 1.0f;
-      m_use = m_new == -INFINITY ? 0.0f : m_new;
-      own_sum = 0.0f;
+        for (int ks = 0; ks < 36; ++ks) {
+          const bf16x8 a = ka[ks & 3];
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+          if (ks + 4 < 36) ka[ks & 3] = *reinterpret_cast<const bf16x8*>(kb + (ks + 4) * 32);
+        }
+        // Issue order: the four leading reads, then matrix op / next read pairs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+
+      // ---- online softmax in the log2 domain; lane holds row `row` ----
+      const int tok0 = cur_tile * kTileTokens + 32 * th + 4 * hi;
+      float own_mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = exp2f(s[i] - m_use);
+        const int tok = tok0 + 8 * (i >> 2) + (i & 3);
+        const float v = tok < vis ? s[i] * p.scale_log2 : -INFINITY;
+        s[i] = v;
+        own_mx = fmaxf(own_mx, v);
+      }
+      own_mx = xor32_max(own_mx);
+      // The reference m moves only when a row max exceeds it by > kRescaleLog2,
+      // so O is rarely rescaled and every probability stays <= 2^kRescaleLog2.
+      const bool ovf = own_mx > m + kRescaleLog2;
+      float m_use = m == -INFINITY ? 0.0f : m;
+      float own_sum = 0.0f;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
         own_sum += e;
         pf[i >> 3][i & 7] = (__bf16)e;
       }
-      own_sum += __shfl_xor(own_sum, 32, 64);
-      __syncthreads();  // every wave has read the old max and flags
+      own_sum = xor32_sum(own_sum);
+      const int pw = wave ^ 2;  // the other token half of this row half
       *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][0]) = pf[0];
       *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][1]) = pf[1];
-      if (hi == 0) xc->sum[wave][lane] = own_sum;
-      if (__any(upd && m != -INFINITY)) {
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+      if (hi == 0) {
+        xc->mx[wave][lane] = own_mx;
+        xc->sum[wave][lane] = own_sum;
       }
-      l *= alpha;
-      m = m_new;
+      const bool wave_ovf = __any(ovf);
+      if (lane == 0) xc->flag[wave] = wave_ovf ? 1 : 0;
       __syncthreads();
-    }
-    const float psum = xc->sum[pw][lane & 31];
-    l += ch == 0 ? own_sum + psum : psum + own_sum;
-    bf16x8 pp[2];
-    pp[0] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][0]);
-    pp[1] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][1]);
-    // Token half 0 probabilities come from the ch = 0 wave, half 1 from ch = 1.
-    const bf16x8 p0 = ch == 0 ? pf[0] : pp[0];
-    const bf16x8 p1 = ch == 0 ? pf[1] : pp[1];
-    const bf16x8 p2 = ch == 0 ? pp[0] : pf[0];
-    const bf16x8 p3 = ch == 0 ? pp[1] : pf[1];
-
-    // ---- O^T[c, r] += C^T[c, t] P^T[t, r] for this wave's 256 channels ----
-    // A operand (k-step kk): channel lane%32 of the block, tokens
-    // 16*kk + 4*hi + {0..3} and +8 + {0..3}, by two transposed LDS reads of
-    // a 4 x 16 block each (16-lane groups: lane j -> row j/4, cols 4*(j%4)).
-    {
-      const int j = lane & 15;
-      const uint8_t* vb = tb + (4 * hi + (j >> 2)) * kRowBytes +
-                          (256 * ch + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2;
+      const int any_ovf = xc->flag[0] | xc->flag[1] | xc->flag[2] | xc->flag[3];
+      if (any_ovf) {
+        // A row max rose: move the reference to the new max (both token halves
+        // agree on it), recompute this wave's probabilities, rescale O and l.
+        const float mx = fmaxf(own_mx, xc->mx[pw][lane & 31]);
+        const bool upd = mx > m + kRescaleLog2;
+        const float m_new = upd ? mx : m;
+        const float alpha = upd ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+        m_use = m_new == -INFINITY ? 0.0f : m_new;
+        own_sum = 0.0f;
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
+        for (int i = 0; i < 16; ++i) {
+          const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
+          own_sum += e;
+          pf[i >> 3][i & 7] = (__bf16)e;
+        }
+        own_sum = xor32_sum(own_sum);
+        __syncthreads();  // every wave has read the old max and flags
+        *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][0]) = pf[0];
+        *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][1]) = pf[1];
+        if (hi == 0) xc->sum[wave][lane] = own_sum;
+        if (__any(upd && m != -INFINITY)) {
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+        }
+        l *= alpha;
+        m = m_new;
+        __syncthreads();
+      }
+      const float psum = xc->sum[pw][lane & 31];
+      l += th == 0 ? own_sum + psum : psum + own_sum;
+      bf16x8 pp[2];
+      pp[0] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][0]);
+      pp[1] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][1]);
+      // Token half 0 probabilities come from the th = 0 wave, half 1 from th = 1.
+      bf16x8 pk[4];
+      pk[0] = th == 0 ? pf[0] : pp[0];
+      pk[1] = th == 0 ? pf[1] : pp[1];
+      pk[2] = th == 0 ? pp[0] : pf[0];
+      pk[3] = th == 0 ? pp[1] : pf[1];
+
+      // ---- O^T[c, r] += C^T[c, t] P^T[t, r] for this wave's 256 channels ----
+      // A operand (k-step kk): channel lane%32 of the block, tokens
+      // 16*kk + 4*hi + {0..3} and +8 + {0..3}, by two transposed LDS reads of
+      // a 4 x 16 block each (16-lane groups: lane j -> row j/4, cols 4*(j%4)).
+      // The 8 channel blocks of a k-step are independent accumulators.
+      {
+        const int jj = lane & 15;
+        const uint8_t* vb = tb + (4 * hi + (jj >> 2)) * kRowBytes +
+                            (256 * th + 16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint8_t* a0 = vb + 16 * kk * kRowBytes + cb * 64;
-          const bf16x8 a = join(tr_read(a0), tr_read(a0 + 8 * kRowBytes));
-          const bf16x8 bp = kk == 0 ? p0 : kk == 1 ? p1 : kk == 2 ? p2 : p3;
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[cb], 0, 0, 0);
+          const uint8_t* vk = vb + 16 * kk * kRowBytes;
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) {
+            const bf16x8 a = join(tr_read(vk + cb * 64), tr_read(vk + cb * 64 + 8 * kRowBytes));
+            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[cb], 0, 0, 0);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+
+      // The prefetched registers go to the other buffer.
+      if (has_next) stage_store(tiles + ((it + 1) & 1) * kTileBytes, st);
+      bad_cur = bad_nxt;
     }
 
-    // The prefetched tile goes to the other buffer.
-    if (has_next) {
-      if constexpr (kFp4) {
-        store_tile_fp4(tiles + ((it + 1) & 1) * kTileBytes, tid, st);
-      } else {
-        store_tile_bf16(tiles + ((it + 1) & 1) * kTileBytes, tid, st);
-      }
-    }
-
-    // ---- end of a segment: write x / lse, or a partial for the combine ----
-    if (it == count - 1 || tile == nt - 1) {
-      const bool whole = seg_lo == 0 && tile == nt - 1;
+    // ---- end of the segment: write x / lse, or a partial for the combine ----
+    {
+      const bool whole = seg_lo == 0 && seg_lo + seg_n == nt;
       const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
       const float nanv = __uint_as_float(0x7fc00000u);
-      float lse_v = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
       if (seg_bad) lse_v = nanv;
       if (row_ok) {
         if (whole) {
-          uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + ((int64_t)b * p.HQ + row) * 512;
+          uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + ((int64_t)seg_b * p.HQ + row) * 512;
 #pragma unroll
           for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const int c = 256 * ch + 32 * cb + 8 * i4 + 4 * hi;
+              const int c = 256 * th + 32 * cb + 8 * i4 + 4 * hi;
               float v[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = seg_bad ? nanv : o[cb][4 * i4 + e] * inv_l;
@@ -513,7 +536,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                   make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
           }
-          if (p.lse != nullptr && hi == 0 && ch == 0) p.lse[(int64_t)b * p.HQ + row] = lse_v;
+          if (p.lse != nullptr && hi == 0 && th == 0) p.lse[(int64_t)seg_b * p.HQ + row] = lse_v;
         } else {
           const int slot = 2 * wg + (first_seg ? 0 : 1);
           const int64_t prow = ((int64_t)g * slots + slot) * 64 + row_local;
@@ -522,7 +545,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const int c = 256 * ch + 32 * cb + 8 * i4 + 4 * hi;
+              const int c = 256 * th + 32 * cb + 8 * i4 + 4 * hi;
               float4 v;
               v.x = o[cb][4 * i4 + 0] * inv_l;
               v.y = o[cb][4 * i4 + 1] * inv_l;
@@ -531,21 +554,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
               *reinterpret_cast<float4*>(xo + c) = v;
             }
           }
-          if (hi == 0 && ch == 0) p.part_lse[prow] = lse_v;
+          if (hi == 0 && th == 0) p.part_lse[prow] = lse_v;
         }
       }
       first_seg = false;
     }
-
-    // Move to the next tile of the run.
-    if (it + 1 < count) {
-      const bool new_seq = tile == nt - 1;
-      b = nb;
-      tile = ntile;
-      L = nL;
-      (void)new_seq;
-    }
-    bad_cur = bad_nxt;
+    // The next segment starts at the prefetch cursor (tile 0 of a later sequence).
+    b = nb;
+    tile = ntile;
+    L = nL;
   }
 }
 

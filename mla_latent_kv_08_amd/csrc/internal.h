@@ -12,6 +12,9 @@ namespace mla {
 // Rows of query (h, q) handled by one attention workgroup on the matrix-core path.
 constexpr int kRowsPerGroup = 64;
 constexpr int kTileTokens = 64;
+// Largest row stride (bytes) of any cache array: a 64-row tile then spans less
+// than 2^31 bytes, so tile loads use 32-bit offsets from the tile's first row.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 struct AttnParams {
   const void* q_lat;  // [B, HQ, Ckv]

@@ -69,6 +69,11 @@ int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t
   if (c->rope_dtype != MLA_F32 && c->rope_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   const int64_t rope_bytes = (int64_t)d_rope * (c->rope_dtype == MLA_F32 ? 4 : 2);
   if (c->latent_stride < lat_bytes || c->rope_stride < rope_bytes) return MLA_ERR_INVALID_ARG;
+  // Tile loads address one 64-row page with 32-bit byte offsets.
+  if (c->latent_stride > mla::kMaxRowStride || c->rope_stride > mla::kMaxRowStride ||
+      c->scale_stride > mla::kMaxRowStride) {
+    return MLA_ERR_UNSUPPORTED;
+  }
   if (c->page_size == 0) {
     if (c->page_table != nullptr) return MLA_ERR_INVALID_ARG;
     if ((int64_t)batch * c->capacity > c->num_rows) return MLA_ERR_INVALID_ARG;
@@ -100,7 +105,7 @@ mla::CacheView view_of(const mla_kv_cache* c) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
 // Token-split policy of the matrix-core attention path: how many workgroups
-// share the tiles of one block of 128 query rows.
+// share the tiles of one block of kRowsPerGroup query rows.
 int attn_workgroups(const mla_dims* d, int32_t max_seq_len, const mla_decode_opts* opts, int cus) {
   const int64_t hq = (int64_t)d->heads * d->q_len;
   const int groups = (int)((hq + kRowsPerGroup - 1) / kRowsPerGroup);
