@@ -11,19 +11,28 @@
 //   O^T[c, r] += sum_t C^T[c, t] P^T[t, r]        c over the 512 latent
 //
 // Both contractions are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-// Wave w = (rh, th): rows 32*rh..+31 of the block; it scores tokens 32*th..+31
-// of each 64-token tile and accumulates latent channels 256*th..+255. The two
-// waves of a row half swap their bf16 probabilities (and row max / sum)
-// through LDS, so each accumulates P.V over all 64 tokens for its channels.
-// Per wave: Q fragments 144 VGPRs, O^T 8 x 16 fp32 accumulators.
+// The eight waves of a workgroup (two per SIMD) have fixed roles:
+//   score waves 0, 1   row block rb = wave (32 rows): query fragments in
+//                      registers, S^T for a 32-token tile, the online softmax
+//                      of their own rows; bf16 probabilities and per-row
+//                      rescale factors go to LDS.
+//   P.V waves 2,3,6,7  latent channels 128*cq .. +127 of all 64 rows (O^T in
+//                      registers); each transposed V fragment feeds both row
+//                      blocks.
+//   load waves 4, 5    copy cache tiles into an LDS ring.
+// Step k of the run: score waves work on tile k, P.V waves on tile k-1 (with
+// the probabilities the score waves left in the previous step), load waves
+// start tile k+2; one barrier separates steps. Score and P.V work land on
+// different SIMDs (0,1 and 2,3), about 36 and 32 matrix ops per SIMD and step.
 //
-// Tiles of 64 tokens (one cache page) are double buffered in LDS: the loads
-// of tile i+1 are issued when tile i starts. bf16 rows go straight to the
-// other buffer by buffer loads with an LDS destination; an FP4 tile is loaded
-// into registers and decoded to bf16 when written to the other buffer after
-// tile i's P.V.
-// The P.V operand (tokens along the contraction) is read with
-// ds_read_b64_tr_b16 from the same row-major tile the score contraction reads.
+// Tiles of 32 tokens (half a cache page) live in a ring of four LDS buffers:
+// the P.V tile, the score tile and two tiles in flight. bf16 rows are copied
+// straight into LDS by buffer loads with an LDS destination; an FP4 tile is
+// loaded into registers one step ahead and decoded to bf16 as it is written.
+// Latent row t holds its 16-byte chunk c at slot c ^ swz(t), which keeps the
+// score reads (16 tokens, one chunk) and the transposed P.V reads (4 tokens,
+// 4 chunks) free of bank conflicts; the RoPE keys of 8 tokens form one
+// chunk-major group after the latent rows.
 //
 // Tokens are split across workgroups (flash-decoding): the tiles of all
 // sequences, end to end, are dealt in equal contiguous runs to the W
@@ -31,31 +40,44 @@
 // and lse directly; a piece of a sequence is written as a partial (x_s
 // normalised, lse_s) and merged by the combine kernel:
 //   lse = log sum_s exp(lse_s),  x = sum_s exp(lse_s - lse) x_s.
-#include <type_traits>
-
 #include "internal.h"
 
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 1168;     // LDS bytes per token: 72 chunks of 16 B + 16 B padding
-constexpr int kSlotsPerRow = kRowBytes / 16;  // 73
-constexpr int kTileBytes = kTileTokens * kRowBytes;  // 74752
+constexpr int kThreads = 512;
+constexpr int kTile = kAttnTileTokens;                 // tokens per LDS tile
+constexpr int kLatRowBytes = 1024;                     // 512 bf16 latent channels
+constexpr int kRopeGroupBytes = 1152;                  // 8 tokens x 128 B, + 128 B pad
+constexpr int kRopeBase = kTile * kLatRowBytes;        // RoPE groups follow the latent rows
+constexpr int kTileBytes = kRopeBase + (kTile / 8) * kRopeGroupBytes;  // 37376
+constexpr int kRing = 4;                               // LDS tile buffers
+constexpr int kPSlotBytes = 2 * 2 * 64 * 16;           // [rb][kk][lane] bf16x8
+constexpr int kPBase = kRing * kTileBytes;
+struct Meta {
+  float alpha[kRowsPerGroup];  // factor on O before this tile's P.V
+  float l[kRowsPerGroup];      // running sum and max after this tile
+  float m[kRowsPerGroup];
+  int rescale[2];              // per row block: some alpha != 1
+  int pad[2];
+};
+constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
+constexpr int kSmemBytes = kMetaBase + 2 * (int)sizeof(Meta);
+constexpr int kDmaPerWave = kTile / 2 + 2;             // bf16 loads per load wave and tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.0f;  // p = 2^(s - m) stays <= 2^8
 
-struct Xchg {
-  uint4 p[4][64][2];  // bf16 probability fragments of each wave
-  float mx[4][32];    // per-row max of each wave's 32 tokens
-  float sum[4][32];   // per-row sum of each wave's probabilities
-  int flag[4];        // a wave saw a row whose max exceeds the reference by > kRescaleLog2
-};
-
-constexpr int kSmemBytes = 2 * kTileBytes + (int)sizeof(Xchg);
+static_assert(kTile == 32 && kRowsPerGroup == 64, "two 32x32 score blocks per tile");
+static_assert(kPageTokens % kTile == 0, "a tile never crosses a page");
+static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(int32x4_t rsrc, lds_void* lds, int size,
+                                                           int voffset, int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 __device__ __forceinline__ shortx4 tr_read(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
@@ -66,13 +88,22 @@ __device__ __forceinline__ bf16x8 join(shortx4 a, shortx4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Slot permutation of the 16-byte chunks of latent row t (an involution on
+// the low four bits of the chunk index).
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (lgkm and exp counters left alone).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ __forceinline__ int seq_len(const AttnParams& p, int b) {
   return clamp_len(p.seq_lens[b], p.cache.capacity);
 }
 
-__device__ __forceinline__ int tiles_of(int L) { return (L + kTileTokens - 1) / kTileTokens; }
+__device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
 
 // Block-wide exclusive scan of one int per thread. *total gets the block sum.
+template <int kBlock>
 __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -85,7 +116,7 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < kBlock / 64; ++w) {
     const int x = s_tmp[w];
     base += (w < wave) ? x : 0;
     tot += x;
@@ -95,33 +126,37 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return base + inc - v;
 }
 
-// First physical row of tile `tile` of sequence b (a tile is one 64-row page).
+// First physical row of attention tile `tile` of sequence b. A tile lies in
+// one page; a page index outside the cache sets `bad`.
 __device__ __forceinline__ int64_t tile_row0(const CacheView& c, int b, int tile, bool& bad) {
-  if (c.page_size == 0) return (int64_t)b * c.capacity + (int64_t)tile * kTileTokens;
-  const int page = c.page_table[(int64_t)b * c.pt_stride + tile];
-  const int64_t r0 = (int64_t)page * kTileTokens;
-  if (page < 0 || r0 + kTileTokens > c.num_rows) {
+  const int t0 = tile * kTile;
+  if (c.page_size == 0) return (int64_t)b * c.capacity + t0;
+  const int page = c.page_table[(int64_t)b * c.pt_stride + t0 / kPageTokens];
+  const int64_t p0 = (int64_t)page * kPageTokens;
+  if (page < 0 || p0 + kPageTokens > c.num_rows) {
     bad = true;
     return 0;
   }
-  return r0;
+  return p0 + t0 % kPageTokens;
 }
 
-// bf16 tiles go to LDS by direct buffer loads: one load instruction per
-// token moves its 1 KiB latent row (64 lanes x 16 B) to the token's LDS row,
-// and one with 8 active lanes moves its 128 B RoPE key behind it. Each buffer
-// descriptor spans exactly the tile's valid rows, so rows at or past `valid`
-// read as zero without touching memory, and no load can leave the tile. The
-// loads of tile i+1 are issued right after the barrier that opens tile i, and
-// each wave waits for its own loads before the barrier that opens tile i+1.
-typedef int int32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(int32x4_t rsrc, lds_void* lds, int size,
-                                                           int voffset, int soffset, int offset,
-                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Walks the tiles of a run: sequence b, tile index within it, its length.
+struct Cursor {
+  int b, tile, L;
+  __device__ void next(const AttnParams& p) {
+    ++tile;
+    if (tile >= tiles_of(L)) {
+      tile = 0;
+      do {
+        ++b;
+      } while (b < p.B && seq_len(p, b) == 0);
+      L = b < p.B ? seq_len(p, b) : 0;
+    }
+  }
+};
 
-// Raw buffer descriptor: base, stride 0, num_records bytes (loads at or past
-// it return zero).
+// Raw buffer descriptor: base, stride 0, num_records bytes; loads at or past
+// num_records return zero and touch no memory.
 __device__ __forceinline__ int32x4_t buffer_rsrc(const uint8_t* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   int32x4_t r;
@@ -132,51 +167,49 @@ __device__ __forceinline__ int32x4_t buffer_rsrc(const uint8_t* base, uint32_t b
   return r;
 }
 
-struct Bf16Stage {};  // nothing passes through registers
-
-__device__ __forceinline__ void load_tile_bf16(const CacheView& c, int64_t row0, int valid, int tid,
-                                               uint8_t* dst, Bf16Stage&) {
-  // The wave index is uniform; saying so keeps the offsets in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+// bf16 tile -> LDS by direct buffer loads. Load wave d moves latent rows
+// 16d .. 16d+15 (one 64-lane load of 1 KiB each; lane i fetches chunk
+// i ^ swz(t) into slot i) and RoPE groups 2d, 2d+1 (lane i: token 8g + i % 8,
+// chunk i / 8). The descriptors span exactly the tile's `valid` rows, so later
+// rows read as zero. Always kDmaPerWave instructions per load wave.
+__device__ __forceinline__ void dma_tile_bf16(const CacheView& c, int64_t row0, int valid, int d,
+                                              int lane, uint8_t* dst) {
   const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
   const uint32_t rs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.rope_stride);
   const int32x4_t lat = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * ls);
   const int32x4_t rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * rs);
 #pragma unroll
-  for (int n = 0; n < kTileTokens / 4; ++n) {
-    const int t = wave * (kTileTokens / 4) + n;
-    llvm_amdgcn_raw_buffer_load_lds(lat, (lds_void*)(dst + t * kRowBytes), 16, lane * 16,
-                                    (int)(t * ls), 0, 0);
+  for (int n = 0; n < kTile / 2; ++n) {
+    const int t = d * (kTile / 2) + n;
+    const int voff = (int)(t * ls) + ((lane ^ swz(t)) << 4);
+    llvm_amdgcn_raw_buffer_load_lds(lat, (lds_void*)(dst + t * kLatRowBytes), 16, voff, 0, 0, 0);
   }
-  if (lane < 8) {
 #pragma unroll
-    for (int n = 0; n < kTileTokens / 4; ++n) {
-      const int t = wave * (kTileTokens / 4) + n;
-      llvm_amdgcn_raw_buffer_load_lds(rope, (lds_void*)(dst + t * kRowBytes + 1024), 16, lane * 16,
-                                      (int)(t * rs), 0, 0);
-    }
+  for (int n = 0; n < 2; ++n) {
+    const int gr = 2 * d + n;
+    const int voff = (int)((gr * 8 + (lane & 7)) * rs) + ((lane >> 3) << 4);
+    llvm_amdgcn_raw_buffer_load_lds(rope, (lds_void*)(dst + kRopeBase + gr * kRopeGroupBytes), 16, voff,
+                                    0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_tile_bf16(uint8_t*, int, const Bf16Stage&) {}
-
-// FP4 tiles: per token 16 code chunks (32 channels each) with their 2 scale
-// bytes, and 8 RoPE chunks. Thread tid takes code chunks s = tid + 256*k
-// (token s >> 4, chunk s & 15) and RoPE chunks s = tid + 256*k (token s >> 3,
-// chunk s & 7); it decodes its codes (E2M1 value times E4M3 scale, exact in
-// bf16) when writing them to the bf16 tile.
+// FP4 tiles, staged by the two load waves (128 lanes, index dt): per token 16
+// code chunks (32 channels each) with their 2 scale bytes, and 8 RoPE chunks.
+// Lane dt takes code chunks s = dt + 128*k (token s >> 4, chunk s & 15) and
+// RoPE chunks s = dt + 128*k (token s >> 3, chunk s & 7); it decodes its codes
+// (E2M1 value times E4M3 scale, exact in bf16) when writing them to the bf16
+// tile. Rows at or past `valid` re-read the last valid row (masked, finite).
 struct Fp4Stage {
   uint4 codes[4];
   uint32_t scales[4];
   uint4 rope[2];
 };
 
-__device__ __forceinline__ void load_tile_fp4(const CacheView& c, int64_t row0, int valid, int tid,
+__device__ __forceinline__ void load_tile_fp4(const CacheView& c, int64_t row0, int valid, int dt,
                                               Fp4Stage& st) {
-  asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int s = tid + kThreads * k;
+    const int s = dt + 128 * k;
     const int64_t r = row0 + min(s >> 4, valid - 1);
     const int j = s & 15;
     st.codes[k] = *reinterpret_cast<const uint4*>(c.latent + r * c.latent_stride + j * 16);
@@ -184,16 +217,16 @@ __device__ __forceinline__ void load_tile_fp4(const CacheView& c, int64_t row0, 
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int s = tid + kThreads * k;
+    const int s = dt + 128 * k;
     const int64_t r = row0 + min(s >> 3, valid - 1);
     st.rope[k] = *reinterpret_cast<const uint4*>(c.rope + r * c.rope_stride + (s & 7) * 16);
   }
 }
 
-__device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int tid, const Fp4Stage& st) {
+__device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int dt, const Fp4Stage& st) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int s = tid + kThreads * k;
+    const int s = dt + 128 * k;
     const int t = s >> 4;
     const int j = s & 15;
     const float s0 = e4m3_to_f32(st.scales[k] & 0xffu);
@@ -209,14 +242,17 @@ __device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int tid, const Fp4S
         const float v1 = __uint_as_float(e2m1_f32_bits((words[qd] >> (8 * e + 4)) & 0xfu)) * sv;
         outw[e] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
       }
-      *reinterpret_cast<uint4*>(dst + t * kRowBytes + (4 * j + qd) * 16) =
+      const int slot = (4 * j + qd) ^ swz(t);
+      *reinterpret_cast<uint4*>(dst + t * kLatRowBytes + slot * 16) =
           make_uint4(outw[0], outw[1], outw[2], outw[3]);
     }
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int s = tid + kThreads * k;
-    *reinterpret_cast<uint4*>(dst + (s >> 3) * kRowBytes + (64 + (s & 7)) * 16) = st.rope[k];
+    const int s = dt + 128 * k;
+    const int t = s >> 3, ch = s & 7;
+    *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
+        st.rope[k];
   }
 }
 
@@ -235,20 +271,20 @@ __device__ __forceinline__ float xor32_sum(float x) {
 template <bool kFp4>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  __shared__ int s_tmp[8];
+  __shared__ int s_tmp[kThreads / 64];
   __shared__ int s_start[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
-  const int rh = wave & 1;   // row half of the block (32 rows)
-  const int th = wave >> 1;  // token half of a tile for S, channel half of O
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_score = wave < 2;
+  const bool is_load = wave == 4 || wave == 5;
 
   // Block -> (run wg, row block g). Consecutive block ids go to the 8 XCDs in
-  // turn; the G row blocks of one run share an XCD (and its L2), and are
-  // dispatched next to each other, so the cache tiles they both read come
-  // from HBM once.
+  // turn; the G row blocks of one run share an XCD (and its L2) and are
+  // dispatched next to each other, so the tiles they both read come from HBM
+  // once.
   const int G = p.groups;
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -264,7 +300,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   int my_tiles = 0;
   for (int b = b_lo; b < b_hi; ++b) my_tiles += tiles_of(seq_len(p, b));
   int total = 0;
-  const int base = block_exclusive_scan(my_tiles, s_tmp, &total);
+  const int base = block_exclusive_scan<kThreads>(my_tiles, s_tmp, &total);
   const int per = (total + p.workgroups - 1) / p.workgroups;
   const int start = wg * per;
   const int end = min(total, start + per);
@@ -283,126 +319,122 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  uint8_t* tiles = smem;  // two bf16 tiles: tile i of the run lives in buffer i & 1
-  Xchg* xc = reinterpret_cast<Xchg*>(smem + 2 * kTileBytes);
-
-  const int row_local = rh * 32 + (lane & 31);
-  const int row = g * 64 + row_local;
-  const bool row_ok = row < p.HQ;
-  const int row_c = row_ok ? row : 0;  // rows past HQ compute on row 0's query, never stored
-  const int qi = row_c % p.Q;
-  const int slots = 2 * p.workgroups;
   const int count = end - start;
+  const int slots = 2 * p.workgroups;
+  Cursor cur;
+  cur.b = __builtin_amdgcn_readfirstlane(s_start[0]);
+  cur.tile = __builtin_amdgcn_readfirstlane(s_start[1]);
+  cur.L = seq_len(p, cur.b);
 
-  // Current tile (b, tile) and the prefetch cursor (nb, ntile).
-  int b = __builtin_amdgcn_readfirstlane(s_start[0]);
-  int tile = __builtin_amdgcn_readfirstlane(s_start[1]);
-  int L = seq_len(p, b);
-  int nb = b, ntile = tile, nL = L;
-  auto advance = [&](int& bb, int& tt, int& LL) {
-    ++tt;
-    if (tt >= tiles_of(LL)) {
-      tt = 0;
-      do {
-        ++bb;
-      } while (bb < p.B && seq_len(p, bb) == 0);
-      LL = bb < p.B ? seq_len(p, bb) : 0;
-    }
-  };
-  using Stage = typename std::conditional<kFp4, Fp4Stage, Bf16Stage>::type;
-  auto stage_load = [&](int bb, int tt, int LL, uint8_t* dst, Stage& st, bool& bad) {
-    const int64_t r0 = tile_row0(p.cache, bb, tt, bad);
-    const int valid = bad ? 1 : min(kTileTokens, LL - tt * kTileTokens);
-    if constexpr (kFp4) {
-      (void)dst;
-      load_tile_fp4(p.cache, r0, valid, tid, st);
-    } else {
-      load_tile_bf16(p.cache, r0, valid, tid, dst, st);
-    }
-  };
-  auto stage_store = [&](uint8_t* dst, const Stage& st) {
-    if constexpr (kFp4) {
-      store_tile_fp4(dst, tid, st);
-    } else {
-      store_tile_bf16(dst, tid, st);
-    }
-  };
+  uint8_t* const ptiles = smem + kPBase;
+  Meta* const metas = reinterpret_cast<Meta*>(smem + kMetaBase);
 
-  // Stage tile 0 of the run into buffer 0 (visible after the first barrier).
-  bool bad_cur = false;
-  {
-    Stage st;
-    stage_load(b, tile, L, tiles, st, bad_cur);
-    stage_store(tiles, st);
-  }
-
-  int it = 0;
-  bool first_seg = true;
-  while (it < count) {
-    // ---- one segment: tiles [seg_lo, seg_lo + seg_n) of sequence seg_b ----
-    const int seg_b = b;
-    const int seg_L = L;
-    const int nt = tiles_of(seg_L);
-    const int seg_lo = tile;
-    const int seg_n = min(count - it, nt - seg_lo);
-    const int vis = seg_L - p.Q + qi + 1;  // this row sees tokens t < vis
-
-    // Q fragments (B operand of S^T = K Qcat^T): row `row_c`, channels
-    // 16*ks + 8*hi .. +7 of [q_lat | q_pe].
-    bf16x8 qf[36];
-    {
-      const int64_t grow = (int64_t)seg_b * p.HQ + row_c;
-      const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) + grow * 512 + 8 * hi);
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) + grow * 64 + 8 * hi);
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
-      // Park the fragments in AGPRs (the matrix ops read them there), which
-      // leaves the VGPRs to the accumulators and the LDS read pipelines.
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) asm volatile("" : "+a"(qf[ks]));
-    }
-    floatx16 o[8];
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) o[cb] = floatx16{};
-    float m = -INFINITY, l = 0.0f;
-    int seg_bad = 0;
-
-    for (int j = 0; j < seg_n; ++j, ++it) {
-      seg_bad |= bad_cur ? 1 : 0;
-      const int cur_tile = seg_lo + j;
-
-      // Tile `it` is in LDS for every wave (each wave's own loads have
-      // landed), and every wave is done with tile it-1, whose buffer
-      // receives tile it+1 below.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-
-      bool bad_nxt = false;
-      const bool has_next = it + 1 < count;
-      Stage st;
-      if (has_next) {
-        advance(nb, ntile, nL);
-        stage_load(nb, ntile, nL, tiles + ((it + 1) & 1) * kTileBytes, st, bad_nxt);
+  if (is_load) {
+    // ================= load waves =================
+    const int d = wave - 4;
+    const int dt = tid - 256;
+    Cursor ic = cur;
+    int issued = 0;
+    Fp4Stage st;
+    auto issue = [&]() {
+      bool bad = false;
+      const int64_t r0 = tile_row0(p.cache, ic.b, ic.tile, bad);
+      const int valid = bad ? 1 : min(kTile, ic.L - ic.tile * kTile);
+      if constexpr (kFp4) {
+        load_tile_fp4(p.cache, r0, valid, dt, st);
+      } else {
+        dma_tile_bf16(p.cache, r0, valid, d, lane, smem + (issued % kRing) * kTileBytes);
       }
-      const uint8_t* tb = tiles + (it & 1) * kTileBytes;
+      ++issued;
+      ic.next(p);
+    };
+    // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in registers).
+    if constexpr (kFp4) {
+      issue();
+      store_tile_fp4(smem, dt, st);
+      if (issued < count) issue();
+    } else {
+      issue();
+      if (issued < count) issue();
+    }
+    for (int k = 0; k <= count; ++k) {
+      if constexpr (!kFp4) {
+        // Tile k has landed (tile k+1 may still be in flight).
+        if (k < count) {
+          if (issued > k + 1) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerWave));
+          } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          }
+        }
+      }
+      __syncthreads();  // step k
+      if constexpr (kFp4) {
+        // Decode tile k+1 (its buffer held tile k-3), then fetch tile k+2.
+        if (k + 1 < count) {
+          store_tile_fp4(smem + ((k + 1) % kRing) * kTileBytes, dt, st);
+          if (issued < count) issue();
+        }
+      } else {
+        // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
+        if (issued < count) issue();
+      }
+    }
+  } else if (is_score) {
+    // ================= score waves: S^T, softmax, probabilities =================
+    const int rb = wave;
+    const int row_local = rb * 32 + (lane & 31);
+    const int row = g * kRowsPerGroup + row_local;
+    const bool rows_on = g * kRowsPerGroup + rb * 32 < p.HQ;  // uniform
+    const int row_c = row < p.HQ ? row : 0;  // rows past HQ compute on row 0's query, never stored
+    const int qi = row_c % p.Q;
+    // Score reads (A = K): token t = lane % 32, chunk 2*ks + hi; for ks < 32
+    // at qk_off[ks % 8] + 256 * (ks / 8), RoPE k-steps at rope_off + 256 * (ks - 32).
+    const int tq = lane & 31;
+    int qk_off[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qk_off[j] = tq * kLatRowBytes + (((2 * j + hi) ^ swz(tq)) << 4);
+    const int rope_off = kRopeBase + (tq >> 3) * kRopeGroupBytes + hi * 128 + (tq & 7) * 16;
 
-      // ---- S^T block: tokens 32*th .. +31 of the tile x rows 32*rh .. +31 ----
-      // K fragments run four reads ahead of the matrix ops; the k-steps
-      // chain on one accumulator.
-      floatx16 s;
+    Cursor sc = cur;
+    bf16x8 qf[36];
+    float m = -INFINITY, l = 0.0f;
+    for (int k = 0; k <= count; ++k) {
+      __syncthreads();  // step k
+      if (k == count || !rows_on) continue;
+      if (k == 0 || sc.tile == 0) {
+        // New segment: query fragments of sequence sc.b (B operand of
+        // S^T = K Qcat^T): row `row_c`, channels 16*ks + 8*hi .. +7 of [q_lat | q_pe].
+        const int64_t grow = (int64_t)sc.b * p.HQ + row_c;
+        const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
+                                                           grow * 512 + 8 * hi);
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
+                                                           grow * 64 + 8 * hi);
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
+        m = -INFINITY;
+        l = 0.0f;
+      }
+      const uint8_t* tb = smem + (k % kRing) * kTileBytes;
+
+      // ---- S^T block: the tile's 32 tokens x this wave's 32 rows ----
+      // K fragments run four reads ahead of the matrix ops; the k-steps chain
+      // on one accumulator.
+      floatx16 s = floatx16{};
       {
-        const uint8_t* kb = tb + (32 * th + (lane & 31)) * kRowBytes + hi * 16;
+        auto kaddr = [&](int ks) {
+          return ks < 32 ? tb + qk_off[ks & 7] + 256 * (ks >> 3) : tb + rope_off + 256 * (ks - 32);
+        };
         bf16x8 ka[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kb + u * 32);
-        s = floatx16{};
+        for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
           const bf16x8 a = ka[ks & 3];
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-          if (ks + 4 < 36) ka[ks & 3] = *reinterpret_cast<const bf16x8*>(kb + (ks + 4) * 32);
+          if (ks + 4 < 36) ka[ks & 3] = *reinterpret_cast<const bf16x8*>(kaddr(ks + 4));
         }
         // Issue order: the four leading reads, then matrix op / next read pairs.
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -415,168 +447,188 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
 
       // ---- online softmax in the log2 domain; lane holds row `row` ----
-      const int tok0 = cur_tile * kTileTokens + 32 * th + 4 * hi;
-      float own_mx = -INFINITY;
+      const int vis = sc.L - p.Q + qi + 1;  // this row sees tokens t < vis
+      const int tok0 = sc.tile * kTile + 4 * hi;
+      float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tok = tok0 + 8 * (i >> 2) + (i & 3);
         const float v = tok < vis ? s[i] * p.scale_log2 : -INFINITY;
         s[i] = v;
-        own_mx = fmaxf(own_mx, v);
+        mx = fmaxf(mx, v);
       }
-      own_mx = xor32_max(own_mx);
-      // The reference m moves only when a row max exceeds it by > kRescaleLog2,
-      // so O is rarely rescaled and every probability stays <= 2^kRescaleLog2.
-      const bool ovf = own_mx > m + kRescaleLog2;
-      float m_use = m == -INFINITY ? 0.0f : m;
-      float own_sum = 0.0f;
+      mx = xor32_max(mx);
+      // The reference m moves only when a row max exceeds it by more than
+      // kRescaleLog2, so O is rarely rescaled and p stays <= 2^kRescaleLog2.
+      const bool upd = mx > m + kRescaleLog2;
+      const float m_new = upd ? mx : m;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+      l *= alpha;
+      m = m_new;
+      const float m_use = m == -INFINITY ? 0.0f : m;
+      float rs = 0.0f;
       bf16x8 pf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
-        own_sum += e;
+        rs += e;
         pf[i >> 3][i & 7] = (__bf16)e;
       }
-      own_sum = xor32_sum(own_sum);
-      const int pw = wave ^ 2;  // the other token half of this row half
-      *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][0]) = pf[0];
-      *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][1]) = pf[1];
+      l += xor32_sum(rs);
+
+      // Probabilities in the P.V B-operand layout [rb][kk][lane]: k-step kk
+      // covers tokens 16*kk + 4*hi + {0..3} and +8 + {0..3}, which are exactly
+      // this lane's pf[kk].
+      uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048;
+      *reinterpret_cast<bf16x8*>(ps + lane * 16) = pf[0];
+      *reinterpret_cast<bf16x8*>(ps + 1024 + lane * 16) = pf[1];
+      Meta* mt = metas + (k & 1);
       if (hi == 0) {
-        xc->mx[wave][lane] = own_mx;
-        xc->sum[wave][lane] = own_sum;
+        mt->alpha[row_local] = alpha;
+        mt->l[row_local] = l;
+        mt->m[row_local] = m;
       }
-      const bool wave_ovf = __any(ovf);
-      if (lane == 0) xc->flag[wave] = wave_ovf ? 1 : 0;
-      __syncthreads();
-      const int any_ovf = xc->flag[0] | xc->flag[1] | xc->flag[2] | xc->flag[3];
-      if (any_ovf) {
-        // A row max rose: move the reference to the new max (both token halves
-        // agree on it), recompute this wave's probabilities, rescale O and l.
-        const float mx = fmaxf(own_mx, xc->mx[pw][lane & 31]);
-        const bool upd = mx > m + kRescaleLog2;
-        const float m_new = upd ? mx : m;
-        const float alpha = upd ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-        m_use = m_new == -INFINITY ? 0.0f : m_new;
-        own_sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
-          own_sum += e;
-          pf[i >> 3][i & 7] = (__bf16)e;
-        }
-        own_sum = xor32_sum(own_sum);
-        __syncthreads();  // every wave has read the old max and flags
-        *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][0]) = pf[0];
-        *reinterpret_cast<bf16x8*>(&xc->p[wave][lane][1]) = pf[1];
-        if (hi == 0) xc->sum[wave][lane] = own_sum;
-        if (__any(upd && m != -INFINITY)) {
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
-        }
-        l *= alpha;
-        m = m_new;
-        __syncthreads();
-      }
-      const float psum = xc->sum[pw][lane & 31];
-      l += th == 0 ? own_sum + psum : psum + own_sum;
-      bf16x8 pp[2];
-      pp[0] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][0]);
-      pp[1] = *reinterpret_cast<const bf16x8*>(&xc->p[pw][lane][1]);
-      // Token half 0 probabilities come from the th = 0 wave, half 1 from th = 1.
-      bf16x8 pk[4];
-      pk[0] = th == 0 ? pf[0] : pp[0];
-      pk[1] = th == 0 ? pf[1] : pp[1];
-      pk[2] = th == 0 ? pp[0] : pf[0];
-      pk[3] = th == 0 ? pp[1] : pf[1];
-
-      // ---- O^T[c, r] += C^T[c, t] P^T[t, r] for this wave's 256 channels ----
-      // A operand (k-step kk): channel lane%32 of the block, tokens
-      // 16*kk + 4*hi + {0..3} and +8 + {0..3}, by two transposed LDS reads of
-      // a 4 x 16 block each (16-lane groups: lane j -> row j/4, cols 4*(j%4)).
-      // The 8 channel blocks of a k-step are independent accumulators.
-      {
-        const int jj = lane & 15;
-        const uint8_t* vb = tb + (4 * hi + (jj >> 2)) * kRowBytes +
-                            (256 * th + 16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint8_t* vk = vb + 16 * kk * kRowBytes;
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
-            const bf16x8 a = join(tr_read(vk + cb * 64), tr_read(vk + cb * 64 + 8 * kRowBytes));
-            o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[cb], 0, 0, 0);
-          }
-        }
-      }
-
-      // The prefetched registers go to the other buffer.
-      if (has_next) stage_store(tiles + ((it + 1) & 1) * kTileBytes, st);
-      bad_cur = bad_nxt;
+      const bool any_upd = __any(upd);
+      if (lane == 0) mt->rescale[rb] = any_upd ? 1 : 0;
+      sc.next(p);
     }
-
-    // ---- end of the segment: write x / lse, or a partial for the combine ----
+  } else {
+    // ================= P.V waves: O^T for 128 channels of all 64 rows =================
+    const int cq = (wave & 1) | ((wave >> 2) << 1);
+    // Transposed reads (A = C^T): 16-lane group reads a 4 x 16 block; lane j
+    // of the group addresses token row j / 4 (+ 4*hi, + 8 for the second read)
+    // and channels 32*cb + 16*g16 + 4*(j % 4) .. +3 of the quarter, at
+    // tr_off[s][cb] + 256 * cq + 16384 * kk.
+    int tr_off[2][4];
     {
-      const bool whole = seg_lo == 0 && seg_lo + seg_n == nt;
-      const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-      const float nanv = __uint_as_float(0x7fc00000u);
-      float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-      if (seg_bad) lse_v = nanv;
-      if (row_ok) {
-        if (whole) {
-          uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + ((int64_t)seg_b * p.HQ + row) * 512;
+      const int j = lane & 15, g16 = (lane >> 4) & 1;
+      const int low2 = 2 * g16 + ((j & 3) >> 1);
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
+      for (int s = 0; s < 2; ++s) {
+        const int t = 4 * hi + (j >> 2) + 8 * s;
+        const int f = swz(t);
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const int c = 256 * th + 32 * cb + 8 * i4 + 4 * hi;
-              float v[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = seg_bad ? nanv : o[cb][4 * i4 + e] * inv_l;
-              *reinterpret_cast<uint2*>(xo + c) =
-                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-          }
-          if (p.lse != nullptr && hi == 0 && th == 0) p.lse[(int64_t)seg_b * p.HQ + row] = lse_v;
-        } else {
-          const int slot = 2 * wg + (first_seg ? 0 : 1);
-          const int64_t prow = ((int64_t)g * slots + slot) * 64 + row_local;
-          float* xo = p.part_x + prow * 512;
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const int c = 256 * th + 32 * cb + 8 * i4 + 4 * hi;
-              float4 v;
-              v.x = o[cb][4 * i4 + 0] * inv_l;
-              v.y = o[cb][4 * i4 + 1] * inv_l;
-              v.z = o[cb][4 * i4 + 2] * inv_l;
-              v.w = o[cb][4 * i4 + 3] * inv_l;
-              *reinterpret_cast<float4*>(xo + c) = v;
-            }
-          }
-          if (hi == 0 && th == 0) p.part_lse[prow] = lse_v;
+        for (int c3 = 0; c3 < 4; ++c3) {
+          tr_off[s][c3] =
+              t * kLatRowBytes + ((((c3 ^ (f >> 2)) << 2) | (low2 ^ (f & 3))) << 4) + 8 * (j & 1) + 256 * cq;
         }
       }
-      first_seg = false;
     }
-    // The next segment starts at the prefetch cursor (tile 0 of a later sequence).
-    b = nb;
-    tile = ntile;
-    L = nL;
+
+    Cursor pc = cur;
+    int seg_lo = pc.tile;
+    int seg_bad = 0;
+    bool first_seg = true;
+    floatx16 o[8];  // [rb * 4 + cb]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+    for (int k = 0; k <= count; ++k) {
+      __syncthreads();  // step k
+      if (k == 0) continue;
+      const int kt = k - 1;  // tile of this step
+      {
+        bool bad = false;
+        (void)tile_row0(p.cache, pc.b, pc.tile, bad);
+        seg_bad |= bad ? 1 : 0;
+      }
+      const Meta* mt = metas + (kt & 1);
+      if (mt->rescale[0] | mt->rescale[1]) {
+        const float a0 = mt->alpha[lane & 31];
+        const float a1 = mt->alpha[32 + (lane & 31)];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          o[cb] *= a0;
+          o[4 + cb] *= a1;
+        }
+      }
+      const uint8_t* tb = smem + (kt % kRing) * kTileBytes;
+      const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps + kk * 1024 + lane * 16);
+        const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048 + kk * 1024 + lane * 16);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint8_t* a0 = tb + 16384 * kk;
+          const bf16x8 a = join(tr_read(a0 + tr_off[0][cb]), tr_read(a0 + tr_off[1][cb]));
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, o[cb], 0, 0, 0);
+          o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, o[4 + cb], 0, 0, 0);
+        }
+      }
+
+      const int nt = tiles_of(pc.L);
+      if (pc.tile == nt - 1 || k == count) {
+        // ---- end of the segment: write x / lse, or a partial for the combine ----
+        const bool whole = seg_lo == 0 && pc.tile == nt - 1;
+        const float nanv = __uint_as_float(0x7fc00000u);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int row_local = rb * 32 + (lane & 31);
+          const int row = g * kRowsPerGroup + row_local;
+          if (row >= p.HQ) continue;
+          const float l = mt->l[row_local];
+          const float m = mt->m[row_local];
+          const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+          float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+          if (seg_bad) lse_v = nanv;
+          if (whole) {
+            uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + ((int64_t)pc.b * p.HQ + row) * 512;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int c = 128 * cq + 32 * cb + 8 * i4 + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = seg_bad ? nanv : o[rb * 4 + cb][4 * i4 + e] * inv_l;
+                *reinterpret_cast<uint2*>(xo + c) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              }
+            }
+            if (p.lse != nullptr && cq == 0 && hi == 0) p.lse[(int64_t)pc.b * p.HQ + row] = lse_v;
+          } else {
+            const int slot = 2 * wg + (first_seg ? 0 : 1);
+            const int64_t prow = ((int64_t)g * slots + slot) * kRowsPerGroup + row_local;
+            float* xo = p.part_x + prow * 512;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int c = 128 * cq + 32 * cb + 8 * i4 + 4 * hi;
+                float4 v;
+                v.x = o[rb * 4 + cb][4 * i4 + 0] * inv_l;
+                v.y = o[rb * 4 + cb][4 * i4 + 1] * inv_l;
+                v.z = o[rb * 4 + cb][4 * i4 + 2] * inv_l;
+                v.w = o[rb * 4 + cb][4 * i4 + 3] * inv_l;
+                *reinterpret_cast<float4*>(xo + c) = v;
+              }
+            }
+            if (cq == 0 && hi == 0) p.part_lse[prow] = lse_v;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+        first_seg = false;
+        seg_bad = 0;
+        seg_lo = 0;
+      }
+      pc.next(p);
+    }
   }
 }
 
 // Merge partial results of sequences whose tiles were split over workgroups,
 // and write x = 0 / lse = -inf for sequences without any cache rows.
 // Grid: (B, groups * 4); each block handles 16 query rows of one sequence.
-__global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnParams p) {
-  __shared__ int s_tmp[8];
+constexpr int kCombineThreads = 256;
+__global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParams p) {
+  __shared__ int s_tmp[kCombineThreads / 64];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int g = blockIdx.y >> 2;
   const int rb = blockIdx.y & 3;
 
-  const int per_thread = (p.B + kThreads - 1) / kThreads;
+  const int per_thread = (p.B + kCombineThreads - 1) / kCombineThreads;
   const int b_lo = min(p.B, tid * per_thread);
   const int b_hi = min(p.B, b_lo + per_thread);
   int my_tiles = 0;
@@ -587,13 +639,13 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnParams p) {
     if (j < b) before += n;
   }
   int cum_b = 0;
-  block_exclusive_scan(before, s_tmp, &cum_b);
+  block_exclusive_scan<kCombineThreads>(before, s_tmp, &cum_b);
   int total_tiles = 0;
-  block_exclusive_scan(my_tiles, s_tmp, &total_tiles);
+  block_exclusive_scan<kCombineThreads>(my_tiles, s_tmp, &total_tiles);
   const int nb = tiles_of(seq_len(p, b));
 
   const int row_local = rb * 16 + (tid >> 4);
-  const int row = g * 64 + row_local;
+  const int row = g * kRowsPerGroup + row_local;
   const int c0 = (tid & 15) * 32;
   if (row >= p.HQ) return;
   const int64_t grow = (int64_t)b * p.HQ + row;
@@ -612,10 +664,11 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnParams p) {
 
   const int slots = 2 * p.workgroups;
   auto slot_of = [&](int i) { return 2 * i + ((i == i_first && cum_b != i_first * per) ? 1 : 0); };
+  auto prow_of = [&](int i) { return ((int64_t)g * slots + slot_of(i)) * kRowsPerGroup + row_local; };
   float mx = -INFINITY;
   bool any_nan = false;
   for (int i = i_first; i <= i_last; ++i) {
-    const float v = p.part_lse[((int64_t)g * slots + slot_of(i)) * 64 + row_local];
+    const float v = p.part_lse[prow_of(i)];
     any_nan |= v != v;
     mx = fmaxf(mx, v);
   }
@@ -631,12 +684,10 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnParams p) {
     lse_v = -INFINITY;
   } else {
     float tot = 0.0f;
-    for (int i = i_first; i <= i_last; ++i) {
-      tot += __expf(p.part_lse[((int64_t)g * slots + slot_of(i)) * 64 + row_local] - mx);
-    }
+    for (int i = i_first; i <= i_last; ++i) tot += __expf(p.part_lse[prow_of(i)] - mx);
     lse_v = mx + __logf(tot);
     for (int i = i_first; i <= i_last; ++i) {
-      const int64_t prow = ((int64_t)g * slots + slot_of(i)) * 64 + row_local;
+      const int64_t prow = prow_of(i);
       const float w = __expf(p.part_lse[prow] - lse_v);
       if (w == 0.0f) continue;
       const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
@@ -669,7 +720,8 @@ hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, hipStream_t s)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B, p.groups * 4), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B, p.groups * (kRowsPerGroup / 16)),
+                     dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 

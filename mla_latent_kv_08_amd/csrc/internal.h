@@ -9,11 +9,15 @@
 
 namespace mla {
 
-// Rows of query (h, q) handled by one attention workgroup on the matrix-core path.
+// Rows of query (h, q) handled by one attention workgroup on the matrix-core
+// path (two blocks of 32 rows).
 constexpr int kRowsPerGroup = 64;
-constexpr int kTileTokens = 64;
-// Largest row stride (bytes) of any cache array: a 64-row tile then spans less
-// than 2^31 bytes, so tile loads use 32-bit offsets from the tile's first row.
+// Cache page size (tokens) of the paged layout.
+constexpr int kPageTokens = 64;
+// Tokens per LDS tile of the matrix-core attention (half a page).
+constexpr int kAttnTileTokens = 32;
+// Largest row stride (bytes) of any cache array: a page of rows then spans
+// less than 2^31 bytes, so tile loads use 32-bit offsets from a tile's first row.
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 struct AttnParams {
@@ -23,10 +27,10 @@ struct AttnParams {
   const int32_t* seq_lens;
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
-  float* part_x;    // [G, 2W, 64, Ckv] fp32 partial results
-  float* part_lse;  // [G, 2W, 64]
+  float* part_x;    // [G, 2W, kRowsPerGroup, Ckv] fp32 partial results
+  float* part_lse;  // [G, 2W, kRowsPerGroup]
   int B, H, Q, HQ, Ckv, Dr;
-  int groups;      // G = ceil(HQ / 64)
+  int groups;      // G = ceil(HQ / kRowsPerGroup)
   int workgroups;  // W per row group
   float scale_log2;  // softmax_scale * log2(e)
 };

@@ -12,7 +12,8 @@
 namespace {
 
 using mla::kRowsPerGroup;
-using mla::kTileTokens;
+using mla::kAttnTileTokens;
+using mla::kPageTokens;
 
 constexpr int kMaxDevices = 64;
 
@@ -77,9 +78,9 @@ int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t
   if (c->page_size == 0) {
     if (c->page_table != nullptr) return MLA_ERR_INVALID_ARG;
     if ((int64_t)batch * c->capacity > c->num_rows) return MLA_ERR_INVALID_ARG;
-  } else if (c->page_size == kTileTokens) {
+  } else if (c->page_size == kPageTokens) {
     if (c->page_table == nullptr || c->page_table_stride <= 0) return MLA_ERR_INVALID_ARG;
-    if ((int64_t)c->page_table_stride * kTileTokens < c->capacity) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)c->page_table_stride * kPageTokens < c->capacity) return MLA_ERR_INVALID_ARG;
   } else {
     return MLA_ERR_UNSUPPORTED;
   }
@@ -109,7 +110,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 int attn_workgroups(const mla_dims* d, int32_t max_seq_len, const mla_decode_opts* opts, int cus) {
   const int64_t hq = (int64_t)d->heads * d->q_len;
   const int groups = (int)((hq + kRowsPerGroup - 1) / kRowsPerGroup);
-  const int64_t max_tiles = (int64_t)d->batch * ((std::max(max_seq_len, 0) + kTileTokens - 1) / kTileTokens);
+  const int64_t max_tiles =
+      (int64_t)d->batch * ((std::max(max_seq_len, 0) + kAttnTileTokens - 1) / kAttnTileTokens);
   if (opts != nullptr && opts->workgroups > 0) return opts->workgroups;
   // One workgroup per compute unit over all row groups, but at least 4 tiles each.
   int64_t w = std::max<int64_t>(1, cus / groups);
