@@ -665,41 +665,66 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   const int slots = 2 * p.workgroups;
   auto slot_of = [&](int i) { return 2 * i + ((i == i_first && cum_b != i_first * per) ? 1 : 0); };
   auto prow_of = [&](int i) { return ((int64_t)g * slots + slot_of(i)) * kRowsPerGroup + row_local; };
-  float mx = -INFINITY;
-  bool any_nan = false;
-  for (int i = i_first; i <= i_last; ++i) {
-    const float v = p.part_lse[prow_of(i)];
-    any_nan |= v != v;
-    mx = fmaxf(mx, v);
-  }
+  // Partials in batches of four, all loads of a batch in flight together;
+  // running max M, sum S and weighted sum acc (rescaled when M rises):
+  //   lse = M + log S,  x = acc / S.
+  constexpr int kBatch = 4;
   float acc[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+  float M = -INFINITY, S = 0.0f;
+  bool any_nan = false;
+  for (int i0 = i_first; i0 <= i_last; i0 += kBatch) {
+    float ls[kBatch];
+    float4 xv[kBatch][8];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = i0 + u <= i_last;
+      const int64_t prow = prow_of(in ? i0 + u : i_first);
+      ls[u] = p.part_lse[prow];
+      if (!in) ls[u] = -INFINITY;
+      const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xv[u][k] = src[k];
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      any_nan |= ls[u] != ls[u];
+      bm = fmaxf(bm, ls[u]);
+    }
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;
+    const float sc = __expf(M - Mn);  // 0 while M is -inf
+    S *= sc;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] *= sc;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
+      S += w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[4 * k + 0] += w * xv[u][k].x;
+        acc[4 * k + 1] += w * xv[u][k].y;
+        acc[4 * k + 2] += w * xv[u][k].z;
+        acc[4 * k + 3] += w * xv[u][k].w;
+      }
+    }
+    M = Mn;
+  }
   float lse_v;
   if (any_nan) {
     lse_v = __uint_as_float(0x7fc00000u);
 #pragma unroll
     for (int k = 0; k < 32; ++k) acc[k] = lse_v;
-  } else if (mx == -INFINITY) {
+  } else if (M == -INFINITY) {
     lse_v = -INFINITY;
   } else {
-    float tot = 0.0f;
-    for (int i = i_first; i <= i_last; ++i) tot += __expf(p.part_lse[prow_of(i)] - mx);
-    lse_v = mx + __logf(tot);
-    for (int i = i_first; i <= i_last; ++i) {
-      const int64_t prow = prow_of(i);
-      const float w = __expf(p.part_lse[prow] - lse_v);
-      if (w == 0.0f) continue;
-      const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
+    lse_v = M + __logf(S);
+    const float inv = 1.0f / S;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float4 v = src[k];
-        acc[4 * k + 0] += w * v.x;
-        acc[4 * k + 1] += w * v.y;
-        acc[4 * k + 2] += w * v.z;
-        acc[4 * k + 3] += w * v.w;
-      }
-    }
+    for (int k = 0; k < 32; ++k) acc[k] *= inv;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
