@@ -54,6 +54,69 @@ def load_traffic(bytes_alg: float):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20  # size of the calibration copy (read and written once each)
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "attn_decode_dsv3_bf16_traffic.json")
+
+
+def _counter_values(run_dir: str, counter: str) -> dict:
+    """Values (KiB) of one rocprofv3 counter per kernel name, one per dispatch."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    values = {}
+    for (name, _), v in per.items():
+        values.setdefault(name, []).append(v)
+    return values
+
+
+def summarize_counters(fetch_dir: str, write_dir: str):
+    """Scale FETCH_SIZE / WRITE_SIZE of the attention call by what the same counters
+    read for the calibration copy, and store the HBM bytes per launch."""
+    fetch = _counter_values(fetch_dir, "FETCH_SIZE")
+    write = _counter_values(write_dir, "WRITE_SIZE")
+
+    def values(d, key):
+        hits = [v for k, vs in d.items() if key in k for v in vs]
+        if not hits:
+            raise SystemExit(f"no dispatch matching {key!r}")
+        return hits
+
+    def pick(d, key):  # mean over the dispatches of a kernel
+        v = values(d, key)
+        return sum(v) / len(v)
+
+    # The calibration copy is the largest copy dispatch of the run (smaller
+    # ones upload the inputs).
+    copy_kib = COPY_BYTES / 1024.0
+    f_factor = copy_kib / max(values(fetch, "copyBuffer"))
+    w_factor = copy_kib / max(values(write, "copyBuffer"))
+    attn_f = pick(fetch, "attn_mfma_kernel<false>") * 1024.0 * f_factor
+    attn_w = pick(write, "attn_mfma_kernel<false>") * 1024.0 * w_factor
+    comb_f = pick(fetch, "attn_combine_kernel") * 1024.0 * f_factor
+    comb_w = pick(write, "attn_combine_kernel") * 1024.0 * w_factor
+    rec = {
+        "kernel_source_hash": kernel_source_hash(),
+        "hbm_bytes_per_launch": attn_f + attn_w + comb_f + comb_w,
+        "attention_kernel": {"fetch_bytes": attn_f, "write_bytes": attn_w},
+        "merge_kernel": {"fetch_bytes": comb_f, "write_bytes": comb_w},
+        "fetch_scale": f_factor, "write_scale": w_factor,
+        "calibration": f"one {COPY_BYTES} B device-to-device copy in the same process",
+    }
+    with open(TRAFFIC_PATH, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, inp, budget_s: float = 15.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
     from oracle import mla_ref
@@ -86,7 +149,15 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (>= 3 defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workgroups", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one device-to-device copy of COPY_BYTES (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calibrate-copy run into the traffic record under profiles/, then exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU form of this "
               "path is a design note, not part of this build.", file=sys.stderr)
@@ -126,6 +197,13 @@ def main():
     ws_bytes = ops.mla_decode_workspace_size(B, H, Q, ops.MLA_BF16, max_len, args.workgroups)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
 
