@@ -51,12 +51,28 @@ __global__ void __launch_bounds__(kThreads) up_f32_kernel(ProjParams p) {
 // ---------------------------------------------------------------------------
 // bf16 on matrix cores (Dn = Vd = 128, Ckv = 512)
 // ---------------------------------------------------------------------------
-// Absorb. grid (H, Ckv/128); 4 waves, wave w owns latent channels
-// c0 + 32w .. +31. D[m = (b,q) row][n = channel] = sum_d q_nope[m][d] W_UK[d][n].
-// W_UK's contraction index d is its slow axis, so the 128 x 128 weight block is
-// staged in LDS and read down its columns to build the B operand.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ bf16x8 tr_pair(const uint16_t* a, const uint16_t* b) {
+  const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(a));
+  const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(b));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Absorb, transposed: q_lat^T[c][m] = sum_d W_UK[d][c] q_nope^T[d][m] for one
+// head and 128 latent channels. grid (H, Ckv/128). The head's 128 x 128 W_UK
+// block and 32 query rows at a time go through LDS with row-contiguous
+// loads; W_UK is read as the A operand (m = c, k = d) by transposed reads,
+// the query rows as the B operand (k = d contiguous). Wave w owns channels
+// c0 + 32w .. +31; results return through LDS so each output row leaves as
+// contiguous 16-byte stores.
+constexpr int kWPad = 144;  // W_UK block row pitch (elements)
+constexpr int kQPad = 136;  // query / output row pitch (elements)
 __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[128 * 136];  // [d][c], padded rows
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[128 * kWPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[32 * kQPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * kQPad];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
   const int h = blockIdx.x;
   const int c0 = blockIdx.y * 128;
@@ -65,78 +81,127 @@ __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
   for (int k = 0; k < 128 * 16 / kThreads; ++k) {
     const int s = tid + kThreads * k;  // 16-byte chunk: row d, chunk j
     const int d = s >> 4, j = s & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(w + (int64_t)d * p.Ckv + c0 + 8 * j);
-    *reinterpret_cast<uint4*>(s_w + d * 136 + 8 * j) = v;
-  }
-  __syncthreads();
-  // B fragments: n = c0 + 32*wave + lane%32, k = d = 16*ks + 8*hi + j.
-  bf16x8 bf[8];
-  const int nloc = 32 * wave + (lane & 31);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf[ks][j] = *reinterpret_cast<const __bf16*>(s_w + (16 * ks + 8 * hi + j) * 136 + nloc);
-    }
+    *reinterpret_cast<uint4*>(s_w + d * kWPad + 8 * j) =
+        *reinterpret_cast<const uint4*>(w + (int64_t)d * p.Ckv + c0 + 8 * j);
   }
   const int M = p.B * p.Q;
+  // Query rows are [B, H, Q, Dn]: row m = (b, q) of head h.
+  auto q_row = [&](int m) {
+    const int bb = m / p.Q, qq = m % p.Q;
+    return ((int64_t)bb * p.H + h) * p.Q + qq;
+  };
+  // Stage thread tid: row tid / 8 of the block, 16 elements at 16 * (tid % 8).
+  const int sr = tid >> 3, sc = 16 * (tid & 7);
   for (int m0 = 0; m0 < M; m0 += 32) {
-    const int m = m0 + (lane & 31);
-    const bool ok = m < M;
-    const int bb = ok ? m / p.Q : 0, qq = ok ? m % p.Q : 0;
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.in) + (((int64_t)bb * p.H + h) * p.Q + qq) * p.Dn;
-    floatx16 acc = floatx16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a = ok ? *reinterpret_cast<const bf16x8*>(q + 16 * ks + 8 * hi) : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[ks], acc, 0, 0, 0);
+    {
+      const int m = min(m0 + sr, M - 1);
+      const uint16_t* q = reinterpret_cast<const uint16_t*>(p.in) + q_row(m) * p.Dn + sc;
+      const uint4 a = *reinterpret_cast<const uint4*>(q);
+      const uint4 b = *reinterpret_cast<const uint4*>(q + 8);
+      *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc) = a;
+      *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc + 8) = b;
     }
-    // D[m][n]: lane holds column n = lane%32, rows 8*(i/4) + 4*hi + i%4.
+    __syncthreads();
+    // A (k-step ks: d = 16*ks + 8*hi + 0..7, channel c0 + 32*wave + lane%32):
+    // 16-lane group g reads rows 16*ks + 8*hi + {0..3} (then +4) of channels
+    // 32*wave + 16*(g & 1) .. +15; lane j of the group addresses row j/4, cols 4*(j%4).
+    floatx16 acc = floatx16{};
+    {
+      const int j = lane & 15, g = (lane >> 4) & 1;
+      const uint16_t* abase = s_w + (8 * hi + (j >> 2)) * kWPad + 32 * wave + 16 * g + 4 * (j & 3);
+      const uint16_t* bbase = s_q + (lane & 31) * kQPad + 8 * hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mr = m0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (mr < M) {
-        const int b2 = mr / p.Q, q2 = mr % p.Q;
-        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b2 * p.H + h) * p.Q + q2) * p.Ckv;
-        o[c0 + nloc] = (uint16_t)f32_to_bf16_bits(acc[i]);
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = tr_pair(abase + 16 * ks * kWPad, abase + (16 * ks + 4) * kWPad);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bbase + 16 * ks);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
+    }
+    // D^T[c][m]: lane holds row m = lane%32, channels 8*(i/4) + 4*hi + i%4 of the wave's 32.
+    {
+      uint16_t* o = s_o + (lane & 31) * kQPad + 32 * wave + 4 * hi;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        *reinterpret_cast<uint2*>(o + 8 * i4) =
+            make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+      }
+    }
+    __syncthreads();
+    if (m0 + sr < M) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + q_row(m0 + sr) * p.Ckv + c0 + sc;
+      *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc);
+      *reinterpret_cast<uint4*>(o + 8) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc + 8);
     }
   }
 }
 
-// Up-projection. grid (H); wave w owns value columns 32w .. 32w+31.
-// D[m = (b,q) row][n = v] = sum_c x[m][c] W_UV[v][c]; both operands have the
-// contraction index contiguous, so fragments load straight from global memory.
+// Up-projection, transposed: out^T[v][m] = sum_c W_UV[v][c] x^T[c][m] for one
+// head and 32 value columns. grid (H, Vd/32). The 32 W_UV rows and 32 rows of
+// x at a time go through LDS with row-contiguous loads (64 lanes per 1 KiB
+// row); both operands are contiguous in c, so fragments are plain 16-byte LDS
+// reads. The four waves split the contraction over c into quarters of 128 and
+// add their partial 32 x 32 blocks in LDS.
+constexpr int kRowPad = 520;  // 1 KiB row + 16 B (elements)
 __global__ void __launch_bounds__(kThreads) up_bf16_kernel(ProjParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[32 * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[32 * kRowPad];
+  __shared__ float s_part[3][16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
   const int h = blockIdx.x;
-  const int v = 32 * wave + (lane & 31);
-  const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) +
-                      ((int64_t)h * (p.Dn + p.Vd) + p.Dn + v) * p.Ckv;
-  bf16x8 bf[32];
+  const int v0 = blockIdx.y * 32;
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) + ((int64_t)h * (p.Dn + p.Vd) + p.Dn + v0) * p.Ckv;
+  // Stage: chunk s = tid + 256*k is row s / 64, 8 elements at 8 * (s % 64).
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) bf[ks] = *reinterpret_cast<const bf16x8*>(w + 16 * ks + 8 * hi);
+  for (int k = 0; k < 8; ++k) {
+    const int s = tid + kThreads * k;
+    const int r = s >> 6, c = 8 * (s & 63);
+    *reinterpret_cast<uint4*>(s_w + r * kRowPad + c) = *reinterpret_cast<const uint4*>(w + (int64_t)r * p.Ckv + c);
+  }
   const int M = p.B * p.Q;
+  auto x_row = [&](int m) {
+    const int bb = m / p.Q, qq = m % p.Q;
+    return ((int64_t)bb * p.H + h) * p.Q + qq;
+  };
+  const int cq = 128 * wave;  // this wave's quarter of the contraction
   for (int m0 = 0; m0 < M; m0 += 32) {
-    const int m = m0 + (lane & 31);
-    const bool ok = m < M;
-    const int bb = ok ? m / p.Q : 0, qq = ok ? m % p.Q : 0;
-    const uint16_t* x = reinterpret_cast<const uint16_t*>(p.in) + (((int64_t)bb * p.H + h) * p.Q + qq) * p.Ckv;
-    floatx16 acc = floatx16{};
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      const bf16x8 a = ok ? *reinterpret_cast<const bf16x8*>(x + 16 * ks + 8 * hi) : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[ks], acc, 0, 0, 0);
+    for (int k = 0; k < 8; ++k) {
+      const int s = tid + kThreads * k;
+      const int r = s >> 6, c = 8 * (s & 63);
+      const uint16_t* x = reinterpret_cast<const uint16_t*>(p.in) + x_row(min(m0 + r, M - 1)) * p.Ckv + c;
+      *reinterpret_cast<uint4*>(s_x + r * kRowPad + c) = *reinterpret_cast<const uint4*>(x);
     }
+    __syncthreads();
+    floatx16 acc = floatx16{};
+    {
+      const uint16_t* a = s_w + (lane & 31) * kRowPad + cq + 8 * hi;
+      const uint16_t* b = s_x + (lane & 31) * kRowPad + cq + 8 * hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mr = m0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (mr < M) {
-        const int b2 = mr / p.Q, q2 = mr % p.Q;
-        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b2 * p.H + h) * p.Q + q2) * p.Vd;
-        o[v] = (uint16_t)f32_to_bf16_bits(acc[i]);
+      for (int ks = 0; ks < 8; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks),
+                                                      *reinterpret_cast<const bf16x8*>(b + 16 * ks), acc, 0, 0, 0);
       }
     }
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_part[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += s_part[0][i][lane] + s_part[1][i][lane] + s_part[2][i][lane];
+      // D^T[v][m]: lane holds row m, value columns v0 + 8*(i/4) + 4*hi + i%4.
+      const int m = m0 + (lane & 31);
+      if (m < M) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + x_row(m) * p.Vd + v0 + 4 * hi;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          *reinterpret_cast<uint2*>(o + 8 * i4) = make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]),
+                                                             pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -155,7 +220,7 @@ hipError_t launch_absorb(const ProjParams& p, bool bf16, hipStream_t s) {
 
 hipError_t launch_up_proj(const ProjParams& p, bool bf16, hipStream_t s) {
   if (bf16) {
-    hipLaunchKernelGGL(up_bf16_kernel, dim3(p.H), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(up_bf16_kernel, dim3(p.H, p.Vd / 32), dim3(kThreads), 0, s, p);
   } else {
     const int64_t rows = (int64_t)p.B * p.H * p.Q;
     hipLaunchKernelGGL(up_f32_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, p);
