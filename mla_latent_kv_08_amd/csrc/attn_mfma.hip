@@ -282,15 +282,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   const bool is_load = wave == 4 || wave == 5;
 
   // Block -> (run wg, row block g). Consecutive block ids go to the 8 XCDs in
-  // turn; the G row blocks of one run share an XCD (and its L2) and are
-  // dispatched next to each other, so the tiles they both read come from HBM
-  // once.
+  // turn. XCD x takes the consecutive runs x*R .. x*R + R-1 (R = ceil(W/8)),
+  // so the runs of one sequence (and the query rows they share) sit in one
+  // L2, and the G row blocks of a run are dispatched next to each other on
+  // it, so the tiles they both read come from HBM once.
   const int G = p.groups;
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int q8 = bid >> 3;
   const int g = q8 % G;
-  const int wg = (q8 / G) * 8 + xcd;
+  const int runs_per_xcd = (p.workgroups + 7) / 8;
+  const int wg = xcd * runs_per_xcd + q8 / G;
   if (wg >= p.workgroups) return;
 
   // ---- this workgroup's run: tiles [start, end) of all sequences end to end ----
@@ -348,6 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       ++issued;
       ic.next(p);
     };
+    __syncthreads();  // the score waves' query loads go out first
     // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in registers).
     if constexpr (kFp4) {
       issue();
@@ -397,67 +400,92 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     const int rope_off = kRopeBase + (tq >> 3) * kRopeGroupBytes + hi * 128 + (tq & 7) * 16;
 
     Cursor sc = cur;
+    // Query fragments of sequence b (B operand of S^T = K Qcat^T): row
+    // `row_c`, channels 16*ks + 8*hi .. +7 of [q_lat | q_pe].
     bf16x8 qf[36];
+    auto load_q = [&](int b) {
+      const int64_t grow = (int64_t)b * p.HQ + row_c;
+      const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
+                                                         grow * 512 + 8 * hi);
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
+                                                         grow * 64 + 8 * hi);
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
+    };
+    if (rows_on) load_q(sc.b);
+    __syncthreads();  // query loads are out before the first tile copies
     float m = -INFINITY, l = 0.0f;
     for (int k = 0; k <= count; ++k) {
       __syncthreads();  // step k
       if (k == count || !rows_on) continue;
       if (k == 0 || sc.tile == 0) {
-        // New segment: query fragments of sequence sc.b (B operand of
-        // S^T = K Qcat^T): row `row_c`, channels 16*ks + 8*hi .. +7 of [q_lat | q_pe].
-        const int64_t grow = (int64_t)sc.b * p.HQ + row_c;
-        const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
-                                                           grow * 512 + 8 * hi);
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
-                                                           grow * 64 + 8 * hi);
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
+        // New segment (sequence sc.b).
+        if (k > 0) load_q(sc.b);
         m = -INFINITY;
         l = 0.0f;
       }
       const uint8_t* tb = smem + (k % kRing) * kTileBytes;
 
       // ---- S^T block: the tile's 32 tokens x this wave's 32 rows ----
-      // K fragments run four reads ahead of the matrix ops; the k-steps chain
-      // on one accumulator.
-      floatx16 s = floatx16{};
+      // K fragments run eight reads ahead of the matrix ops. Even and odd
+      // k-steps accumulate separately: this wave is the only matrix-op issuer
+      // on its SIMD, and one dependent chain would run at about half rate.
+      floatx16 s;
       {
         auto kaddr = [&](int ks) {
           return ks < 32 ? tb + qk_off[ks & 7] + 256 * (ks >> 3) : tb + rope_off + 256 * (ks - 32);
         };
-        bf16x8 ka[4];
+        constexpr int kAhead = 8;
+        bf16x8 ka[kAhead];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
+        for (int u = 0; u < kAhead; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
+        floatx16 s0 = floatx16{}, s1 = floatx16{};
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
-          const bf16x8 a = ka[ks & 3];
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-          if (ks + 4 < 36) ka[ks & 3] = *reinterpret_cast<const bf16x8*>(kaddr(ks + 4));
+          const bf16x8 a = ka[ks % kAhead];
+          if (ks & 1) {
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s1, 0, 0, 0);
+          } else {
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s0, 0, 0, 0);
+          }
+          if (ks + kAhead < 36) ka[ks % kAhead] = *reinterpret_cast<const bf16x8*>(kaddr(ks + kAhead));
         }
-        // Issue order: the four leading reads, then matrix op / next read pairs.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        s = s0 + s1;
+        // Issue order: the leading reads, then matrix op / next read pairs.
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
+        for (int ks = 0; ks < 36 - kAhead; ++ks) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
       }
 
       // ---- online softmax in the log2 domain; lane holds row `row` ----
+      // Raw scores; the scale (log2 units) enters through the row max and one
+      // fused multiply-add per exponent. With a positive scale the max of the
+      // raw scores gives the max of the scaled ones.
+      const float c = p.scale_log2;
       const int vis = sc.L - p.Q + qi + 1;  // this row sees tokens t < vis
       const int tok0 = sc.tile * kTile + 4 * hi;
-      float mx = -INFINITY;
+      // Every row of the block sees the whole tile (uniform): no masking.
+      const bool whole_tile = c > 0.0f && (sc.tile + 1) * kTile <= sc.L - p.Q + 1;
+      if (!whole_tile) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = tok0 + 8 * (i >> 2) + (i & 3);
-        const float v = tok < vis ? s[i] * p.scale_log2 : -INFINITY;
-        s[i] = v;
-        mx = fmaxf(mx, v);
+        for (int i = 0; i < 16; ++i) {
+          const int tok = tok0 + 8 * (i >> 2) + (i & 3);
+          s[i] = tok < vis ? s[i] * c : -INFINITY;
+        }
       }
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+      mx = fmaxf(mx, s[15]);
       mx = xor32_max(mx);
+      if (whole_tile) mx *= c;
+      const float sc_c = whole_tile ? c : 1.0f;  // factor still to apply to s
       // The reference m moves only when a row max exceeds it by more than
       // kRescaleLog2, so O is rarely rescaled and p stays <= 2^kRescaleLog2.
       const bool upd = mx > m + kRescaleLog2;
@@ -470,7 +498,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       bf16x8 pf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc_c, -m_use));
         rs += e;
         pf[i >> 3][i & 7] = (__bf16)e;
       }
@@ -515,6 +543,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
     }
 
+    __syncthreads();  // the score waves' query loads go out first
     Cursor pc = cur;
     int seg_lo = pc.tile;
     int seg_bad = 0;
