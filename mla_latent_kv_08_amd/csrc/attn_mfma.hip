@@ -10,20 +10,23 @@
 //   online softmax over t per row r (scaled, causal limit per row)
 //   O^T[c, r] += sum_t C^T[c, t] P^T[t, r]        c over the 512 latent
 //
-// Both contractions are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-// The eight waves of a workgroup (two per SIMD) have fixed roles:
-//   score waves 0, 1   row block rb = wave (32 rows): query fragments in
-//                      registers, S^T for a 32-token tile, the online softmax
-//                      of their own rows; bf16 probabilities and per-row
-//                      rescale factors go to LDS.
-//   P.V waves 2,3,6,7  latent channels 128*cq .. +127 of all 64 rows (O^T in
-//                      registers); each transposed V fragment feeds both row
-//                      blocks.
-//   load waves 4, 5    copy cache tiles into an LDS ring.
-// Step k of the run: score waves work on tile k, P.V waves on tile k-1 (with
-// the probabilities the score waves left in the previous step), load waves
-// start tile k+2; one barrier separates steps. Score and P.V work land on
-// different SIMDs (0,1 and 2,3), about 36 and 32 matrix ops per SIMD and step.
+// Both contractions run on bf16 matrix ops with fp32 accumulation. The eight
+// waves of a workgroup are two per SIMD, one of each role on every SIMD, so
+// the matrix work and the softmax arithmetic are spread evenly:
+//   score waves 0..3   row block rb = wave / 2 (32 rows), token half
+//                      th = wave % 2 of the tile (16 tokens): query fragments
+//                      in registers, S^T by v_mfma_f32_16x16x32_bf16, the
+//                      softmax of those 32 rows x 16 tokens.
+//   P.V waves 4..7     latent channels 128*cq .. +127 of all 64 rows (O^T in
+//                      registers, v_mfma_f32_32x32x16_bf16); each transposed
+//                      V fragment feeds both row blocks. They also start the
+//                      tile copies into LDS.
+// Step k has two phases split by barriers. Phase 1: score waves form S^T for
+// tile k and publish their 16-token row maxima; P.V waves start tile k+2 and
+// apply the first 16 tokens of tile k-1. Phase 2: each score wave takes the
+// tile max of both halves, so the two halves of a row block keep one running
+// max m and rescale decision, and writes bf16 probabilities and its own part
+// of the row sum; P.V waves apply the other 16 tokens of tile k-1.
 //
 // Tiles of 32 tokens (half a cache page) live in a ring of four LDS buffers:
 // the P.V tile, the score tile and two tiles in flight. bf16 rows are copied
@@ -47,6 +50,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kTile = kAttnTileTokens;                 // tokens per LDS tile
+constexpr int kHalf = kTile / 2;                       // tokens per score wave
 constexpr int kLatRowBytes = 1024;                     // 512 bf16 latent channels
 constexpr int kRopeGroupBytes = 1152;                  // 8 tokens x 128 B, + 128 B pad
 constexpr int kRopeBase = kTile * kLatRowBytes;        // RoPE groups follow the latent rows
@@ -56,28 +60,58 @@ constexpr int kPSlotBytes = 2 * 2 * 64 * 16;           // [rb][kk][lane] bf16x8
 constexpr int kPBase = kRing * kTileBytes;
 struct Meta {
   float alpha[kRowsPerGroup];  // factor on O before this tile's P.V
-  float l[kRowsPerGroup];      // running sum and max after this tile
-  float m[kRowsPerGroup];
+  float m[kRowsPerGroup];      // running max after this tile
+  float l[2][kRowsPerGroup];   // running sum of each token half after this tile
   int rescale[2];              // per row block: some alpha != 1
   int pad[2];
 };
 constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
-constexpr int kSmemBytes = kMetaBase + 2 * (int)sizeof(Meta);
-constexpr int kDmaPerWave = kTile / 2 + 2;             // bf16 loads per load wave and tile
+constexpr int kMaxBase = kMetaBase + 2 * (int)sizeof(Meta);  // tile row maxima [rb][th][32]
+constexpr int kSmemBytes = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);
+constexpr int kDmaPerWave = kTile / 4 + 1;             // bf16 loads per P.V wave and tile
+// Query rows of a run's first sequence are staged once in ring buffers 2 and
+// 3 (free until step 0 starts tile 2): latent row r (1 KiB) holds chunk c at
+// slot c ^ (r % 16); the RoPE part is chunk-major, [8 chunks][64 rows][16 B].
+constexpr int kQBase = 2 * kTileBytes;
+constexpr int kQRopeBase = kQBase + kRowsPerGroup * kLatRowBytes;
+// Final results of a run are staged per P.V wave in free ring buffers as 32
+// rows x 128 fp32 channels, rows padded to 132 floats (bank spread).
+constexpr int kStageRow = 132;
+constexpr int kStageBytes = 32 * kStageRow * (int)sizeof(float);
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.0f;  // p = 2^(s - m) stays <= 2^8
 
-static_assert(kTile == 32 && kRowsPerGroup == 64, "two 32x32 score blocks per tile");
+static_assert(kTile == 32 && kRowsPerGroup == 64, "two 32-row blocks, two 16-token halves per tile");
 static_assert(kPageTokens % kTile == 0, "a tile never crosses a page");
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
+static_assert(kQRopeBase + 8 * kRowsPerGroup * 16 <= 4 * kTileBytes, "query staging fits buffers 2, 3");
+static_assert(2 * kStageBytes <= kTileBytes, "two P.V waves stage in one free buffer");
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(int32x4_t rsrc, lds_void* lds, int size,
-                                                           int voffset, int soffset, int offset,
-                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// One buffer load of 16 bytes per lane straight into LDS: lane i's bytes land
+// at LDS address lds_base + 16*i. The instruction has no register result; it
+// is written out here because the compiler, unable to tell which LDS bytes
+// such a load writes, would otherwise wait for all of them still in flight
+// before every later LDS read of the issuing wave, draining the copies meant
+// to overlap the next steps. The copying waves wait for their own copies
+// (vmcnt) before the barrier that hands a tile to the other waves. M0 (the
+// LDS address) is set inside the block; nothing else in these kernels keeps a
+// value in M0.
+__device__ __forceinline__ void lds_copy16(int32x4_t rsrc, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
 
 __device__ __forceinline__ shortx4 tr_read(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
@@ -96,8 +130,27 @@ __device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 
 // outstanding (lgkm and exp counters left alone).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Read-only int tables (sequence lengths, page tables) through the constant
+// address space: with a wave-uniform index this is a scalar load, which does
+// not wait behind the wave's outstanding vector loads (tile copies).
+__device__ __forceinline__ int load_ro(const int32_t* base, int64_t i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(base))[i];
+}
+
 __device__ __forceinline__ int seq_len(const AttnParams& p, int b) {
-  return clamp_len(p.seq_lens[b], p.cache.capacity);
+  return clamp_len(load_ro(p.seq_lens, b), p.cache.capacity);
+}
+
+// Workgroup barrier ordering LDS only. __syncthreads() also drains every
+// outstanding global access of the wave (vmcnt(0)), which would wait for the
+// tile copies meant to stay in flight across steps; the copy waves wait for
+// exactly the copies the next step reads before arriving here.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
@@ -131,7 +184,7 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 __device__ __forceinline__ int64_t tile_row0(const CacheView& c, int b, int tile, bool& bad) {
   const int t0 = tile * kTile;
   if (c.page_size == 0) return (int64_t)b * c.capacity + t0;
-  const int page = c.page_table[(int64_t)b * c.pt_stride + t0 / kPageTokens];
+  const int page = load_ro(c.page_table, (int64_t)b * c.pt_stride + t0 / kPageTokens);
   const int64_t p0 = (int64_t)page * kPageTokens;
   if (page < 0 || p0 + kPageTokens > c.num_rows) {
     bad = true;
@@ -167,11 +220,11 @@ __device__ __forceinline__ int32x4_t buffer_rsrc(const uint8_t* base, uint32_t b
   return r;
 }
 
-// bf16 tile -> LDS by direct buffer loads. Load wave d moves latent rows
-// 16d .. 16d+15 (one 64-lane load of 1 KiB each; lane i fetches chunk
-// i ^ swz(t) into slot i) and RoPE groups 2d, 2d+1 (lane i: token 8g + i % 8,
-// chunk i / 8). The descriptors span exactly the tile's `valid` rows, so later
-// rows read as zero. Always kDmaPerWave instructions per load wave.
+// bf16 tile -> LDS by direct buffer loads. Copy wave d (of four) moves latent
+// rows 8d .. 8d+7 (one 64-lane load of 1 KiB each; lane i fetches chunk
+// i ^ swz(t) into slot i) and RoPE group d (lane i: token 8d + i % 8, chunk
+// i / 8). The descriptors span exactly the tile's `valid` rows, so later rows
+// read as zero. Always kDmaPerWave instructions per wave.
 __device__ __forceinline__ void dma_tile_bf16(const CacheView& c, int64_t row0, int valid, int d,
                                               int lane, uint8_t* dst) {
   const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
@@ -179,54 +232,45 @@ __device__ __forceinline__ void dma_tile_bf16(const CacheView& c, int64_t row0, 
   const int32x4_t lat = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * ls);
   const int32x4_t rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * rs);
 #pragma unroll
-  for (int n = 0; n < kTile / 2; ++n) {
-    const int t = d * (kTile / 2) + n;
+  for (int n = 0; n < kTile / 4; ++n) {
+    const int t = d * (kTile / 4) + n;
     const int voff = (int)(t * ls) + ((lane ^ swz(t)) << 4);
-    llvm_amdgcn_raw_buffer_load_lds(lat, (lds_void*)(dst + t * kLatRowBytes), 16, voff, 0, 0, 0);
+    lds_copy16(lat, lds_addr(dst + t * kLatRowBytes), voff);
   }
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int gr = 2 * d + n;
-    const int voff = (int)((gr * 8 + (lane & 7)) * rs) + ((lane >> 3) << 4);
-    llvm_amdgcn_raw_buffer_load_lds(rope, (lds_void*)(dst + kRopeBase + gr * kRopeGroupBytes), 16, voff,
-                                    0, 0, 0);
-  }
+  const int voff = (int)((d * 8 + (lane & 7)) * rs) + ((lane >> 3) << 4);
+  lds_copy16(rope, lds_addr(dst + kRopeBase + d * kRopeGroupBytes), voff);
 }
 
-// FP4 tiles, staged by the two load waves (128 lanes, index dt): per token 16
+// FP4 tiles, staged by the four P.V waves (256 lanes, index dt): per token 16
 // code chunks (32 channels each) with their 2 scale bytes, and 8 RoPE chunks.
-// Lane dt takes code chunks s = dt + 128*k (token s >> 4, chunk s & 15) and
-// RoPE chunks s = dt + 128*k (token s >> 3, chunk s & 7); it decodes its codes
-// (E2M1 value times E4M3 scale, exact in bf16) when writing them to the bf16
-// tile. Rows at or past `valid` re-read the last valid row (masked, finite).
+// Lane dt takes code chunks s = dt + 256*k (token s >> 4, chunk s & 15) and
+// RoPE chunk s = dt (token s >> 3, chunk s & 7); it decodes its codes (E2M1
+// value times E4M3 scale, exact in bf16) when writing them to the bf16 tile.
+// Rows at or past `valid` re-read the last valid row (masked, finite).
 struct Fp4Stage {
-  uint4 codes[4];
-  uint32_t scales[4];
-  uint4 rope[2];
+  uint4 codes[2];
+  uint32_t scales[2];
+  uint4 rope;
 };
 
 __device__ __forceinline__ void load_tile_fp4(const CacheView& c, int64_t row0, int valid, int dt,
                                               Fp4Stage& st) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int s = dt + 128 * k;
+  for (int k = 0; k < 2; ++k) {
+    const int s = dt + 256 * k;
     const int64_t r = row0 + min(s >> 4, valid - 1);
     const int j = s & 15;
     st.codes[k] = *reinterpret_cast<const uint4*>(c.latent + r * c.latent_stride + j * 16);
     st.scales[k] = *reinterpret_cast<const uint16_t*>(c.scale + r * c.scale_stride + j * 2);
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = dt + 128 * k;
-    const int64_t r = row0 + min(s >> 3, valid - 1);
-    st.rope[k] = *reinterpret_cast<const uint4*>(c.rope + r * c.rope_stride + (s & 7) * 16);
-  }
+  const int64_t r = row0 + min(dt >> 3, valid - 1);
+  st.rope = *reinterpret_cast<const uint4*>(c.rope + r * c.rope_stride + (dt & 7) * 16);
 }
 
 __device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int dt, const Fp4Stage& st) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int s = dt + 128 * k;
+  for (int k = 0; k < 2; ++k) {
+    const int s = dt + 256 * k;
     const int t = s >> 4;
     const int j = s & 15;
     const float s0 = e4m3_to_f32(st.scales[k] & 0xffu);
@@ -247,24 +291,27 @@ __device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int dt, const Fp4St
           make_uint4(outw[0], outw[1], outw[2], outw[3]);
     }
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = dt + 128 * k;
-    const int t = s >> 3, ch = s & 7;
-    *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
-        st.rope[k];
-  }
+  const int t = dt >> 3, ch = dt & 7;
+  *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) = st.rope;
 }
 
-// Both halves of a wave64 register combined lane-wise: lanes l and l ^ 32
-// get the same op(x_l, x_l^32) (operands in the same order), via
-// v_permlane32_swap instead of an LDS permute.
+// Lane-wise combination across lane groups: lanes l and l ^ 32 (or l ^ 16)
+// get the same op(x_lo, x_hi), operands in the same order on both, via
+// v_permlane32_swap / v_permlane16_swap instead of an LDS permute.
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -278,8 +325,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   const int lane = tid & 63;
   const int hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool is_score = wave < 2;
-  const bool is_load = wave == 4 || wave == 5;
+  const bool is_score = wave < 4;
 
   // Block -> (run wg, row block g). Consecutive block ids go to the 8 XCDs in
   // turn. XCD x takes the consecutive runs x*R .. x*R + R-1 (R = ceil(W/8)),
@@ -330,11 +376,239 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 
   uint8_t* const ptiles = smem + kPBase;
   Meta* const metas = reinterpret_cast<Meta*>(smem + kMetaBase);
+  float* const tile_max = reinterpret_cast<float*>(smem + kMaxBase);
 
-  if (is_load) {
-    // ================= load waves =================
-    const int d = wave - 4;
-    const int dt = tid - 256;
+  if (is_score) {
+    // ================= score waves: S^T, softmax, probabilities =================
+    const int rb = wave >> 1;
+    const int th = wave & 1;
+    // 16x16 operand layouts: lane -> index l16 (token for K, row for Q) and
+    // k group g4 (channels 8*g4 .. +7 of each 32-channel k-step).
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const bool rows_on = g * kRowsPerGroup + rb * 32 < p.HQ;  // uniform
+    // Rows of the two 16-row halves rh: rb*32 + 16*rh + l16. Rows past HQ
+    // compute on row 0's query and are never stored.
+    int row_c[2], qi[2];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      const int row = g * kRowsPerGroup + rb * 32 + 16 * rh + l16;
+      row_c[rh] = row < p.HQ ? row : 0;
+      qi[rh] = row_c[rh] % p.Q;
+    }
+    // K reads (A operand): token tq, chunk 4*ks + g4 of the latent row for
+    // ks < 16 (at k_off[ks % 4] + 256 * (ks / 4)), RoPE chunk 4*(ks-16) + g4
+    // for ks = 16, 17 (at rope_off + 512 * (ks - 16)).
+    const int tq = kHalf * th + l16;
+    int k_off[4];
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tq * kLatRowBytes + (((4 * b4 + g4) ^ swz(tq)) << 4);
+    const int rope_off = kRopeBase + (tq >> 3) * kRopeGroupBytes + g4 * 128 + (tq & 7) * 16;
+
+    Cursor sc = cur;
+    // Query fragments (B operand): row half rh, channels 32*ks + 8*g4 .. +7 of
+    // [q_lat | q_pe]; from the staged rows at the run start, from global
+    // memory at a later sequence of the run.
+    bf16x8 qf[2][18];
+    auto load_q = [&](int b) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int64_t grow = (int64_t)b * p.HQ + row_c[rh];
+        const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
+                                                           grow * 512 + 8 * g4);
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
+                                                           grow * 64 + 8 * g4);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qf[rh][ks] = ql[4 * ks];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) qf[rh][16 + ks] = qp[4 * ks];
+      }
+    };
+    {
+      // Score wave w copies latent rows 16w .. 16w+15 and RoPE chunks 2w,
+      // 2w+1 of the group's query rows; rows past HQ read as zero.
+      const int64_t grow0 = (int64_t)cur.b * p.HQ + g * kRowsPerGroup;
+      const int nrows = min(kRowsPerGroup, p.HQ - g * kRowsPerGroup);
+      const int32x4_t ql =
+          buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_lat) + grow0 * kLatRowBytes, nrows * kLatRowBytes);
+      const int32x4_t qp = buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_pe) + grow0 * 128, nrows * 128);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int r = 16 * wave + n;
+        lds_copy16(ql, lds_addr(smem + kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int c = 2 * wave + n;
+        lds_copy16(qp, lds_addr(smem + kQRopeBase + c * 1024), lane * 128 + c * 16);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    lds_barrier();  // query rows staged
+    if (rows_on) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int r = rb * 32 + 16 * rh + l16;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          qf[rh][ks] = *reinterpret_cast<const bf16x8*>(smem + kQBase + r * kLatRowBytes +
+                                                         (((4 * ks + g4) ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          qf[rh][16 + ks] = *reinterpret_cast<const bf16x8*>(smem + kQRopeBase + (4 * ks + g4) * 1024 + r * 16);
+        }
+      }
+    }
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+    for (int k = 0; k <= count; ++k) {
+      lds_barrier();  // step k, phase 1
+      const bool active = rows_on && k < count;
+      floatx4 s[2];
+      float mx[2];
+      float sc_c = 1.0f;
+      if (active) {
+        if (k == 0 || sc.tile == 0) {
+          // New segment (sequence sc.b).
+          if (k > 0) load_q(sc.b);
+          m[0] = m[1] = -INFINITY;
+          l[0] = l[1] = 0.0f;
+        }
+        const uint8_t* tb = smem + (k % kRing) * kTileBytes;
+
+        // ---- S^T: this wave's 16 tokens x 32 rows (two 16x16 blocks) ----
+        // Each K fragment feeds both row halves; even and odd k-steps
+        // accumulate separately so no matrix op waits on the one before.
+        {
+          auto kaddr = [&](int ks) {
+            return ks < 16 ? tb + k_off[ks & 3] + 256 * (ks >> 2) : tb + rope_off + 512 * (ks - 16);
+          };
+          constexpr int kAhead = 6;
+          bf16x8 ka[kAhead];
+#pragma unroll
+          for (int u = 0; u < kAhead; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
+          floatx4 acc[2][2];
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) acc[rh][0] = acc[rh][1] = floatx4{};
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) {
+            const bf16x8 a = ka[ks % kAhead];
+            acc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], acc[0][ks & 1], 0, 0, 0);
+            acc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], acc[1][ks & 1], 0, 0, 0);
+            if (ks + kAhead < 18) ka[ks % kAhead] = *reinterpret_cast<const bf16x8*>(kaddr(ks + kAhead));
+          }
+          s[0] = acc[0][0] + acc[0][1];
+          s[1] = acc[1][0] + acc[1][1];
+          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+          for (int ks = 0; ks < 18 - kAhead; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+        }
+
+        // ---- scale, causal limit, row max over this half ----
+        // Lane holds rows rb*32 + 16*rh + l16, tokens tok0 + i (i < 4). Raw
+        // scores; with a positive scale and no masking the scale enters
+        // through the max and one fused multiply-add per exponent.
+        const float c = p.scale_log2;
+        const int tok0 = sc.tile * kTile + kHalf * th + 4 * g4;
+        const bool whole_tile = c > 0.0f && (sc.tile + 1) * kTile <= sc.L - p.Q + 1;
+        sc_c = whole_tile ? c : 1.0f;
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          if (!whole_tile) {
+            const int vis = sc.L - p.Q + qi[rh] + 1;  // the row sees tokens t < vis
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[rh][i] = tok0 + i < vis ? s[rh][i] * c : -INFINITY;
+          }
+          float v = fmaxf(fmaxf(s[rh][0], s[rh][1]), fmaxf(s[rh][2], s[rh][3]));
+          v = xor32_max(xor16_max(v));
+          mx[rh] = whole_tile ? v * c : v;
+        }
+        if (g4 == 0) {
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) tile_max[(rb * 2 + th) * 32 + 16 * rh + l16] = mx[rh];
+        }
+      }
+      lds_barrier();  // step k, phase 2
+      if (active) {
+        // ---- online softmax in the log2 domain ----
+        // Both halves see the same tile max, so their running max m and
+        // rescale decisions stay identical. The reference m moves only when
+        // the tile max exceeds it by more than kRescaleLog2, so O is rarely
+        // rescaled and p stays <= 2^kRescaleLog2.
+        float alpha[2];
+        bool upd[2];
+        bf16x4 pk[2];
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          const float mt = fmaxf(mx[rh], tile_max[(rb * 2 + (th ^ 1)) * 32 + 16 * rh + l16]);
+          upd[rh] = mt > m[rh] + kRescaleLog2;
+          const float m_new = upd[rh] ? mt : m[rh];
+          alpha[rh] = upd[rh] ? __builtin_amdgcn_exp2f(m[rh] - m_new) : 1.0f;
+          m[rh] = m_new;
+          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+          float rs = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
+            rs += e;
+            pk[rh][i] = (__bf16)e;
+          }
+          l[rh] = l[rh] * alpha[rh] + xor32_sum(xor16_sum(rs));
+        }
+        // Probabilities in the P.V B-operand layout [rb][kk][lane]: k-step
+        // kk = th covers this half's tokens; lane L holds row L % 32, tokens
+        // 8 * (L / 32) .. +7, so this lane's 4 tokens go to lane
+        // 16*rh + l16 + 32*(g4 / 2) at element 4 * (g4 % 2).
+        uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048 + th * 1024 + 8 * (g4 & 1);
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          *reinterpret_cast<bf16x4*>(ps + (16 * rh + l16 + 32 * (g4 >> 1)) * 16) = pk[rh];
+        }
+        Meta* mt = metas + (k & 1);
+        if (g4 == 0) {
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) {
+            const int rl = rb * 32 + 16 * rh + l16;
+            if (th == 0) {
+              mt->alpha[rl] = alpha[rh];
+              mt->m[rl] = m[rh];
+            }
+            mt->l[th][rl] = l[rh];
+          }
+        }
+        const bool any_upd = __any(upd[0] || upd[1]);
+        if (th == 0 && lane == 0) mt->rescale[rb] = any_upd ? 1 : 0;
+      }
+      if (k < count) sc.next(p);
+    }
+  } else {
+    // ================= P.V waves: O^T for 128 channels of all 64 rows =================
+    const int cq = wave - 4;
+    // Transposed reads (A = C^T): 16-lane group reads a 4 x 16 block; lane j
+    // of the group addresses token row 8*hi + 4*s + j / 4 of the k-step and
+    // channels 32*cb + 16*g16 + 4*(j % 4) .. +3 of the quarter, at
+    // tr_off[s][cb] + 16384 * kk.
+    int tr_off[2][4];
+    {
+      const int j = lane & 15, g16 = (lane >> 4) & 1;
+      const int low2 = 2 * g16 + ((j & 3) >> 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int t = 8 * hi + 4 * s + (j >> 2);
+        const int f = swz(t);
+#pragma unroll
+        for (int c3 = 0; c3 < 4; ++c3) {
+          tr_off[s][c3] =
+              t * kLatRowBytes + ((((c3 ^ (f >> 2)) << 2) | (low2 ^ (f & 3))) << 4) + 8 * (j & 1) + 256 * cq;
+        }
+      }
+    }
+
+    // ---- tile copies: tile k+2 starts in step k ----
+    const int dt = cq * 64 + lane;
     Cursor ic = cur;
     int issued = 0;
     Fp4Stage st;
@@ -345,33 +619,52 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       if constexpr (kFp4) {
         load_tile_fp4(p.cache, r0, valid, dt, st);
       } else {
-        dma_tile_bf16(p.cache, r0, valid, d, lane, smem + (issued % kRing) * kTileBytes);
+        dma_tile_bf16(p.cache, r0, valid, cq, lane, smem + (issued % kRing) * kTileBytes);
       }
       ++issued;
       ic.next(p);
     };
-    __syncthreads();  // the score waves' query loads go out first
-    // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in registers).
-    if constexpr (kFp4) {
-      issue();
-      store_tile_fp4(smem, dt, st);
-      if (issued < count) issue();
-    } else {
-      issue();
-      if (issued < count) issue();
-    }
+    // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in
+    // registers) into buffers 0 and 1, beside the staged query rows.
+    issue();
+    if constexpr (kFp4) store_tile_fp4(smem, dt, st);
+    if (issued < count) issue();
+    lds_barrier();  // query rows staged
+
+    Cursor pc = cur;
+    int seg_lo = pc.tile;
+    int seg_bad = 0;
+    bool first_seg = true;
+    bool stored = false;  // output stores issued since the last wait
+    floatx16 o[8];        // [rb * 4 + cb]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+    auto pv_half = [&](int kt, int kk) {
+      const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
+      const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 a = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, o[cb], 0, 0, 0);
+        o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, o[4 + cb], 0, 0, 0);
+      }
+    };
     for (int k = 0; k <= count; ++k) {
       if constexpr (!kFp4) {
-        // Tile k has landed (tile k+1 may still be in flight).
+        // Tile k has landed (tile k+1 may still be in flight unless output
+        // stores were issued after it).
         if (k < count) {
-          if (issued > k + 1) {
+          if (issued > k + 1 && !stored) {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerWave));
           } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           }
         }
       }
-      __syncthreads();  // step k
+      stored = false;
+      lds_barrier();  // step k, phase 1
       if constexpr (kFp4) {
         // Decode tile k+1 (its buffer held tile k-3), then fetch tile k+2.
         if (k + 1 < count) {
@@ -382,226 +675,100 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
         if (issued < count) issue();
       }
-    }
-  } else if (is_score) {
-    // ================= score waves: S^T, softmax, probabilities =================
-    const int rb = wave;
-    const int row_local = rb * 32 + (lane & 31);
-    const int row = g * kRowsPerGroup + row_local;
-    const bool rows_on = g * kRowsPerGroup + rb * 32 < p.HQ;  // uniform
-    const int row_c = row < p.HQ ? row : 0;  // rows past HQ compute on row 0's query, never stored
-    const int qi = row_c % p.Q;
-    // Score reads (A = K): token t = lane % 32, chunk 2*ks + hi; for ks < 32
-    // at qk_off[ks % 8] + 256 * (ks / 8), RoPE k-steps at rope_off + 256 * (ks - 32).
-    const int tq = lane & 31;
-    int qk_off[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qk_off[j] = tq * kLatRowBytes + (((2 * j + hi) ^ swz(tq)) << 4);
-    const int rope_off = kRopeBase + (tq >> 3) * kRopeGroupBytes + hi * 128 + (tq & 7) * 16;
-
-    Cursor sc = cur;
-    // Query fragments of sequence b (B operand of S^T = K Qcat^T): row
-    // `row_c`, channels 16*ks + 8*hi .. +7 of [q_lat | q_pe].
-    bf16x8 qf[36];
-    auto load_q = [&](int b) {
-      const int64_t grow = (int64_t)b * p.HQ + row_c;
-      const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
-                                                         grow * 512 + 8 * hi);
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
-                                                         grow * 64 + 8 * hi);
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) qf[ks] = ql[2 * ks];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[32 + ks] = qp[2 * ks];
-    };
-    if (rows_on) load_q(sc.b);
-    __syncthreads();  // query loads are out before the first tile copies
-    float m = -INFINITY, l = 0.0f;
-    for (int k = 0; k <= count; ++k) {
-      __syncthreads();  // step k
-      if (k == count || !rows_on) continue;
-      if (k == 0 || sc.tile == 0) {
-        // New segment (sequence sc.b).
-        if (k > 0) load_q(sc.b);
-        m = -INFINITY;
-        l = 0.0f;
-      }
-      const uint8_t* tb = smem + (k % kRing) * kTileBytes;
-
-      // ---- S^T block: the tile's 32 tokens x this wave's 32 rows ----
-      // K fragments run eight reads ahead of the matrix ops. Even and odd
-      // k-steps accumulate separately: this wave is the only matrix-op issuer
-      // on its SIMD, and one dependent chain would run at about half rate.
-      floatx16 s;
-      {
-        auto kaddr = [&](int ks) {
-          return ks < 32 ? tb + qk_off[ks & 7] + 256 * (ks >> 3) : tb + rope_off + 256 * (ks - 32);
-        };
-        constexpr int kAhead = 8;
-        bf16x8 ka[kAhead];
-#pragma unroll
-        for (int u = 0; u < kAhead; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
-        floatx16 s0 = floatx16{}, s1 = floatx16{};
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          const bf16x8 a = ka[ks % kAhead];
-          if (ks & 1) {
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s1, 0, 0, 0);
-          } else {
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s0, 0, 0, 0);
-          }
-          if (ks + kAhead < 36) ka[ks % kAhead] = *reinterpret_cast<const bf16x8*>(kaddr(ks + kAhead));
-        }
-        s = s0 + s1;
-        // Issue order: the leading reads, then matrix op / next read pairs.
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-        for (int ks = 0; ks < 36 - kAhead; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-      }
-
-      // ---- online softmax in the log2 domain; lane holds row `row` ----
-      // Raw scores; the scale (log2 units) enters through the row max and one
-      // fused multiply-add per exponent. With a positive scale the max of the
-      // raw scores gives the max of the scaled ones.
-      const float c = p.scale_log2;
-      const int vis = sc.L - p.Q + qi + 1;  // this row sees tokens t < vis
-      const int tok0 = sc.tile * kTile + 4 * hi;
-      // Every row of the block sees the whole tile (uniform): no masking.
-      const bool whole_tile = c > 0.0f && (sc.tile + 1) * kTile <= sc.L - p.Q + 1;
-      if (!whole_tile) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = tok0 + 8 * (i >> 2) + (i & 3);
-          s[i] = tok < vis ? s[i] * c : -INFINITY;
-        }
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
-      mx = fmaxf(mx, s[15]);
-      mx = xor32_max(mx);
-      if (whole_tile) mx *= c;
-      const float sc_c = whole_tile ? c : 1.0f;  // factor still to apply to s
-      // The reference m moves only when a row max exceeds it by more than
-      // kRescaleLog2, so O is rarely rescaled and p stays <= 2^kRescaleLog2.
-      const bool upd = mx > m + kRescaleLog2;
-      const float m_new = upd ? mx : m;
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-      l *= alpha;
-      m = m_new;
-      const float m_use = m == -INFINITY ? 0.0f : m;
-      float rs = 0.0f;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc_c, -m_use));
-        rs += e;
-        pf[i >> 3][i & 7] = (__bf16)e;
-      }
-      l += xor32_sum(rs);
-
-      // Probabilities in the P.V B-operand layout [rb][kk][lane]: k-step kk
-      // covers tokens 16*kk + 4*hi + {0..3} and +8 + {0..3}, which are exactly
-      // this lane's pf[kk].
-      uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048;
-      *reinterpret_cast<bf16x8*>(ps + lane * 16) = pf[0];
-      *reinterpret_cast<bf16x8*>(ps + 1024 + lane * 16) = pf[1];
-      Meta* mt = metas + (k & 1);
-      if (hi == 0) {
-        mt->alpha[row_local] = alpha;
-        mt->l[row_local] = l;
-        mt->m[row_local] = m;
-      }
-      const bool any_upd = __any(upd);
-      if (lane == 0) mt->rescale[rb] = any_upd ? 1 : 0;
-      sc.next(p);
-    }
-  } else {
-    // ================= P.V waves: O^T for 128 channels of all 64 rows =================
-    const int cq = (wave & 1) | ((wave >> 2) << 1);
-    // Transposed reads (A = C^T): 16-lane group reads a 4 x 16 block; lane j
-    // of the group addresses token row j / 4 (+ 4*hi, + 8 for the second read)
-    // and channels 32*cb + 16*g16 + 4*(j % 4) .. +3 of the quarter, at
-    // tr_off[s][cb] + 256 * cq + 16384 * kk.
-    int tr_off[2][4];
-    {
-      const int j = lane & 15, g16 = (lane >> 4) & 1;
-      const int low2 = 2 * g16 + ((j & 3) >> 1);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int t = 4 * hi + (j >> 2) + 8 * s;
-        const int f = swz(t);
-#pragma unroll
-        for (int c3 = 0; c3 < 4; ++c3) {
-          tr_off[s][c3] =
-              t * kLatRowBytes + ((((c3 ^ (f >> 2)) << 2) | (low2 ^ (f & 3))) << 4) + 8 * (j & 1) + 256 * cq;
-        }
-      }
-    }
-
-    __syncthreads();  // the score waves' query loads go out first
-    Cursor pc = cur;
-    int seg_lo = pc.tile;
-    int seg_bad = 0;
-    bool first_seg = true;
-    floatx16 o[8];  // [rb * 4 + cb]
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = floatx16{};
-    for (int k = 0; k <= count; ++k) {
-      __syncthreads();  // step k
-      if (k == 0) continue;
       const int kt = k - 1;  // tile of this step
-      {
+      if (k > 0) {
         bool bad = false;
         (void)tile_row0(p.cache, pc.b, pc.tile, bad);
         seg_bad |= bad ? 1 : 0;
-      }
-      const Meta* mt = metas + (kt & 1);
-      if (mt->rescale[0] | mt->rescale[1]) {
-        const float a0 = mt->alpha[lane & 31];
-        const float a1 = mt->alpha[32 + (lane & 31)];
+        const Meta* mt = metas + (kt & 1);
+        if (mt->rescale[0] | mt->rescale[1]) {
+          const float a0 = mt->alpha[lane & 31];
+          const float a1 = mt->alpha[32 + (lane & 31)];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          o[cb] *= a0;
-          o[4 + cb] *= a1;
+          for (int cb = 0; cb < 4; ++cb) {
+            o[cb] *= a0;
+            o[4 + cb] *= a1;
+          }
         }
+        pv_half(kt, 0);
       }
-      const uint8_t* tb = smem + (kt % kRing) * kTileBytes;
-      const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps + kk * 1024 + lane * 16);
-        const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048 + kk * 1024 + lane * 16);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const uint8_t* a0 = tb + 16384 * kk;
-          const bf16x8 a = join(tr_read(a0 + tr_off[0][cb]), tr_read(a0 + tr_off[1][cb]));
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, o[cb], 0, 0, 0);
-          o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, o[4 + cb], 0, 0, 0);
-        }
-      }
+      lds_barrier();  // step k, phase 2
+      if (k == 0) continue;
+      pv_half(kt, 1);
 
       const int nt = tiles_of(pc.L);
       if (pc.tile == nt - 1 || k == count) {
         // ---- end of the segment: write x / lse, or a partial for the combine ----
+        const Meta* mt = metas + (kt & 1);
         const bool whole = seg_lo == 0 && pc.tile == nt - 1;
         const float nanv = __uint_as_float(0x7fc00000u);
+        const int slot = 2 * wg + (first_seg ? 0 : 1);
+        const int64_t prow0 = ((int64_t)g * slots + slot) * kRowsPerGroup;  // partial rows of the group
+        const int64_t xrow0 = (int64_t)pc.b * p.HQ + g * kRowsPerGroup;     // output rows of the group
+        // At the run's last step every ring buffer but the one just read is
+        // free: results pass through LDS and leave as whole rows.
+        const bool staged = k == count;
+        float* const stage = reinterpret_cast<float*>(smem + ((kt + 1 + (cq >> 1)) % kRing) * kTileBytes +
+                                                      (cq & 1) * kStageBytes);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int row_local = rb * 32 + (lane & 31);
-          const int row = g * kRowsPerGroup + row_local;
-          if (row >= p.HQ) continue;
-          const float l = mt->l[row_local];
+          const bool row_ok = g * kRowsPerGroup + row_local < p.HQ;
+          const float l = mt->l[0][row_local] + mt->l[1][row_local];
           const float m = mt->m[row_local];
           const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
           float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
           if (seg_bad) lse_v = nanv;
-          if (whole) {
-            uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + ((int64_t)pc.b * p.HQ + row) * 512;
+          if (row_ok && cq == 0 && hi == 0) {
+            if (whole) {
+              if (p.lse != nullptr) p.lse[xrow0 + row_local] = lse_v;
+            } else {
+              p.part_lse[prow0 + row_local] = lse_v;
+            }
+          }
+          const bool nan_x = whole && seg_bad;
+          if (staged) {
+            // Lane holds row `row_local`, channels 32*cb + 8*i4 + 4*hi + {0..3}.
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                float4 v;
+                v.x = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + 0] * inv_l;
+                v.y = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + 1] * inv_l;
+                v.z = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + 2] * inv_l;
+                v.w = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + 3] * inv_l;
+                *reinterpret_cast<float4*>(stage + (lane & 31) * kStageRow + 32 * cb + 8 * i4 + 4 * hi) = v;
+              }
+            }
+            if (whole) {
+              // 16 lanes per row, 8 channels (16 B of bf16) each.
+#pragma unroll
+              for (int it = 0; it < 8; ++it) {
+                const int r = 4 * it + (lane >> 4);
+                const float* src = stage + r * kStageRow + 8 * (lane & 15);
+                const float4 a = *reinterpret_cast<const float4*>(src);
+                const float4 b = *reinterpret_cast<const float4*>(src + 4);
+                if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
+                  uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32 + r) * 512 + 128 * cq +
+                                 8 * (lane & 15);
+                  *reinterpret_cast<uint4*>(xo) = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                                             pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+                }
+              }
+            } else {
+              // 32 lanes per row, 4 channels (16 B of fp32) each.
+#pragma unroll
+              for (int it = 0; it < 16; ++it) {
+                const int r = 2 * it + (lane >> 5);
+                const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageRow + 4 * (lane & 31));
+                if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
+                  *reinterpret_cast<float4*>(p.part_x + (prow0 + rb * 32 + r) * 512 + 128 * cq + 4 * (lane & 31)) = v;
+                }
+              }
+            }
+          } else if (row_ok) {
+            // Mid-run segment end (the ring is in use): direct stores.
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
@@ -609,30 +776,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                 const int c = 128 * cq + 32 * cb + 8 * i4 + 4 * hi;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = seg_bad ? nanv : o[rb * 4 + cb][4 * i4 + e] * inv_l;
-                *reinterpret_cast<uint2*>(xo + c) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                for (int e = 0; e < 4; ++e) v[e] = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + e] * inv_l;
+                if (whole) {
+                  uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512;
+                  *reinterpret_cast<uint2*>(xo + c) =
+                      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                } else {
+                  *reinterpret_cast<float4*>(p.part_x + (prow0 + row_local) * 512 + c) =
+                      make_float4(v[0], v[1], v[2], v[3]);
+                }
               }
             }
-            if (p.lse != nullptr && cq == 0 && hi == 0) p.lse[(int64_t)pc.b * p.HQ + row] = lse_v;
-          } else {
-            const int slot = 2 * wg + (first_seg ? 0 : 1);
-            const int64_t prow = ((int64_t)g * slots + slot) * kRowsPerGroup + row_local;
-            float* xo = p.part_x + prow * 512;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) {
-                const int c = 128 * cq + 32 * cb + 8 * i4 + 4 * hi;
-                float4 v;
-                v.x = o[rb * 4 + cb][4 * i4 + 0] * inv_l;
-                v.y = o[rb * 4 + cb][4 * i4 + 1] * inv_l;
-                v.z = o[rb * 4 + cb][4 * i4 + 2] * inv_l;
-                v.w = o[rb * 4 + cb][4 * i4 + 3] * inv_l;
-                *reinterpret_cast<float4*>(xo + c) = v;
-              }
-            }
-            if (cq == 0 && hi == 0) p.part_lse[prow] = lse_v;
           }
         }
 #pragma unroll
@@ -640,6 +794,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         first_seg = false;
         seg_bad = 0;
         seg_lo = 0;
+        stored = true;
       }
       pc.next(p);
     }
