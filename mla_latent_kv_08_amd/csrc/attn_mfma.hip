@@ -67,7 +67,8 @@ struct Meta {
 };
 constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
 constexpr int kMaxBase = kMetaBase + 2 * (int)sizeof(Meta);  // tile row maxima [rb][th][32]
-constexpr int kSmemBytes = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);
+constexpr int kFlagBase = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);  // [rb][th] step published
+constexpr int kSmemBytes = kFlagBase + 4 * (int)sizeof(int);
 constexpr int kDmaPerWave = kTile / 4 + 1;             // bf16 loads per P.V wave and tile
 // Query rows of a run's first sequence are staged once in ring buffers 2 and
 // 3 (free until step 0 starts tile 2): latent row r (1 KiB) holds chunk c at
@@ -90,6 +91,7 @@ static_assert(2 * kStageBytes <= kTileBytes, "two P.V waves stage in one free bu
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) volatile int lds_vint;
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 // One buffer load of 16 bytes per lane straight into LDS: lane i's bytes land
@@ -220,25 +222,35 @@ __device__ __forceinline__ int32x4_t buffer_rsrc(const uint8_t* base, uint32_t b
   return r;
 }
 
-// bf16 tile -> LDS by direct buffer loads. Copy wave d (of four) moves latent
-// rows 8d .. 8d+7 (one 64-lane load of 1 KiB each; lane i fetches chunk
-// i ^ swz(t) into slot i) and RoPE group d (lane i: token 8d + i % 8, chunk
-// i / 8). The descriptors span exactly the tile's `valid` rows, so later rows
-// read as zero. Always kDmaPerWave instructions per wave.
-__device__ __forceinline__ void dma_tile_bf16(const CacheView& c, int64_t row0, int valid, int d,
-                                              int lane, uint8_t* dst) {
-  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
-  const uint32_t rs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.rope_stride);
-  const int32x4_t lat = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * ls);
-  const int32x4_t rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * rs);
-#pragma unroll
-  for (int n = 0; n < kTile / 4; ++n) {
+// bf16 tile -> LDS by direct buffer loads, in kDmaPerWave pieces per copy
+// wave d (of four): piece n < 8 moves latent row t = 8d + n (one 64-lane load
+// of 1 KiB; lane i fetches chunk i ^ swz(t) into slot i), piece 8 the RoPE
+// group d (lane i: token 8d + i % 8, chunk i / 8). The descriptors span
+// exactly the tile's `valid` rows, so later rows read as zero.
+struct TileCopy {
+  int32x4_t lat, rope;
+  uint32_t ls, rs;
+  const uint8_t* dst;
+};
+
+__device__ __forceinline__ TileCopy tile_copy(const CacheView& c, int64_t row0, int valid, const uint8_t* dst) {
+  TileCopy t;
+  t.ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
+  t.rs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.rope_stride);
+  t.lat = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * t.ls);
+  t.rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * t.rs);
+  t.dst = dst;
+  return t;
+}
+
+__device__ __forceinline__ void tile_copy_piece(const TileCopy& tc, int d, int lane, int n) {
+  if (n < kTile / 4) {
     const int t = d * (kTile / 4) + n;
-    const int voff = (int)(t * ls) + ((lane ^ swz(t)) << 4);
-    lds_copy16(lat, lds_addr(dst + t * kLatRowBytes), voff);
+    lds_copy16(tc.lat, lds_addr(tc.dst + t * kLatRowBytes), (int)(t * tc.ls) + ((lane ^ swz(t)) << 4));
+  } else {
+    lds_copy16(tc.rope, lds_addr(tc.dst + kRopeBase + d * kRopeGroupBytes),
+               (int)((d * 8 + (lane & 7)) * tc.rs) + ((lane >> 3) << 4));
   }
-  const int voff = (int)((d * 8 + (lane & 7)) * rs) + ((lane >> 3) << 4);
-  lds_copy16(rope, lds_addr(dst + kRopeBase + d * kRopeGroupBytes), voff);
 }
 
 // FP4 tiles, staged by the four P.V waves (256 lanes, index dt): per token 16
@@ -377,6 +389,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   uint8_t* const ptiles = smem + kPBase;
   Meta* const metas = reinterpret_cast<Meta*>(smem + kMetaBase);
   float* const tile_max = reinterpret_cast<float*>(smem + kMaxBase);
+  int* const pair_flag = reinterpret_cast<int*>(smem + kFlagBase);
 
   if (is_score) {
     // ================= score waves: S^T, softmax, probabilities =================
@@ -443,6 +456,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    if (lane == 0) pair_flag[wave] = 0;
     lds_barrier();  // query rows staged
     if (rows_on) {
 #pragma unroll
@@ -461,7 +475,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     }
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
     for (int k = 0; k <= count; ++k) {
-      lds_barrier();  // step k, phase 1
+      lds_barrier();  // step k
       const bool active = rows_on && k < count;
       floatx4 s[2];
       float mx[2];
@@ -476,6 +490,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         const uint8_t* tb = smem + (k % kRing) * kTileBytes;
 
         // ---- S^T: this wave's 16 tokens x 32 rows (two 16x16 blocks) ----
+        // The score chain (S, then the softmax) bounds the step; while its
+        // matrix ops run, this wave issues ahead of the P.V wave sharing the
+        // SIMD, whose matrix ops then fill the softmax phase.
+        __builtin_amdgcn_s_setprio(2);
         // Each K fragment feeds both row halves; even and odd k-steps
         // accumulate separately so no matrix op waits on the one before.
         {
@@ -507,6 +525,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
         }
 
+        __builtin_amdgcn_s_setprio(0);
+
         // ---- scale, causal limit, row max over this half ----
         // Lane holds rows rb*32 + 16*rh + l16, tokens tok0 + i (i < 4). Raw
         // scores; with a positive scale and no masking the scale enters
@@ -530,8 +550,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh) tile_max[(rb * 2 + th) * 32 + 16 * rh + l16] = mx[rh];
         }
+        // Publish this half's maxima for step k, then wait for the other
+        // half's. Both waves of the pair reach this point in every active
+        // step; the wait is bounded all the same.
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): maxima written
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) *(lds_vint*)(pair_flag + wave) = k + 1;
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          if (__builtin_amdgcn_readfirstlane(*(lds_vint*)(pair_flag + (wave ^ 1))) > k) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
       }
-      lds_barrier();  // step k, phase 2
       if (active) {
         // ---- online softmax in the log2 domain ----
         // Both halves see the same tile max, so their running max m and
@@ -612,17 +642,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     Cursor ic = cur;
     int issued = 0;
     Fp4Stage st;
-    auto issue = [&]() {
+    // Next tile's copy: its LDS buffer and descriptors (FP4: its registers loaded).
+    auto next_copy = [&]() {
       bool bad = false;
       const int64_t r0 = tile_row0(p.cache, ic.b, ic.tile, bad);
       const int valid = bad ? 1 : min(kTile, ic.L - ic.tile * kTile);
-      if constexpr (kFp4) {
-        load_tile_fp4(p.cache, r0, valid, dt, st);
-      } else {
-        dma_tile_bf16(p.cache, r0, valid, cq, lane, smem + (issued % kRing) * kTileBytes);
-      }
+      const TileCopy tc = tile_copy(p.cache, r0, valid, smem + (issued % kRing) * kTileBytes);
+      if constexpr (kFp4) load_tile_fp4(p.cache, r0, valid, dt, st);
       ++issued;
       ic.next(p);
+      return tc;
+    };
+    auto issue = [&]() {
+      const TileCopy tc = next_copy();
+      if constexpr (!kFp4) {
+#pragma unroll
+        for (int n = 0; n < kDmaPerWave; ++n) tile_copy_piece(tc, cq, lane, n);
+      }
     };
     // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in
     // registers) into buffers 0 and 1, beside the staged query rows.
@@ -639,6 +675,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     floatx16 o[8];        // [rb * 4 + cb]
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+    // P.V of 16 tokens (k-step kk) of tile kt.
     auto pv_half = [&](int kt, int kk) {
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
@@ -664,19 +701,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         }
       }
       stored = false;
-      lds_barrier();  // step k, phase 1
+      lds_barrier();  // step k
+      // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1
+      // (FP4: decode tile k+1 into the buffer tile k-3 left, fetch tile k+2).
       if constexpr (kFp4) {
-        // Decode tile k+1 (its buffer held tile k-3), then fetch tile k+2.
         if (k + 1 < count) {
           store_tile_fp4(smem + ((k + 1) % kRing) * kTileBytes, dt, st);
           if (issued < count) issue();
         }
-      } else {
-        // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
-        if (issued < count) issue();
+      } else if (issued < count) {
+        issue();
       }
       const int kt = k - 1;  // tile of this step
-      if (k > 0) {
+      if (k == 0) continue;
+      {
         bool bad = false;
         (void)tile_row0(p.cache, pc.b, pc.tile, bad);
         seg_bad |= bad ? 1 : 0;
@@ -692,8 +730,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         }
         pv_half(kt, 0);
       }
-      lds_barrier();  // step k, phase 2
-      if (k == 0) continue;
       pv_half(kt, 1);
 
       const int nt = tiles_of(pc.L);
