@@ -362,6 +362,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   int total = 0;
   const int base = block_exclusive_scan<kThreads>(my_tiles, s_tmp, &total);
   const int per = (total + p.workgroups - 1) / p.workgroups;
+  if (wg == 0 && g == 0) {
+    // The run plan, for the combine kernel.
+    int acc = base;
+    for (int b = b_lo; b < b_hi; ++b) {
+      p.plan[b] = acc;
+      acc += tiles_of(seq_len(p, b));
+    }
+    if (tid == 0) p.plan[p.B] = total;
+  }
   const int start = wg * per;
   const int end = min(total, start + per);
   if (start >= end) return;
@@ -842,27 +851,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 // Grid: (B, groups * 4); each block handles 16 query rows of one sequence.
 constexpr int kCombineThreads = 256;
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParams p) {
-  __shared__ int s_tmp[kCombineThreads / 64];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int g = blockIdx.y >> 2;
   const int rb = blockIdx.y & 3;
 
-  const int per_thread = (p.B + kCombineThreads - 1) / kCombineThreads;
-  const int b_lo = min(p.B, tid * per_thread);
-  const int b_hi = min(p.B, b_lo + per_thread);
-  int my_tiles = 0;
-  int before = 0;
-  for (int j = b_lo; j < b_hi; ++j) {
-    const int n = tiles_of(seq_len(p, j));
-    my_tiles += n;
-    if (j < b) before += n;
-  }
-  int cum_b = 0;
-  block_exclusive_scan<kCombineThreads>(before, s_tmp, &cum_b);
-  int total_tiles = 0;
-  block_exclusive_scan<kCombineThreads>(my_tiles, s_tmp, &total_tiles);
+  // Run plan left by the attention kernel.
   const int nb = tiles_of(seq_len(p, b));
+  const int cum_b = p.plan[b];
+  const int total_tiles = p.plan[p.B];
 
   const int row_local = rb * 16 + (tid >> 4);
   const int row = g * kRowsPerGroup + row_local;

@@ -29,6 +29,7 @@ struct AttnParams {
   float* lse;    // [B, HQ] or null
   float* part_x;    // [G, 2W, kRowsPerGroup, Ckv] fp32 partial results
   float* part_lse;  // [G, 2W, kRowsPerGroup]
+  int* plan;        // [B + 1]: run-order index of each sequence's first tile, then the total
   int B, H, Q, HQ, Ckv, Dr;
   int groups;      // G = ceil(HQ / kRowsPerGroup)
   int workgroups;  // W per row group
