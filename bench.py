@@ -258,19 +258,36 @@ def main():
     ms_step = ms_total / args.steps
 
     # The attention call alone (attention kernel + merge), over the cache
-    # copies in turn: each timed on its stream by a pair of HIP events.
-    ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev_attn[i][0].record(stream)
+    # copies in turn, on its stream: one pair of HIP events around `steps`
+    # back-to-back calls gives the average (the host enqueues ahead, so no
+    # launch latency enters); a pair around each call of a second pass gives
+    # the spread (those include the per-call launch gap when the GPU waits
+    # for the host).
+    def attn_call(i):
         if not args.graph:
             attend(i % ncopy, stream)
         else:
             attn_graphs[i % ncopy].replay()
+
+    attn_call(0)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    a0.record(stream)
+    for i in range(args.steps):
+        attn_call(i)
+    a1.record(stream)
+    host_us = (time.perf_counter() - h0) / args.steps * 1e6
+    torch.cuda.synchronize()
+    attn_avg_ms = a0.elapsed_time(a1) / args.steps
+    ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev_attn[i][0].record(stream)
+        attn_call(i)
         ev_attn[i][1].record(stream)
     torch.cuda.synchronize()
     attn_ms = sorted(a.elapsed_time(b) for a, b in ev_attn)
-    attn_avg_ms = sum(attn_ms) / len(attn_ms)
     pct = lambda p: attn_ms[min(len(attn_ms) - 1, int(p * len(attn_ms)))]  # noqa: E731
     if not torch.isfinite(out.float()).all():
         print("non-finite output", file=sys.stderr)
@@ -307,7 +324,8 @@ def main():
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},
         "attn": {"kernel": "mla_decode_attn (token-split attention + merge)",
-                 "avg_ms": attn_avg_ms, "p50_ms": pct(0.5), "p95_ms": pct(0.95), "p99_ms": pct(0.99),
+                 "avg_ms": attn_avg_ms, "host_us_per_call": host_us,
+                 "per_call_p50_ms": pct(0.5), "per_call_p95_ms": pct(0.95), "per_call_p99_ms": pct(0.99),
                  "alg_bytes": bytes_alg, "alg_flops": flops, "kv_GBps": cache_bytes / attn_s / 1e9,
                  "mfma_TFLOPs": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                  "kernel_source_hash": kernel_source_hash()},
