@@ -137,8 +137,168 @@ def cpu_baseline(w, inp, budget_s: float = 15.0):
             break
     dt = time.perf_counter() - t0
     return {"value": done * w.Q / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{done} of {w.B} sequences (all {w.H} heads, {int(inp.seq_lens[0])} cached tokens "
                       f"each), fp64 non-absorbed oracle, {dt:.1f} s wall"}
+
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cache_row_bytes(w) -> int:
+    """Bytes of one cached token: [latent | rope] in the storage dtype, or FP4 codes + scales + bf16 rope."""
+    if w.dtype == "fp4":
+        return w.Ckv // 2 + w.Ckv // 16 + 2 * w.Dr
+    return (w.Ckv + w.Dr) * (4 if w.dtype == "f32" else 2)
+
+
+def attn_cost(w, lens):
+    """Algorithmic bytes and flops of one attention call: every visible cache row read once,
+    q_lat / q_pe read and x / lse written once; 2*(Ckv + Dr + Ckv) flop per (head, query,
+    visible token), with query q of Q seeing the first len - Q + q + 1 tokens."""
+    es = 4 if w.dtype == "f32" else 2
+    cache_bytes = sum(lens) * cache_row_bytes(w)
+    io_bytes = w.B * w.H * w.Q * (w.Ckv * es + w.Dr * es + w.Ckv * es + 4)
+    flops = sum(w.H * max(0, min(L, L - w.Q + q + 1)) * 2 * (2 * w.Ckv + w.Dr)
+                for L in lens for q in range(w.Q))
+    return cache_bytes, io_bytes, flops
+
+
+def time_back_to_back(fn, n: int, stream) -> float:
+    """Average ms of fn(i) over n calls enqueued back to back between one pair of HIP events."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def setup_attn_case(w, dev, copies: int):
+    """Seeded inputs of workload w on the GPU: q_lat from mla_absorb_q, the cache in the
+    workload's layout (paged ones with NaN in every unused row), outputs and workspace."""
+    import torch
+    import workloads as W
+    from mla_latent_kv_08_amd import ops
+    inp = W.generate(w)
+    pl = W.place(inp)
+    pt = pl.page_table.to(dev) if pl.page_table is not None else None
+    lens = [int(v) for v in inp.seq_lens]
+    seq_lens = inp.seq_lens.to(dev)
+    max_len = max(lens)
+    caches = []
+    if w.dtype != "fp4":
+        phys = W.combined_rows(inp.latent, inp.rope, pl, fill=float("nan"))
+        for _ in range(copies):
+            caches.append(ops.LatentCache.combined(phys.to(dev), w.Ckv, pl.capacity, page_table=pt))
+        del phys
+    else:
+        # FP4 rows are written by the library's own append (fp32 latent in, codes + scales out).
+        row = ops.LatentCache.fp4_row_bytes(w.Ckv, w.Dr)
+        buf = torch.full((pl.n_rows, row), 0xFF, dtype=torch.uint8, device=dev)
+        first = ops.LatentCache.fp4(buf, w.Ckv, pl.capacity, page_table=pt)
+        c = torch.zeros(w.B, max_len, w.Ckv, dtype=torch.float32)
+        r = torch.zeros(w.B, max_len, w.Dr, dtype=inp.rope.dtype)
+        for b, L in enumerate(lens):
+            if L:
+                c[b, max_len - L:] = inp.seq_latent(b)
+                r[b, max_len - L:] = inp.seq_rope(b)
+        ops.mla_cache_append(c.to(dev), r.to(dev), first, seq_lens)
+        del c, r
+        caches.append(first)
+        for _ in range(copies - 1):
+            caches.append(ops.LatentCache.fp4(buf.clone(), w.Ckv, pl.capacity, page_table=pt))
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    q_lat = torch.empty(w.B, w.H, w.Q, w.Ckv, dtype=dt, device=dev)
+    ops.mla_absorb_q(inp.q_nope.to(dev), inp.wkv_b.to(dev), q_lat)
+    code = ops.MLA_F32 if w.dtype == "f32" else ops.MLA_BF16
+    ws = ops.mla_decode_workspace_size(w.B, w.H, w.Q, code, max_len)
+    torch.cuda.synchronize()
+    return {"lens": lens, "caches": caches, "seq_lens": seq_lens, "max_len": max_len,
+            "q_lat": q_lat, "q_pe": inp.q_pe.to(dev), "x": torch.empty_like(q_lat),
+            "lse": torch.empty(w.B, w.H, w.Q, dtype=torch.float32, device=dev),
+            "workspace": torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)}
+
+
+# The other workloads of the method's measurement table: the attention call
+# alone, with its own roofline. Caches of 436 MB and more exceed the 256 MB
+# Infinity Cache; the FP4 one is still rotated over two copies.
+OTHER_WORKLOADS = {"tiny_f32": 1, "ragged_paged_bf16": 1, "long_splitkv_bf16": 1, "mtp_fp4": 2}
+
+
+def measure_other_workloads(dev, stream, reps: int) -> dict:
+    import torch
+    import workloads as W
+    from mla_latent_kv_08_amd import ops
+    out = {}
+    for name, copies in OTHER_WORKLOADS.items():
+        w = W.WORKLOADS[name]
+        print(f"bench: workload {name}", file=sys.stderr, flush=True)
+        case = setup_attn_case(w, dev, copies)
+
+        def call(i, case=case, w=w):
+            ops.mla_decode_attn(case["q_lat"], case["q_pe"], case["caches"][i % len(case["caches"])],
+                                case["seq_lens"], case["max_len"], w.softmax_scale, case["x"],
+                                case["lse"], workspace=case["workspace"], stream=stream)
+
+        ms = time_back_to_back(call, reps, stream)
+        if not torch.isfinite(case["x"].float()).all():
+            raise SystemExit(f"{name}: non-finite attention output")
+        cache_b, io_b, flops = attn_cost(w, case["lens"])
+        t = ms / 1e3
+        t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
+        t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        rec = {"attn_avg_ms": ms, "B": w.B, "H": w.H, "Q": w.Q, "tokens": sum(case["lens"]),
+               "cache": ("paged 64-token pages" if w.paged else "contiguous") + f", {w.dtype} latent",
+               "cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops,
+               "kv_GBps": cache_b / t / 1e9, "mfma_TFLOPs": flops / t / 1e12}
+        if w.dtype == "f32":
+            rec["bound"] = "launch latency"
+        else:
+            rec["bound"] = "hbm" if t_hbm >= t_mfma else "mfma"
+            rec["t_roofline_us"] = max(t_hbm, t_mfma) * 1e6
+            rec["roofline_frac"] = max(t_hbm, t_mfma) / t
+        out[name] = rec
+        del case
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def copy_gbps(dev, stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy rate (bytes read + written per second) as context for the roofline."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = time_back_to_back(lambda i: dst.copy_(src), reps, stream)
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def gpu_context(dev) -> dict:
+    import subprocess
+    import torch
+    info = {"device": torch.cuda.get_device_name(dev), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        info["clocks"] = [ln.split(":", 2)[-1].strip() for ln in r.stdout.splitlines()
+                          if "sclk" in ln or "mclk" in ln or "fclk" in ln][:6]
+    except Exception as e:  # pragma: no cover - tool missing or slow
+        info["clocks"] = f"unavailable ({type(e).__name__})"
+    return info
 
 
 def main():
@@ -152,6 +312,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step (and the timed attention calls) from captured HIP "
                          "graphs instead of launching the calls one by one")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads (ragged paged, long context, FP4 MTP, tiny fp32) "
+                         "and the context figures (copy rate, clocks)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device-to-device copy of COPY_BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -257,6 +420,30 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
 
+    # Each call's share of a step: a second eager pass with an event between
+    # consecutive calls (so each call sees the cache state of a real step).
+    names = ("append", "absorb", "attn", "up_proj")
+    in_step = {k: 0.0 for k in names}
+    if not args.graph:
+        evs = []
+        for i in range(args.steps):
+            c = i % ncopy
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[0].record(stream)
+            ops.mla_cache_append(c_new, r_new, caches[c], seq_lens, stream=stream)
+            e[1].record(stream)
+            ops.mla_absorb_q(q_nope, wkv_b, q_lat, stream=stream)
+            e[2].record(stream)
+            attend(c, stream)
+            e[3].record(stream)
+            ops.mla_up_proj_v(x, wkv_b, out, stream=stream)
+            e[4].record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        for e in evs:
+            for j, k in enumerate(names):
+                in_step[k] += e[j].elapsed_time(e[j + 1]) / args.steps
+
     # The attention call alone (attention kernel + merge), over the cache
     # copies in turn, on its stream: one pair of HIP events around `steps`
     # back-to-back calls gives the average (the host enqueues ahead, so no
@@ -294,14 +481,31 @@ def main():
         sys.exit(3)
 
     lens = [int(v) for v in inp.seq_lens]
-    cache_bytes = sum(lens) * (w.Ckv + w.Dr) * 2
-    io_bytes = B * H * Q * (w.Ckv * 2 + w.Dr * 2 + w.Ckv * 2 + 4)
+    cache_bytes, io_bytes, flops = attn_cost(w, lens)
     bytes_alg = cache_bytes + io_bytes
-    flops = sum(H * min(L, L - Q + q + 1) * 2 * (2 * w.Ckv + w.Dr) for L in lens for q in range(Q))
+    # The projections against their own weight-bandwidth roofline (bf16 weights
+    # read once, activations in and out once).
+    wt = H * w.Dn * w.Ckv * 2
+    proj_bytes = {"absorb": wt + B * H * Q * (w.Dn + w.Ckv) * 2,
+                  "up_proj": H * w.Vd * w.Ckv * 2 + B * H * Q * (w.Ckv + w.Vd) * 2,
+                  "append": 2 * B * Q * (w.Ckv + w.Dr) * 2}
     attn_s = attn_avg_ms / 1e3
     achieved_gbps = bytes_alg / attn_s / 1e9
     tflops = flops / attn_s / 1e12
     traffic = load_traffic(bytes_alg)
+    calls = {}
+    for k in names:
+        if args.graph:
+            break
+        calls[k] = {"ms": in_step[k]}
+        if k in proj_bytes and in_step[k] > 0:
+            gbps = proj_bytes[k] / (in_step[k] / 1e3) / 1e9
+            calls[k].update({"alg_bytes": proj_bytes[k], "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS})
+    others, context = None, None
+    if not args.headline_only:
+        others = measure_other_workloads(dev, stream, max(10, args.steps))
+        context = gpu_context(dev)
+        context["copy_GBps"] = copy_gbps(dev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
     rec = {
         "metric": METRIC,
@@ -329,6 +533,9 @@ def main():
                  "alg_bytes": bytes_alg, "alg_flops": flops, "kv_GBps": cache_bytes / attn_s / 1e9,
                  "mfma_TFLOPs": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                  "kernel_source_hash": kernel_source_hash()},
+        "calls_in_step": calls or None,
+        "workloads": others,
+        "context": context,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
