@@ -19,39 +19,55 @@ __device__ __forceinline__ float load_src(const void* base, int64_t idx, int dty
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
-// grid (B * Qn); one 64-lane wave per new token.
+// grid (B * Qn); one 64-lane wave per new token. The source row is read
+// into registers before the length (and the page table) is looked at, so the
+// row's load and the position lookup overlap instead of following each other.
+constexpr int kAppendWords = 8;  // 4-byte words per lane and pass (2 KiB per wave)
 __global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
   const int lane = threadIdx.x;
   const int b = blockIdx.x / p.Qn;
   const int j = blockIdx.x % p.Qn;
-  const int len = p.seq_lens[b];
-  const int pos = len - p.Qn + j;
-  if (pos < 0 || pos >= p.cache.capacity) return;
-  bool bad = false;
-  const int64_t r = phys_row(p.cache, b, pos, bad);
-  if (bad) return;
   const int64_t src_row = (int64_t)b * p.Qn + j;
   const CacheView& c = p.cache;
+  const int rope_words = p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
+  const bool fp4 = p.latent_dtype == MLA_FP4_E2M1_E4M3X16;
+  const int lat_words = fp4 ? 0 : p.Ckv * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
+  const uint32_t* __restrict__ src_pe = reinterpret_cast<const uint32_t*>(p.k_pe) + src_row * rope_words;
+  const uint32_t* __restrict__ src_lat = reinterpret_cast<const uint32_t*>(p.c_kv) + src_row * lat_words;
 
-  // RoPE part: same dtype in and out.
-  const int rb = p.rope_dtype == MLA_F32 ? 4 : 2;
-  {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.k_pe) + src_row * p.Dr * rb;
-    uint8_t* dst = const_cast<uint8_t*>(c.rope) + r * c.rope_stride;
-    for (int i = lane * 4; i < p.Dr * rb; i += 64 * 4) {
-      *reinterpret_cast<uint32_t*>(dst + i) = *reinterpret_cast<const uint32_t*>(src + i);
-    }
+  // First pass of the row (RoPE words, then latent words) into registers.
+  const int total = rope_words + lat_words;
+  uint32_t v[kAppendWords];
+#pragma unroll
+  for (int k = 0; k < kAppendWords; ++k) {
+    const int i = lane + 64 * k;
+    v[k] = i < rope_words ? src_pe[i] : (i < total ? src_lat[i - rope_words] : 0u);
   }
-
+  const int len = p.seq_lens[b];
+  const int pos = len - p.Qn + j;
+  if (pos < 0 || pos >= c.capacity) return;
+  bool bad = false;
+  const int64_t r = phys_row(c, b, pos, bad);
+  if (bad) return;
+  uint32_t* dst_pe = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(c.rope) + r * c.rope_stride);
   uint8_t* lat = const_cast<uint8_t*>(c.latent) + r * c.latent_stride;
-  if (p.latent_dtype != MLA_FP4_E2M1_E4M3X16) {
-    const int eb = p.latent_dtype == MLA_F32 ? 4 : 2;
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.c_kv) + src_row * p.Ckv * eb;
-    for (int i = lane * 4; i < p.Ckv * eb; i += 64 * 4) {
-      *reinterpret_cast<uint32_t*>(lat + i) = *reinterpret_cast<const uint32_t*>(src + i);
+  uint32_t* dst_lat = reinterpret_cast<uint32_t*>(lat);
+  for (int base = 0; base < total; base += 64 * kAppendWords) {
+    if (base > 0) {
+#pragma unroll
+      for (int k = 0; k < kAppendWords; ++k) {
+        const int i = base + lane + 64 * k;
+        v[k] = i < rope_words ? src_pe[i] : (i < total ? src_lat[i - rope_words] : 0u);
+      }
     }
-    return;
+#pragma unroll
+    for (int k = 0; k < kAppendWords; ++k) {
+      const int i = base + lane + 64 * k;
+      if (i < rope_words) dst_pe[i] = v[k];
+      else if (i < total) dst_lat[i - rope_words] = v[k];
+    }
   }
+  if (!fp4) return;
 
   // FP4: a pair of lanes per 16-channel group, 8 channels per lane.
   uint8_t* scl = const_cast<uint8_t*>(c.scale) + r * c.scale_stride;

@@ -77,31 +77,39 @@ __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
   const int h = blockIdx.x;
   const int c0 = blockIdx.y * 128;
   const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)h * (p.Dn + p.Vd) * p.Ckv;
-#pragma unroll
-  for (int k = 0; k < 128 * 16 / kThreads; ++k) {
-    const int s = tid + kThreads * k;  // 16-byte chunk: row d, chunk j
-    const int d = s >> 4, j = s & 15;
-    *reinterpret_cast<uint4*>(s_w + d * kWPad + 8 * j) =
-        *reinterpret_cast<const uint4*>(w + (int64_t)d * p.Ckv + c0 + 8 * j);
-  }
   const int M = p.B * p.Q;
   // Query rows are [B, H, Q, Dn]: row m = (b, q) of head h.
   auto q_row = [&](int m) {
     const int bb = m / p.Q, qq = m % p.Q;
     return ((int64_t)bb * p.H + h) * p.Q + qq;
   };
+  if (M <= 0) return;
   // Stage thread tid: row tid / 8 of the block, 16 elements at 16 * (tid % 8).
   const int sr = tid >> 3, sc = 16 * (tid & 7);
+  const uint16_t* qin = reinterpret_cast<const uint16_t*>(p.in) + sc;
+  // The weight block and the first query block are requested together.
+  uint4 wr[128 * 16 / kThreads];
+#pragma unroll
+  for (int k = 0; k < 128 * 16 / kThreads; ++k) {
+    const int s = tid + kThreads * k;  // 16-byte chunk: row d, chunk j
+    wr[k] = *reinterpret_cast<const uint4*>(w + (int64_t)(s >> 4) * p.Ckv + c0 + 8 * (s & 15));
+  }
+  // This thread's share of the next query block, in flight.
+  uint4 qa = *reinterpret_cast<const uint4*>(qin + q_row(min(sr, M - 1)) * p.Dn);
+  uint4 qb = *reinterpret_cast<const uint4*>(qin + q_row(min(sr, M - 1)) * p.Dn + 8);
+#pragma unroll
+  for (int k = 0; k < 128 * 16 / kThreads; ++k) {
+    const int s = tid + kThreads * k;
+    *reinterpret_cast<uint4*>(s_w + (s >> 4) * kWPad + 8 * (s & 15)) = wr[k];
+  }
   for (int m0 = 0; m0 < M; m0 += 32) {
-    {
-      const int m = min(m0 + sr, M - 1);
-      const uint16_t* q = reinterpret_cast<const uint16_t*>(p.in) + q_row(m) * p.Dn + sc;
-      const uint4 a = *reinterpret_cast<const uint4*>(q);
-      const uint4 b = *reinterpret_cast<const uint4*>(q + 8);
-      *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc) = a;
-      *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc + 8) = b;
-    }
+    *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc) = qa;
+    *reinterpret_cast<uint4*>(s_q + sr * kQPad + sc + 8) = qb;
     __syncthreads();
+    if (m0 + 32 < M) {
+      qa = *reinterpret_cast<const uint4*>(qin + q_row(min(m0 + 32 + sr, M - 1)) * p.Dn);
+      qb = *reinterpret_cast<const uint4*>(qin + q_row(min(m0 + 32 + sr, M - 1)) * p.Dn + 8);
+    }
     // A (k-step ks: d = 16*ks + 8*hi + 0..7, channel c0 + 32*wave + lane%32):
     // 16-lane group g reads rows 16*ks + 8*hi + {0..3} (then +4) of channels
     // 32*wave + 16*(g & 1) .. +15; lane j of the group addresses row j/4, cols 4*(j%4).
@@ -150,26 +158,50 @@ __global__ void __launch_bounds__(kThreads) up_bf16_kernel(ProjParams p) {
   const int h = blockIdx.x;
   const int v0 = blockIdx.y * 32;
   const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) + ((int64_t)h * (p.Dn + p.Vd) + p.Dn + v0) * p.Ckv;
-  // Stage: chunk s = tid + 256*k is row s / 64, 8 elements at 8 * (s % 64).
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int s = tid + kThreads * k;
-    const int r = s >> 6, c = 8 * (s & 63);
-    *reinterpret_cast<uint4*>(s_w + r * kRowPad + c) = *reinterpret_cast<const uint4*>(w + (int64_t)r * p.Ckv + c);
-  }
   const int M = p.B * p.Q;
   auto x_row = [&](int m) {
     const int bb = m / p.Q, qq = m % p.Q;
     return ((int64_t)bb * p.H + h) * p.Q + qq;
   };
+  if (M <= 0) return;
+  // Stage: chunk s = tid + 256*k is row s / 64, 8 elements at 8 * (s % 64).
+  const uint16_t* xin = reinterpret_cast<const uint16_t*>(p.in);
   const int cq = 128 * wave;  // this wave's quarter of the contraction
-  for (int m0 = 0; m0 < M; m0 += 32) {
+  // The first block's x rows are requested together with the weight rows.
+  // (Each staging array lives in one straight stretch of code: carried across
+  // a branch or the loop, the compiler keeps such an array in scratch memory.)
+  {
+    uint4 wr[8], xr[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int s = tid + kThreads * k;
-      const int r = s >> 6, c = 8 * (s & 63);
-      const uint16_t* x = reinterpret_cast<const uint16_t*>(p.in) + x_row(min(m0 + r, M - 1)) * p.Ckv + c;
-      *reinterpret_cast<uint4*>(s_x + r * kRowPad + c) = *reinterpret_cast<const uint4*>(x);
+      wr[k] = *reinterpret_cast<const uint4*>(w + (int64_t)(s >> 6) * p.Ckv + 8 * (s & 63));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = tid + kThreads * k;
+      xr[k] = *reinterpret_cast<const uint4*>(xin + x_row(min(s >> 6, M - 1)) * p.Ckv + 8 * (s & 63));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = tid + kThreads * k;
+      *reinterpret_cast<uint4*>(s_w + (s >> 6) * kRowPad + 8 * (s & 63)) = wr[k];
+      *reinterpret_cast<uint4*>(s_x + (s >> 6) * kRowPad + 8 * (s & 63)) = xr[k];
+    }
+  }
+  for (int m0 = 0; m0 < M; m0 += 32) {
+    if (m0 > 0) {
+      uint4 xr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = tid + kThreads * k;
+        xr[k] = *reinterpret_cast<const uint4*>(xin + x_row(min(m0 + (s >> 6), M - 1)) * p.Ckv + 8 * (s & 63));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = tid + kThreads * k;
+        *reinterpret_cast<uint4*>(s_x + (s >> 6) * kRowPad + 8 * (s & 63)) = xr[k];
+      }
     }
     __syncthreads();
     floatx16 acc = floatx16{};
