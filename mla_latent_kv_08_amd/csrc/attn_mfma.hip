@@ -55,9 +55,13 @@ constexpr int kLatRowBytes = 1024;                     // 512 bf16 latent channe
 constexpr int kRopeGroupBytes = 1152;                  // 8 tokens x 128 B, + 128 B pad
 constexpr int kRopeBase = kTile * kLatRowBytes;        // RoPE groups follow the latent rows
 constexpr int kTileBytes = kRopeBase + (kTile / 8) * kRopeGroupBytes;  // 37376
-constexpr int kRing = 4;                               // LDS tile buffers
 constexpr int kPSlotBytes = 2 * 2 * 64 * 16;           // [rb][kk][lane] bf16x8
-constexpr int kPBase = kRing * kTileBytes;
+// A raw FP4 tile as copied from the cache: codes [32][256 B], E4M3 scales
+// [32][32 B], bf16 RoPE [32][128 B].
+constexpr int kRawCodeBytes = kTile * 256;
+constexpr int kRawScaleBase = kRawCodeBytes;
+constexpr int kRawRopeBase = kRawScaleBase + kTile * 32;
+constexpr int kRawBytes = kRawRopeBase + kTile * 128;  // 13312
 struct Meta {
   float alpha[kRowsPerGroup];  // factor on O before this tile's P.V
   float m[kRowsPerGroup];      // running max after this tile
@@ -65,16 +69,35 @@ struct Meta {
   int rescale[2];              // per row block: some alpha != 1
   int pad[2];
 };
-constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
-constexpr int kMaxBase = kMetaBase + 2 * (int)sizeof(Meta);  // tile row maxima [rb][th][32]
-constexpr int kFlagBase = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);  // [rb][th] step published
-constexpr int kSmemBytes = kFlagBase + 4 * (int)sizeof(int);
 constexpr int kDmaPerWave = kTile / 4 + 1;             // bf16 loads per P.V wave and tile
-// Query rows of a run's first sequence are staged once in ring buffers 2 and
-// 3 (free until step 0 starts tile 2): latent row r (1 KiB) holds chunk c at
-// slot c ^ (r % 16); the RoPE part is chunk-major, [8 chunks][64 rows][16 B].
-constexpr int kQBase = 2 * kTileBytes;
-constexpr int kQRopeBase = kQBase + kRowsPerGroup * kLatRowBytes;
+constexpr int kFp4DmaPerWave = 4;                      // FP4 loads per P.V wave and tile
+
+// LDS layout. bf16 cache: a ring of four tile buffers (the P.V tile, the
+// score tile, two tiles in flight). FP4 cache: a ring of three bf16 tile
+// buffers (P.V tile, score tile, the next tile being decoded) and three raw
+// slots, so three raw tiles are in flight while one is decoded. Then the
+// probability slots, the per-tile metadata, the tile row maxima [rb][th][32]
+// and the pair flags [rb][th].
+// Query rows of a run's first sequence are staged once in two ring buffers
+// that stay free until step 0 (bf16: 2 and 3, whose tile copies start in
+// step 0; FP4: 1 and 2, whose decoding starts in step 0): latent row r
+// (1 KiB) holds chunk c at slot c ^ (r % 16); the RoPE part is chunk-major,
+// [8 chunks][64 rows][16 B].
+template <bool kFp4>
+struct Lds {
+  static constexpr int kRing = kFp4 ? 3 : 4;
+  static constexpr int kRawSlots = kFp4 ? 3 : 0;
+  static constexpr int kRawBase = kRing * kTileBytes;
+  static constexpr int kPBase = kRawBase + kRawSlots * kRawBytes;
+  static constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
+  static constexpr int kMaxBase = kMetaBase + 2 * (int)sizeof(Meta);
+  static constexpr int kFlagBase = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);
+  static constexpr int kBytes = kFlagBase + 4 * (int)sizeof(int);
+  static constexpr int kQBase = (kFp4 ? 1 : 2) * kTileBytes;
+  static constexpr int kQRopeBase = kQBase + kRowsPerGroup * kLatRowBytes;
+  static_assert(kBytes <= 160 * 1024, "LDS budget");
+  static_assert(kQRopeBase + 8 * kRowsPerGroup * 16 <= kQBase + 2 * kTileBytes, "query staging fits two buffers");
+};
 // Final results of a run are staged per P.V wave in free ring buffers as 32
 // rows x 128 fp32 channels, rows padded to 132 floats (bank spread).
 constexpr int kStageRow = 132;
@@ -84,8 +107,6 @@ constexpr float kRescaleLog2 = 8.0f;  // p = 2^(s - m) stays <= 2^8
 
 static_assert(kTile == 32 && kRowsPerGroup == 64, "two 32-row blocks, two 16-token halves per tile");
 static_assert(kPageTokens % kTile == 0, "a tile never crosses a page");
-static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
-static_assert(kQRopeBase + 8 * kRowsPerGroup * 16 <= 4 * kTileBytes, "query staging fits buffers 2, 3");
 static_assert(2 * kStageBytes <= kTileBytes, "two P.V waves stage in one free buffer");
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -253,58 +274,85 @@ __device__ __forceinline__ void tile_copy_piece(const TileCopy& tc, int d, int l
   }
 }
 
-// FP4 tiles, staged by the four P.V waves (256 lanes, index dt): per token 16
-// code chunks (32 channels each) with their 2 scale bytes, and 8 RoPE chunks.
-// Lane dt takes code chunks s = dt + 256*k (token s >> 4, chunk s & 15) and
-// RoPE chunk s = dt (token s >> 3, chunk s & 7); it decodes its codes (E2M1
-// value times E4M3 scale, exact in bf16) when writing them to the bf16 tile.
-// Rows at or past `valid` re-read the last valid row (masked, finite).
-struct Fp4Stage {
-  uint4 codes[2];
-  uint32_t scales[2];
-  uint4 rope;
+// FP4 tiles. P.V wave d (of four) copies and decodes tokens 8d .. 8d+7 of
+// each tile, so it only ever reads raw bytes its own copies wrote and needs
+// no barrier between copy and decode. Its four buffer-to-LDS loads per tile:
+// the codes of tokens 8d .. 8d+3 and 8d+4 .. 8d+7 (lane i: token i / 16,
+// 16-byte chunk i % 16), their RoPE keys (lane i: token i / 8, chunk i % 8)
+// and their scales (lanes 0..15: token i / 2, half i % 2). The descriptors
+// span exactly the tile's `valid` rows, so later rows read as zero (code 0
+// times scale 0).
+struct Fp4Copy {
+  int32x4_t codes, scales, rope;
+  uint32_t cs, ss, rs;
 };
 
-__device__ __forceinline__ void load_tile_fp4(const CacheView& c, int64_t row0, int valid, int dt,
-                                              Fp4Stage& st) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = dt + 256 * k;
-    const int64_t r = row0 + min(s >> 4, valid - 1);
-    const int j = s & 15;
-    st.codes[k] = *reinterpret_cast<const uint4*>(c.latent + r * c.latent_stride + j * 16);
-    st.scales[k] = *reinterpret_cast<const uint16_t*>(c.scale + r * c.scale_stride + j * 2);
-  }
-  const int64_t r = row0 + min(dt >> 3, valid - 1);
-  st.rope = *reinterpret_cast<const uint4*>(c.rope + r * c.rope_stride + (dt & 7) * 16);
+__device__ __forceinline__ Fp4Copy fp4_copy(const CacheView& c, int64_t row0, int valid) {
+  Fp4Copy f;
+  f.cs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.latent_stride);
+  f.ss = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.scale_stride);
+  f.rs = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.rope_stride);
+  f.codes = buffer_rsrc(c.latent + row0 * c.latent_stride, (uint32_t)valid * f.cs);
+  f.scales = buffer_rsrc(c.scale + row0 * c.scale_stride, (uint32_t)valid * f.ss);
+  f.rope = buffer_rsrc(c.rope + row0 * c.rope_stride, (uint32_t)valid * f.rs);
+  return f;
 }
 
-__device__ __forceinline__ void store_tile_fp4(uint8_t* dst, int dt, const Fp4Stage& st) {
+__device__ __forceinline__ void fp4_copy_pieces(const Fp4Copy& f, const uint8_t* raw, int d, int lane) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = dt + 256 * k;
-    const int t = s >> 4;
-    const int j = s & 15;
-    const float s0 = e4m3_to_f32(st.scales[k] & 0xffu);
-    const float s1 = e4m3_to_f32(st.scales[k] >> 8);
-    const uint32_t words[4] = {st.codes[k].x, st.codes[k].y, st.codes[k].z, st.codes[k].w};
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * d + 4 * h + (lane >> 4);
+    lds_copy16(f.codes, lds_addr(raw + (8 * d + 4 * h) * 256), (int)(t * f.cs) + ((lane & 15) << 4));
+  }
+  {
+    const int t = 8 * d + (lane >> 3);
+    lds_copy16(f.rope, lds_addr(raw + kRawRopeBase + 8 * d * 128), (int)(t * f.rs) + ((lane & 7) << 4));
+  }
+  if (lane < 16) {
+    const int t = 8 * d + (lane >> 1);
+    lds_copy16(f.scales, lds_addr(raw + kRawScaleBase + 8 * d * 32), (int)(t * f.ss) + ((lane & 1) << 4));
+  }
+}
+
+// Two codes (byte e of w) times scale s as two bf16. The hardware conversion
+// takes only the exponent of its scale, so it runs at scale 1 (exact E2M1
+// values) and the E4M3 scale is applied in fp32; every product of an E2M1
+// value and an E4M3 scale fits in bf16, so taking the high halves is exact.
+template <int e>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, e);
+  const uint32_t u = __builtin_bit_cast(uint32_t, r);
+  const float lo = __uint_as_float(u << 16) * s;
+  const float hi = __uint_as_float(u & 0xffff0000u) * s;
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Decode P.V wave d's 8 tokens of a raw tile into the bf16 tile (latent rows
+// with the chunk swizzle, RoPE groups). Lane i: code chunks u = i and i + 64
+// (token u / 16, 32 channels at 32 * (u % 16)) and RoPE chunk i.
+__device__ __forceinline__ void fp4_decode(const uint8_t* raw, uint8_t* dst, int d, int lane) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = lane + 64 * h;
+    const int t = 8 * d + (u >> 4);
+    const int j = u & 15;
+    const uint4 cw = *reinterpret_cast<const uint4*>(raw + 8 * d * 256 + u * 16);
+    const uint32_t sc = *reinterpret_cast<const uint16_t*>(raw + kRawScaleBase + 8 * d * 32 + 2 * u);
+    const float s0 = e4m3_to_f32(sc & 0xffu);
+    const float s1 = e4m3_to_f32(sc >> 8);
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
       const float sv = qd < 2 ? s0 : s1;
-      uint32_t outw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v0 = __uint_as_float(e2m1_f32_bits((words[qd] >> (8 * e)) & 0xfu)) * sv;
-        const float v1 = __uint_as_float(e2m1_f32_bits((words[qd] >> (8 * e + 4)) & 0xfu)) * sv;
-        outw[e] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
-      }
       const int slot = (4 * j + qd) ^ swz(t);
       *reinterpret_cast<uint4*>(dst + t * kLatRowBytes + slot * 16) =
-          make_uint4(outw[0], outw[1], outw[2], outw[3]);
+          make_uint4(fp4_pair<0>(words[qd], sv), fp4_pair<1>(words[qd], sv), fp4_pair<2>(words[qd], sv),
+                     fp4_pair<3>(words[qd], sv));
     }
   }
-  const int t = dt >> 3, ch = dt & 7;
-  *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) = st.rope;
+  const int t = 8 * d + (lane >> 3), ch = lane & 7;
+  *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
+      *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + lane * 16);
 }
 
 // Lane-wise combination across lane groups: lanes l and l ^ 32 (or l ^ 16)
@@ -329,7 +377,9 @@ __device__ __forceinline__ float xor16_sum(float x) {
 
 template <bool kFp4>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  using L = Lds<kFp4>;
+  constexpr int kRing = L::kRing;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
   __shared__ int s_tmp[kThreads / 64];
   __shared__ int s_start[2];
 
@@ -395,10 +445,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   cur.tile = __builtin_amdgcn_readfirstlane(s_start[1]);
   cur.L = seq_len(p, cur.b);
 
-  uint8_t* const ptiles = smem + kPBase;
-  Meta* const metas = reinterpret_cast<Meta*>(smem + kMetaBase);
-  float* const tile_max = reinterpret_cast<float*>(smem + kMaxBase);
-  int* const pair_flag = reinterpret_cast<int*>(smem + kFlagBase);
+  uint8_t* const ptiles = smem + L::kPBase;
+  Meta* const metas = reinterpret_cast<Meta*>(smem + L::kMetaBase);
+  float* const tile_max = reinterpret_cast<float*>(smem + L::kMaxBase);
+  int* const pair_flag = reinterpret_cast<int*>(smem + L::kFlagBase);
 
   if (is_score) {
     // ================= score waves: S^T, softmax, probabilities =================
@@ -456,12 +506,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const int r = 16 * wave + n;
-        lds_copy16(ql, lds_addr(smem + kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
+        lds_copy16(ql, lds_addr(smem + L::kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
       }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int c = 2 * wave + n;
-        lds_copy16(qp, lds_addr(smem + kQRopeBase + c * 1024), lane * 128 + c * 16);
+        lds_copy16(qp, lds_addr(smem + L::kQRopeBase + c * 1024), lane * 128 + c * 16);
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -473,12 +523,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         const int r = rb * 32 + 16 * rh + l16;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
-          qf[rh][ks] = *reinterpret_cast<const bf16x8*>(smem + kQBase + r * kLatRowBytes +
+          qf[rh][ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQBase + r * kLatRowBytes +
                                                          (((4 * ks + g4) ^ (r & 15)) << 4));
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          qf[rh][16 + ks] = *reinterpret_cast<const bf16x8*>(smem + kQRopeBase + (4 * ks + g4) * 1024 + r * 16);
+          qf[rh][16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + r * 16);
         }
       }
     }
@@ -646,34 +696,43 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
     }
 
-    // ---- tile copies: tile k+2 starts in step k ----
-    const int dt = cq * 64 + lane;
+    // ---- tile copies: bf16 tile k+2 starts in step k; FP4 raw tile k+4
+    // starts in step k, after tile k+1 was decoded out of the same slot ----
     Cursor ic = cur;
     int issued = 0;
-    Fp4Stage st;
-    // Next tile's copy: its LDS buffer and descriptors (FP4: its registers loaded).
-    auto next_copy = [&]() {
+    auto issue = [&]() {
       bool bad = false;
       const int64_t r0 = tile_row0(p.cache, ic.b, ic.tile, bad);
       const int valid = bad ? 1 : min(kTile, ic.L - ic.tile * kTile);
-      const TileCopy tc = tile_copy(p.cache, r0, valid, smem + (issued % kRing) * kTileBytes);
-      if constexpr (kFp4) load_tile_fp4(p.cache, r0, valid, dt, st);
-      ++issued;
-      ic.next(p);
-      return tc;
-    };
-    auto issue = [&]() {
-      const TileCopy tc = next_copy();
-      if constexpr (!kFp4) {
+      if constexpr (kFp4) {
+        const Fp4Copy fc = fp4_copy(p.cache, r0, valid);
+        fp4_copy_pieces(fc, smem + L::kRawBase + (issued % L::kRawSlots) * kRawBytes, cq, lane);
+      } else {
+        const TileCopy tc = tile_copy(p.cache, r0, valid, smem + (issued % kRing) * kTileBytes);
 #pragma unroll
         for (int n = 0; n < kDmaPerWave; ++n) tile_copy_piece(tc, cq, lane, n);
       }
+      ++issued;
+      ic.next(p);
     };
-    // Prologue: tiles 0 and 1 on their way (FP4: tile 0 decoded, tile 1 in
-    // registers) into buffers 0 and 1, beside the staged query rows.
+    // Prologue. bf16: tiles 0 and 1 on their way into buffers 0 and 1, beside
+    // the staged query rows. FP4: raw tiles 0..2 on their way; tile 0 decoded
+    // into buffer 0 (this wave's tokens, from its own copies), then tile 3
+    // started in the slot tile 0 left.
     issue();
-    if constexpr (kFp4) store_tile_fp4(smem, dt, st);
     if (issued < count) issue();
+    if constexpr (kFp4) {
+      if (issued < count) issue();
+      if (issued == 3) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4DmaPerWave));
+      } else if (issued == 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4DmaPerWave));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      fp4_decode(smem + L::kRawBase, smem, cq, lane);
+      if (issued < count) issue();
+    }
     lds_barrier();  // query rows staged
 
     Cursor pc = cur;
@@ -708,17 +767,32 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           }
         }
+      } else {
+        // Raw tile k+1 has landed (tiles k+2, k+3 may still be in flight
+        // unless output stores were issued after them).
+        if (k + 1 < count) {
+          const int ahead = stored ? 0 : issued - (k + 2);
+          if (ahead >= 2) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4DmaPerWave));
+          } else if (ahead == 1) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4DmaPerWave));
+          } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          }
+        }
       }
       stored = false;
       lds_barrier();  // step k
-      // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1
-      // (FP4: decode tile k+1 into the buffer tile k-3 left, fetch tile k+2).
       if constexpr (kFp4) {
+        // Decode tile k+1 into the buffer tile k-2 left at the end of step
+        // k-1, then refill its raw slot with tile k+4.
         if (k + 1 < count) {
-          store_tile_fp4(smem + ((k + 1) % kRing) * kTileBytes, dt, st);
+          fp4_decode(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
+                     smem + ((k + 1) % kRing) * kTileBytes, cq, lane);
           if (issued < count) issue();
         }
       } else if (issued < count) {
+        // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
         issue();
       }
       const int kt = k - 1;  // tile of this step
