@@ -3,16 +3,21 @@
 // One workgroup per query row (b, h, q). Tokens are visited in chunks of 256:
 // each thread scores one token (dot product of [q_lat | q_pe] with the
 // token's [latent | rope] row, scaled), the chunk's maximum and sum update the
-// running softmax state, and each thread accumulates the probability-weighted
-// latent for its own channels (exercise page: two score streams merged and
-// scaled, causal mask, softmax, weighted sum over kv_cache).
+// running softmax state, and the probability-weighted latent rows are summed
+// (exercise page: two score streams merged and scaled, causal mask, softmax,
+// weighted sum over kv_cache). In the weighted sum wave w takes tokens w,
+// w + 4, ... of the chunk and lane i the 16-byte chunks i, i + 64, ... of each
+// row, so every row is one coalesced read; the four waves' sums are added at
+// the end.
 #include "internal.h"
 
 namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChanPerThread = 8;  // Ckv <= 2048
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxVec = 8;  // float4 chunks per lane: Ckv <= 2048
+constexpr int kBatch = 16;  // tokens per wave and batch of the weighted sum
 
 __device__ float block_max(float v, float* s_tmp) {
   for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
@@ -21,7 +26,7 @@ __device__ float block_max(float v, float* s_tmp) {
   if (lane == 0) s_tmp[wave] = v;
   __syncthreads();
   float r = s_tmp[0];
-  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, s_tmp[w]);
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, s_tmp[w]);
   return r;
 }
 
@@ -32,15 +37,44 @@ __device__ float block_sum(float v, float* s_tmp) {
   if (lane == 0) s_tmp[wave] = v;
   __syncthreads();
   float r = 0.0f;
-  for (int w = 0; w < kThreads / 64; ++w) r += s_tmp[w];
+  for (int w = 0; w < kWaves; ++w) r += s_tmp[w];
   return r;
 }
 
+// Dot product of n floats (n % 4 == 0) of a global row with LDS values, four
+// partial sums so the loads and multiply-adds overlap.
+__device__ __forceinline__ float dot_row(const float* __restrict__ g, const float* s, int n) {
+  float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+  int i = 0;
+  for (; i + 16 <= n; i += 16) {
+    const float4 a = *reinterpret_cast<const float4*>(g + i);
+    const float4 b = *reinterpret_cast<const float4*>(g + i + 4);
+    const float4 c = *reinterpret_cast<const float4*>(g + i + 8);
+    const float4 e = *reinterpret_cast<const float4*>(g + i + 12);
+    const float4 sa = *reinterpret_cast<const float4*>(s + i);
+    const float4 sb = *reinterpret_cast<const float4*>(s + i + 4);
+    const float4 sc = *reinterpret_cast<const float4*>(s + i + 8);
+    const float4 se = *reinterpret_cast<const float4*>(s + i + 12);
+    d0 += sa.x * a.x + sa.y * a.y + sa.z * a.z + sa.w * a.w;
+    d1 += sb.x * b.x + sb.y * b.y + sb.z * b.z + sb.w * b.w;
+    d2 += sc.x * c.x + sc.y * c.y + sc.z * c.z + sc.w * c.w;
+    d3 += se.x * e.x + se.y * e.y + se.z * e.z + se.w * e.w;
+  }
+  for (; i < n; i += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(g + i);
+    const float4 sa = *reinterpret_cast<const float4*>(s + i);
+    d0 += sa.x * a.x + sa.y * a.y + sa.z * a.z + sa.w * a.w;
+  }
+  return (d0 + d1) + (d2 + d3);
+}
+
 __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
-  extern __shared__ float s_dyn[];  // [Ckv + Dr] query, then [256] probabilities
+  // [Ckv + Dr] query, [256] probabilities, [256] row indices; the wave sums
+  // [4][Ckv] reuse the space at the end.
+  extern __shared__ __attribute__((aligned(16))) float s_dyn[];
   __shared__ float s_tmp[8];
   __shared__ int s_rows_bad;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.y;
   const int row = blockIdx.x;  // (h, q) with q fastest
   const int qi = row % p.Q;
@@ -58,10 +92,11 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   const int L = clamp_len(p.seq_lens[b], p.cache.capacity);
   const int n = max(0, min(L, L - p.Q + qi + 1));
   const float scale = p.scale_log2;  // log2 domain
+  const int nvec = p.Ckv / 4;        // float4 chunks per latent row
 
-  float acc[kMaxChanPerThread];
+  float4 acc[kMaxVec];
 #pragma unroll
-  for (int k = 0; k < kMaxChanPerThread; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < kMaxVec; ++k) acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float m = -INFINITY, l = 0.0f;
   __syncthreads();
 
@@ -75,17 +110,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
       s_row[tid] = r;
       const float* cl = reinterpret_cast<const float*>(p.cache.latent + r * p.cache.latent_stride);
       const float* cr = reinterpret_cast<const float*>(p.cache.rope + r * p.cache.rope_stride);
-      float d = 0.0f;
-      for (int i = 0; i < p.Ckv; i += 4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cl + i);
-        d += s_q[i] * c4.x + s_q[i + 1] * c4.y + s_q[i + 2] * c4.z + s_q[i + 3] * c4.w;
-      }
-      for (int i = 0; i < p.Dr; i += 4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cr + i);
-        d += s_q[p.Ckv + i] * c4.x + s_q[p.Ckv + i + 1] * c4.y + s_q[p.Ckv + i + 2] * c4.z +
-             s_q[p.Ckv + i + 3] * c4.w;
-      }
-      sv = d * scale;
+      sv = (dot_row(cl, s_q, p.Ckv) + dot_row(cr, s_q + p.Ckv, p.Dr)) * scale;
     }
     const float mc = block_max(sv, s_tmp);
     const float m_new = fmaxf(m, mc);
@@ -97,27 +122,63 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
     m = m_new;
     const int cnt = min(kThreads, n - t0);
 #pragma unroll
-    for (int k = 0; k < kMaxChanPerThread; ++k) {
-      const int ch = tid + k * kThreads;
-      if (ch < p.Ckv) {
-        float a = acc[k] * alpha;
-        for (int j = 0; j < cnt; ++j) {
-          const float* cl = reinterpret_cast<const float*>(p.cache.latent + s_row[j] * p.cache.latent_stride);
-          a += s_p[j] * cl[ch];
+    for (int k = 0; k < kMaxVec; ++k) {
+      acc[k].x *= alpha;
+      acc[k].y *= alpha;
+      acc[k].z *= alpha;
+      acc[k].w *= alpha;
+    }
+    // kBatch tokens per wave at a time, so that many row reads are in flight.
+    for (int j0 = wave; j0 < cnt; j0 += kWaves * kBatch) {
+#pragma unroll
+      for (int k = 0; k < kMaxVec; ++k) {
+        if (64 * k < nvec) {  // wave-uniform
+          const int c = min(lane + 64 * k, nvec - 1);
+          float4 v[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int j = min(j0 + kWaves * u, cnt - 1);
+            v[u] = reinterpret_cast<const float4*>(p.cache.latent + s_row[j] * p.cache.latent_stride)[c];
+          }
+          if (lane + 64 * k < nvec) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const float pj = j0 + kWaves * u < cnt ? s_p[j0 + kWaves * u] : 0.0f;
+              acc[k].x += pj * v[u].x;
+              acc[k].y += pj * v[u].y;
+              acc[k].z += pj * v[u].z;
+              acc[k].w += pj * v[u].w;
+            }
+          }
         }
-        acc[k] = a;
       }
     }
     __syncthreads();
   }
+  // Sum of the four waves' partial rows (the query / probability space is no
+  // longer needed).
+  float4* s_red = reinterpret_cast<float4*>(s_dyn);
+#pragma unroll
+  for (int k = 0; k < kMaxVec; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nvec) s_red[wave * nvec + c] = acc[k];
+  }
+  __syncthreads();
   const bool bad = s_rows_bad != 0;
   const float nanv = __uint_as_float(0x7fc00000u);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  float* xo = reinterpret_cast<float*>(p.x_lat) + grow * p.Ckv;
+  float4* xo = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.x_lat) + grow * p.Ckv);
+  for (int c = tid; c < nvec; c += kThreads) {
+    float4 v = s_red[c];
 #pragma unroll
-  for (int k = 0; k < kMaxChanPerThread; ++k) {
-    const int ch = tid + k * kThreads;
-    if (ch < p.Ckv) xo[ch] = bad ? nanv : acc[k] * inv;
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 u = s_red[w * nvec + c];
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    xo[c] = bad ? make_float4(nanv, nanv, nanv, nanv) : make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
   }
   if (p.lse != nullptr && tid == 0) {
     p.lse[grow] = bad ? nanv : (l > 0.0f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY);
@@ -127,7 +188,9 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s) {
-  const size_t lds = (size_t)(p.Ckv + p.Dr + kThreads) * sizeof(float) + kThreads * sizeof(int64_t) + 16;
+  const size_t main_bytes = (size_t)(p.Ckv + p.Dr + kThreads) * sizeof(float) + kThreads * sizeof(int64_t);
+  const size_t red_bytes = (size_t)kWaves * p.Ckv * sizeof(float);
+  const size_t lds = (main_bytes > red_bytes ? main_bytes : red_bytes) + 16;
   hipLaunchKernelGGL(attn_f32_kernel, dim3(p.HQ, p.B), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }

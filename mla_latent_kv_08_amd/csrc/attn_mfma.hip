@@ -935,16 +935,18 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   const int cum_b = p.plan[b];
   const int total_tiles = p.plan[p.B];
 
+  // 16 lanes per row; lane j of a row holds channels 4j + 64k .. +3 (k < 8),
+  // so each 16-byte load of the 16 lanes covers 256 contiguous bytes.
   const int row_local = rb * 16 + (tid >> 4);
   const int row = g * kRowsPerGroup + row_local;
-  const int c0 = (tid & 15) * 32;
+  const int c0 = (tid & 15) * 4;
   if (row >= p.HQ) return;
   const int64_t grow = (int64_t)b * p.HQ + row;
   uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + grow * p.Ckv;
 
   if (nb == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint2*>(xo + c0 + 4 * k) = make_uint2(0, 0);
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint2*>(xo + c0 + 64 * k) = make_uint2(0, 0);
     if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = -INFINITY;
     return;
   }
@@ -976,7 +978,7 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
       if (!in) ls[u] = -INFINITY;
       const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) xv[u][k] = src[k];
+      for (int k = 0; k < 8; ++k) xv[u][k] = src[16 * k];
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -1019,7 +1021,7 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    *reinterpret_cast<uint2*>(xo + c0 + 4 * k) =
+    *reinterpret_cast<uint2*>(xo + c0 + 64 * k) =
         make_uint2(pack_bf16x2(acc[4 * k], acc[4 * k + 1]), pack_bf16x2(acc[4 * k + 2], acc[4 * k + 3]));
   }
   if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = lse_v;
