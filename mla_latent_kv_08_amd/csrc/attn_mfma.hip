@@ -113,6 +113,7 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) volatile int lds_vint;
+typedef __attribute__((address_space(3))) volatile float lds_vfloat;
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 // One buffer load of 16 bytes per lane straight into LDS: lane i's bytes land
@@ -129,6 +130,23 @@ __device__ __forceinline__ void lds_copy16(int32x4_t rsrc, uint32_t lds_base, in
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc)
                : "memory");
+}
+
+// One round trip for the row-max exchange: the partner's flag word, then its
+// maxima for rows l16 and 16 + l16 (64 bytes further), read in that order and
+// waited for inside the block (the results are complete when it ends). The
+// wait also covers this wave's own LDS writes issued before it.
+__device__ __forceinline__ int poll_pair(uint32_t a_flag, uint32_t a_max, float& m0, float& m1) {
+  int f;
+  asm volatile(
+      "ds_read_b32 %0, %3\n\t"
+      "ds_read_b32 %1, %4\n\t"
+      "ds_read_b32 %2, %4 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f), "=&v"(m0), "=&v"(m1)
+      : "v"(a_flag), "v"(a_max)
+      : "memory");
+  return f;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -537,7 +555,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       lds_barrier();  // step k
       const bool active = rows_on && k < count;
       floatx4 s[2];
-      float mx[2];
+      float mx[2], pmx[2];
       float sc_c = 1.0f;
       if (active) {
         if (k == 0 || sc.tile == 0) {
@@ -609,14 +627,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh) tile_max[(rb * 2 + th) * 32 + 16 * rh + l16] = mx[rh];
         }
-        // Publish this half's maxima for step k, then wait for the other
-        // half's. Both waves of the pair reach this point in every active
-        // step; the wait is bounded all the same.
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): maxima written
+        // Publish this half's maxima for step k (the maxima, then the flag),
+        // and read the other half's flag and maxima in one round trip until
+        // the flag shows step k. LDS operations of one wave complete in issue
+        // order, so maxima read after a flag showing step k are the ones
+        // written before it. Both waves of the pair reach this point in every
+        // active step; the wait is bounded all the same.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0) *(lds_vint*)(pair_flag + wave) = k + 1;
+        const uint32_t a_flag = lds_addr(reinterpret_cast<const uint8_t*>(pair_flag + (wave ^ 1)));
+        const uint32_t a_max = (uint32_t)reinterpret_cast<uintptr_t>(
+            (const __attribute__((address_space(3))) float*)(tile_max + (rb * 2 + (th ^ 1)) * 32 + l16));
         for (int spin = 0; spin < (1 << 22); ++spin) {
-          if (__builtin_amdgcn_readfirstlane(*(lds_vint*)(pair_flag + (wave ^ 1))) > k) break;
+          const int f = poll_pair(a_flag, a_max, pmx[0], pmx[1]);
+          if (__builtin_amdgcn_readfirstlane(f) > k) break;
           __builtin_amdgcn_s_sleep(1);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -632,7 +656,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         bf16x4 pk[2];
 #pragma unroll
         for (int rh = 0; rh < 2; ++rh) {
-          const float mt = fmaxf(mx[rh], tile_max[(rb * 2 + (th ^ 1)) * 32 + 16 * rh + l16]);
+          const float mt = fmaxf(mx[rh], pmx[rh]);
           upd[rh] = mt > m[rh] + kRescaleLog2;
           const float m_new = upd[rh] ? mt : m[rh];
           alpha[rh] = upd[rh] ? __builtin_amdgcn_exp2f(m[rh] - m_new) : 1.0f;
