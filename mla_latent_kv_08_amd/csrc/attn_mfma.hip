@@ -41,7 +41,8 @@
 // sequences, end to end, are dealt in equal contiguous runs to the W
 // workgroups of each row block. A run that covers a whole sequence writes x
 // and lse directly; a piece of a sequence is written as a partial (x_s
-// normalised, lse_s) and merged by the combine kernel:
+// normalised, in bf16 like x itself; lse_s in fp32) and merged by the
+// combine kernel in fp32:
 //   lse = log sum_s exp(lse_s),  x = sum_s exp(lse_s - lse) x_s.
 #include "internal.h"
 
@@ -884,30 +885,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                 *reinterpret_cast<float4*>(stage + (lane & 31) * kStageRow + 32 * cb + 8 * i4 + 4 * hi) = v;
               }
             }
-            if (whole) {
-              // 16 lanes per row, 8 channels (16 B of bf16) each.
+            // 16 lanes per row, 8 channels (16 B of bf16) each, to the x row or
+            // the partial row.
+            uint16_t* const dst0 = whole ? reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32) * 512
+                                         : p.part_x + (prow0 + rb * 32) * 512;
 #pragma unroll
-              for (int it = 0; it < 8; ++it) {
-                const int r = 4 * it + (lane >> 4);
-                const float* src = stage + r * kStageRow + 8 * (lane & 15);
-                const float4 a = *reinterpret_cast<const float4*>(src);
-                const float4 b = *reinterpret_cast<const float4*>(src + 4);
-                if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
-                  uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32 + r) * 512 + 128 * cq +
-                                 8 * (lane & 15);
-                  *reinterpret_cast<uint4*>(xo) = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                                                             pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-                }
-              }
-            } else {
-              // 32 lanes per row, 4 channels (16 B of fp32) each.
-#pragma unroll
-              for (int it = 0; it < 16; ++it) {
-                const int r = 2 * it + (lane >> 5);
-                const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageRow + 4 * (lane & 31));
-                if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
-                  *reinterpret_cast<float4*>(p.part_x + (prow0 + rb * 32 + r) * 512 + 128 * cq + 4 * (lane & 31)) = v;
-                }
+            for (int it = 0; it < 8; ++it) {
+              const int r = 4 * it + (lane >> 4);
+              const float* src = stage + r * kStageRow + 8 * (lane & 15);
+              const float4 a = *reinterpret_cast<const float4*>(src);
+              const float4 b = *reinterpret_cast<const float4*>(src + 4);
+              if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
+                *reinterpret_cast<uint4*>(dst0 + r * 512 + 128 * cq + 8 * (lane & 15)) =
+                    make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                               pack_bf16x2(b.z, b.w));
               }
             }
           } else if (row_ok) {
@@ -920,14 +911,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + e] * inv_l;
-                if (whole) {
-                  uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512;
-                  *reinterpret_cast<uint2*>(xo + c) =
-                      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                } else {
-                  *reinterpret_cast<float4*>(p.part_x + (prow0 + row_local) * 512 + c) =
-                      make_float4(v[0], v[1], v[2], v[3]);
-                }
+                uint16_t* const xo = whole ? reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512
+                                           : p.part_x + (prow0 + row_local) * 512;
+                *reinterpret_cast<uint2*>(xo + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
               }
             }
           }
@@ -959,18 +945,18 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   const int cum_b = p.plan[b];
   const int total_tiles = p.plan[p.B];
 
-  // 16 lanes per row; lane j of a row holds channels 4j + 64k .. +3 (k < 8),
+  // 16 lanes per row; lane j of a row holds channels 8j + 128k .. +7 (k < 4),
   // so each 16-byte load of the 16 lanes covers 256 contiguous bytes.
   const int row_local = rb * 16 + (tid >> 4);
   const int row = g * kRowsPerGroup + row_local;
-  const int c0 = (tid & 15) * 4;
+  const int c0 = (tid & 15) * 8;
   if (row >= p.HQ) return;
   const int64_t grow = (int64_t)b * p.HQ + row;
   uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + grow * p.Ckv;
 
   if (nb == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint2*>(xo + c0 + 64 * k) = make_uint2(0, 0);
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(xo + c0 + 128 * k) = make_uint4(0, 0, 0, 0);
     if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = -INFINITY;
     return;
   }
@@ -993,16 +979,16 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   bool any_nan = false;
   for (int i0 = i_first; i0 <= i_last; i0 += kBatch) {
     float ls[kBatch];
-    float4 xv[kBatch][8];
+    uint4 xv[kBatch][4];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool in = i0 + u <= i_last;
       const int64_t prow = prow_of(in ? i0 + u : i_first);
       ls[u] = p.part_lse[prow];
       if (!in) ls[u] = -INFINITY;
-      const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
+      const uint4* src = reinterpret_cast<const uint4*>(p.part_x + prow * 512 + c0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) xv[u][k] = src[16 * k];
+      for (int k = 0; k < 4; ++k) xv[u][k] = src[16 * k];
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -1021,11 +1007,13 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
       const float w = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
       S += w;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[4 * k + 0] += w * xv[u][k].x;
-        acc[4 * k + 1] += w * xv[u][k].y;
-        acc[4 * k + 2] += w * xv[u][k].z;
-        acc[4 * k + 3] += w * xv[u][k].w;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t wd[4] = {xv[u][k].x, xv[u][k].y, xv[u][k].z, xv[u][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[8 * k + 2 * e] += w * __uint_as_float(wd[e] << 16);
+          acc[8 * k + 2 * e + 1] += w * __uint_as_float(wd[e] & 0xffff0000u);
+        }
       }
     }
     M = Mn;
@@ -1044,9 +1032,10 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
     for (int k = 0; k < 32; ++k) acc[k] *= inv;
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    *reinterpret_cast<uint2*>(xo + c0 + 64 * k) =
-        make_uint2(pack_bf16x2(acc[4 * k], acc[4 * k + 1]), pack_bf16x2(acc[4 * k + 2], acc[4 * k + 3]));
+  for (int k = 0; k < 4; ++k) {
+    *reinterpret_cast<uint4*>(xo + c0 + 128 * k) =
+        make_uint4(pack_bf16x2(acc[8 * k], acc[8 * k + 1]), pack_bf16x2(acc[8 * k + 2], acc[8 * k + 3]),
+                   pack_bf16x2(acc[8 * k + 4], acc[8 * k + 5]), pack_bf16x2(acc[8 * k + 6], acc[8 * k + 7]));
   }
   if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = lse_v;
 }

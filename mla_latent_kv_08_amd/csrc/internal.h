@@ -27,7 +27,7 @@ struct AttnParams {
   const int32_t* seq_lens;
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
-  float* part_x;    // [G, 2W, kRowsPerGroup, Ckv] fp32 partial results
+  uint16_t* part_x;  // [G, 2W, kRowsPerGroup, Ckv] bf16 partial results
   float* part_lse;  // [G, 2W, kRowsPerGroup]
   int* plan;        // [B + 1]: run-order index of each sequence's first tile, then the total
   int B, H, Q, HQ, Ckv, Dr;

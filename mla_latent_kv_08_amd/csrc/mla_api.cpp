@@ -150,8 +150,8 @@ size_t attn_workspace_bytes(const mla_dims* d, int32_t dtype, int w) {
   const int64_t hq = (int64_t)d->heads * d->q_len;
   const int64_t groups = (hq + kRowsPerGroup - 1) / kRowsPerGroup;
   const int64_t rows = groups * 2 * w * kRowsPerGroup;
-  // partial x [rows, Ckv] fp32, partial lse [rows], run plan [B + 1] int32
-  return (size_t)(rows * d->d_latent * 4 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
+  // partial x [rows, Ckv] bf16, partial lse [rows] fp32, run plan [B + 1] int32
+  return (size_t)(rows * d->d_latent * 2 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
 }
 
 }  // namespace
@@ -265,8 +265,8 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   p.groups = (p.HQ + kRowsPerGroup - 1) / kRowsPerGroup;
   p.workgroups = w;
   const int64_t part_rows = (int64_t)p.groups * 2 * w * kRowsPerGroup;
-  p.part_x = static_cast<float*>(workspace);
-  p.part_lse = p.part_x + part_rows * p.Ckv;
+  p.part_x = static_cast<uint16_t*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(p.part_x + part_rows * p.Ckv);
   p.plan = reinterpret_cast<int*>(p.part_lse + part_rows);
   return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, s));
 }
