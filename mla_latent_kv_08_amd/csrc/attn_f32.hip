@@ -8,7 +8,7 @@
 // weighted sum over kv_cache). In the weighted sum wave w takes tokens w,
 // w + 4, ... of the chunk and lane i the 16-byte chunks i, i + 64, ... of each
 // row, so every row is one coalesced read; the four waves' sums are added at
-// the end.
+// the end. Ckv <= 2048 (the C ABI checks it).
 #include "internal.h"
 
 namespace mla {
@@ -16,8 +16,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxVec = 8;  // float4 chunks per lane: Ckv <= 2048
-constexpr int kBatch = 16;  // tokens per wave and batch of the weighted sum
 
 __device__ float block_max(float v, float* s_tmp) {
   for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
@@ -41,33 +39,33 @@ __device__ float block_sum(float v, float* s_tmp) {
   return r;
 }
 
-// Dot product of n floats (n % 4 == 0) of a global row with LDS values, four
-// partial sums so the loads and multiply-adds overlap.
+// Dot product of n floats (n % 4 == 0) of a global row with LDS values. The
+// row is read kDotBatch 16-byte loads at a time, all in flight together, into
+// four partial sums.
+constexpr int kDotBatch = 16;
 __device__ __forceinline__ float dot_row(const float* __restrict__ g, const float* s, int n) {
-  float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+  float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int i = 0;
-  for (; i + 16 <= n; i += 16) {
-    const float4 a = *reinterpret_cast<const float4*>(g + i);
-    const float4 b = *reinterpret_cast<const float4*>(g + i + 4);
-    const float4 c = *reinterpret_cast<const float4*>(g + i + 8);
-    const float4 e = *reinterpret_cast<const float4*>(g + i + 12);
-    const float4 sa = *reinterpret_cast<const float4*>(s + i);
-    const float4 sb = *reinterpret_cast<const float4*>(s + i + 4);
-    const float4 sc = *reinterpret_cast<const float4*>(s + i + 8);
-    const float4 se = *reinterpret_cast<const float4*>(s + i + 12);
-    d0 += sa.x * a.x + sa.y * a.y + sa.z * a.z + sa.w * a.w;
-    d1 += sb.x * b.x + sb.y * b.y + sb.z * b.z + sb.w * b.w;
-    d2 += sc.x * c.x + sc.y * c.y + sc.z * c.z + sc.w * c.w;
-    d3 += se.x * e.x + se.y * e.y + se.z * e.z + se.w * e.w;
+  for (; i + 4 * kDotBatch <= n; i += 4 * kDotBatch) {
+    float4 a[kDotBatch];
+#pragma unroll
+    for (int u = 0; u < kDotBatch; ++u) a[u] = *reinterpret_cast<const float4*>(g + i + 4 * u);
+#pragma unroll
+    for (int u = 0; u < kDotBatch; ++u) {
+      const float4 q = *reinterpret_cast<const float4*>(s + i + 4 * u);
+      d[u & 3] += q.x * a[u].x + q.y * a[u].y + q.z * a[u].z + q.w * a[u].w;
+    }
   }
   for (; i < n; i += 4) {
     const float4 a = *reinterpret_cast<const float4*>(g + i);
-    const float4 sa = *reinterpret_cast<const float4*>(s + i);
-    d0 += sa.x * a.x + sa.y * a.y + sa.z * a.z + sa.w * a.w;
+    const float4 q = *reinterpret_cast<const float4*>(s + i);
+    d[0] += q.x * a.x + q.y * a.y + q.z * a.z + q.w * a.w;
   }
-  return (d0 + d1) + (d2 + d3);
+  return (d[0] + d[1]) + (d[2] + d[3]);
 }
 
+// KV: 16-byte chunks of a latent row per lane (Ckv <= 256 * KV).
+template <int KV>
 __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   // [Ckv + Dr] query, [256] probabilities, [256] row indices; the wave sums
   // [4][Ckv] reuse the space at the end.
@@ -94,9 +92,9 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   const float scale = p.scale_log2;  // log2 domain
   const int nvec = p.Ckv / 4;        // float4 chunks per latent row
 
-  float4 acc[kMaxVec];
+  float4 acc[KV];
 #pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int k = 0; k < KV; ++k) acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float m = -INFINITY, l = 0.0f;
   __syncthreads();
 
@@ -122,34 +120,34 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
     m = m_new;
     const int cnt = min(kThreads, n - t0);
 #pragma unroll
-    for (int k = 0; k < kMaxVec; ++k) {
+    for (int k = 0; k < KV; ++k) {
       acc[k].x *= alpha;
       acc[k].y *= alpha;
       acc[k].z *= alpha;
       acc[k].w *= alpha;
     }
-    // kBatch tokens per wave at a time, so that many row reads are in flight.
-    for (int j0 = wave; j0 < cnt; j0 += kWaves * kBatch) {
+    // NB tokens per wave at a time, every chunk of their rows requested
+    // together.
+    constexpr int NB = 32 / KV;
+    for (int j0 = wave; j0 < cnt; j0 += kWaves * NB) {
+      float4 v[NB][KV];
 #pragma unroll
-      for (int k = 0; k < kMaxVec; ++k) {
-        if (64 * k < nvec) {  // wave-uniform
-          const int c = min(lane + 64 * k, nvec - 1);
-          float4 v[kBatch];
+      for (int u = 0; u < NB; ++u) {
+        const float4* row = reinterpret_cast<const float4*>(p.cache.latent +
+                                                            s_row[min(j0 + kWaves * u, cnt - 1)] *
+                                                                p.cache.latent_stride);
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            const int j = min(j0 + kWaves * u, cnt - 1);
-            v[u] = reinterpret_cast<const float4*>(p.cache.latent + s_row[j] * p.cache.latent_stride)[c];
-          }
-          if (lane + 64 * k < nvec) {
+        for (int k = 0; k < KV; ++k) v[u][k] = row[min(lane + 64 * k, nvec - 1)];
+      }
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-              const float pj = j0 + kWaves * u < cnt ? s_p[j0 + kWaves * u] : 0.0f;
-              acc[k].x += pj * v[u].x;
-              acc[k].y += pj * v[u].y;
-              acc[k].z += pj * v[u].z;
-              acc[k].w += pj * v[u].w;
-            }
-          }
+      for (int u = 0; u < NB; ++u) {
+        const float pj = j0 + kWaves * u < cnt ? s_p[j0 + kWaves * u] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+          acc[k].x += pj * v[u][k].x;
+          acc[k].y += pj * v[u][k].y;
+          acc[k].z += pj * v[u][k].z;
+          acc[k].w += pj * v[u][k].w;
         }
       }
     }
@@ -159,7 +157,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   // longer needed).
   float4* s_red = reinterpret_cast<float4*>(s_dyn);
 #pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) {
+  for (int k = 0; k < KV; ++k) {
     const int c = lane + 64 * k;
     if (c < nvec) s_red[wave * nvec + c] = acc[k];
   }
@@ -191,7 +189,16 @@ hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s) {
   const size_t main_bytes = (size_t)(p.Ckv + p.Dr + kThreads) * sizeof(float) + kThreads * sizeof(int64_t);
   const size_t red_bytes = (size_t)kWaves * p.Ckv * sizeof(float);
   const size_t lds = (main_bytes > red_bytes ? main_bytes : red_bytes) + 16;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(p.HQ, p.B), dim3(kThreads), lds, s, p);
+  const dim3 grid(p.HQ, p.B);
+  if (p.Ckv <= 256) {
+    hipLaunchKernelGGL(attn_f32_kernel<1>, grid, dim3(kThreads), lds, s, p);
+  } else if (p.Ckv <= 512) {
+    hipLaunchKernelGGL(attn_f32_kernel<2>, grid, dim3(kThreads), lds, s, p);
+  } else if (p.Ckv <= 1024) {
+    hipLaunchKernelGGL(attn_f32_kernel<4>, grid, dim3(kThreads), lds, s, p);
+  } else {
+    hipLaunchKernelGGL(attn_f32_kernel<8>, grid, dim3(kThreads), lds, s, p);
+  }
   return hipGetLastError();
 }
 
