@@ -346,6 +346,17 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// Value of an E4M3 ("FN") scale byte, without branches (lanes hold different
+// scales): subnormal m * 2^-9, normal (1 + m/8) * 2^(e-7), NaN for e=15, m=7.
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 0xfu, m = byte & 7u;
+  const float sub = (float)m * 0.001953125f;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  float v = e == 0u ? sub : nrm;
+  v = (e == 15u && m == 7u) ? __uint_as_float(0x7fc00000u) : v;
+  return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
+}
+
 // Decode P.V wave d's 8 tokens of a raw tile into the bf16 tile (latent rows
 // with the chunk swizzle, RoPE groups). Lane i: code chunks u = i and i + 64
 // (token u / 16, 32 channels at 32 * (u % 16)) and RoPE chunk i.
@@ -357,8 +368,8 @@ __device__ __forceinline__ void fp4_decode(const uint8_t* raw, uint8_t* dst, int
     const int j = u & 15;
     const uint4 cw = *reinterpret_cast<const uint4*>(raw + 8 * d * 256 + u * 16);
     const uint32_t sc = *reinterpret_cast<const uint16_t*>(raw + kRawScaleBase + 8 * d * 32 + 2 * u);
-    const float s0 = e4m3_to_f32(sc & 0xffu);
-    const float s1 = e4m3_to_f32(sc >> 8);
+    const float s0 = e4m3_value(sc & 0xffu);
+    const float s1 = e4m3_value(sc >> 8);
     const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
@@ -812,8 +823,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         // Decode tile k+1 into the buffer tile k-2 left at the end of step
         // k-1, then refill its raw slot with tile k+4.
         if (k + 1 < count) {
+          // The decode bounds the FP4 step, so it issues ahead of the score
+          // wave on the same SIMD.
+          __builtin_amdgcn_s_setprio(3);
           fp4_decode(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
                      smem + ((k + 1) % kRing) * kTileBytes, cq, lane);
+          __builtin_amdgcn_s_setprio(0);
           if (issued < count) issue();
         }
       } else if (issued < count) {
