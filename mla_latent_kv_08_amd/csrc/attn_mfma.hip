@@ -357,12 +357,12 @@ __device__ __forceinline__ float e4m3_value(uint32_t byte) {
   return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
 }
 
-// Decode P.V wave d's 8 tokens of a raw tile into the bf16 tile (latent rows
-// with the chunk swizzle, RoPE groups). Lane i: code chunks u = i and i + 64
-// (token u / 16, 32 channels at 32 * (u % 16)) and RoPE chunk i.
-__device__ __forceinline__ void fp4_decode(const uint8_t* raw, uint8_t* dst, int d, int lane) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+// Decode part h (tokens 8d + 4h .. +3) of P.V wave d's 8 tokens of a raw
+// tile into the bf16 tile (latent rows with the chunk swizzle, RoPE groups).
+// Lane i: code chunk u = i + 64h (token u / 16, 32 channels at 32 * (u % 16));
+// lanes 0..31 also move RoPE chunk 32h + i.
+__device__ __forceinline__ void fp4_decode_part(const uint8_t* raw, uint8_t* dst, int d, int lane, int h) {
+  {
     const int u = lane + 64 * h;
     const int t = 8 * d + (u >> 4);
     const int j = u & 15;
@@ -380,9 +380,12 @@ __device__ __forceinline__ void fp4_decode(const uint8_t* raw, uint8_t* dst, int
                      fp4_pair<3>(words[qd], sv));
     }
   }
-  const int t = 8 * d + (lane >> 3), ch = lane & 7;
-  *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
-      *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + lane * 16);
+  if (lane < 32) {
+    const int c = lane + 32 * h;
+    const int t = 8 * d + (c >> 3), ch = c & 7;
+    *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
+        *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + c * 16);
+  }
 }
 
 // Lane-wise combination across lane groups: lanes l and l ^ 32 (or l ^ 16)
@@ -707,6 +710,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         const bool any_upd = __any(upd[0] || upd[1]);
         if (th == 0 && lane == 0) mt->rescale[rb] = any_upd ? 1 : 0;
       }
+      if constexpr (kFp4) {
+        // Second half of P.V wave `wave`'s tokens of tile k+1 (its raw bytes
+        // landed before this step's barrier).
+        if (k + 1 < count) {
+          fp4_decode_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
+                          smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
+        }
+      }
       if (k < count) sc.next(p);
     }
   } else {
@@ -753,8 +764,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     };
     // Prologue. bf16: tiles 0 and 1 on their way into buffers 0 and 1, beside
     // the staged query rows. FP4: raw tiles 0..2 on their way; tile 0 decoded
-    // into buffer 0 (this wave's tokens, from its own copies), then tile 3
-    // started in the slot tile 0 left.
+    // into buffer 0 (this wave's tokens, from its own copies).
     issue();
     if (issued < count) issue();
     if constexpr (kFp4) {
@@ -766,8 +776,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
-      fp4_decode(smem + L::kRawBase, smem, cq, lane);
-      if (issued < count) issue();
+      fp4_decode_part(smem + L::kRawBase, smem, cq, lane, 0);
+      fp4_decode_part(smem + L::kRawBase, smem, cq, lane, 1);
     }
     lds_barrier();  // query rows staged
 
@@ -804,8 +814,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           }
         }
       } else {
-        // Raw tile k+1 has landed (tiles k+2, k+3 may still be in flight
-        // unless output stores were issued after them).
+        // Raw tile k+1 has landed (tile k+2 may still be in flight unless
+        // output stores were issued after it).
         if (k + 1 < count) {
           const int ahead = stored ? 0 : issued - (k + 2);
           if (ahead >= 2) {
@@ -820,16 +830,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       stored = false;
       lds_barrier();  // step k
       if constexpr (kFp4) {
-        // Decode tile k+1 into the buffer tile k-2 left at the end of step
-        // k-1, then refill its raw slot with tile k+4.
+        // Raw tile k+3 goes to the slot tile k left (decoded in step k-1);
+        // then the first half of this wave's tokens of tile k+1 is decoded
+        // into the buffer tile k-2 left (the score wave of the same index
+        // decodes the other half at the end of its step).
+        if (issued < count) issue();
         if (k + 1 < count) {
           // The decode bounds the FP4 step, so it issues ahead of the score
           // wave on the same SIMD.
           __builtin_amdgcn_s_setprio(3);
-          fp4_decode(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
-                     smem + ((k + 1) % kRing) * kTileBytes, cq, lane);
+          fp4_decode_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
+                          smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
           __builtin_amdgcn_s_setprio(0);
-          if (issued < count) issue();
         }
       } else if (issued < count) {
         // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
