@@ -91,6 +91,17 @@ def test_mtp_fp4_reduced():
     T.compare(g.run(), T.oracle(inp), w)
 
 
+# The FP4 tile pipeline keeps three raw tiles in flight and splits each tile's
+# decode between two waves; runs of 1, 2, 3 and more tiles, and runs that
+# cross sequence boundaries, all pass through its prologue and refill paths.
+@pytest.mark.parametrize("workgroups", [1, 3, 40, 200])
+def test_mtp_fp4_split_counts(workgroups):
+    w = W.reduced(W.WORKLOADS["mtp_fp4"], 4, [700, 33, 1, 260])
+    inp, g = _case(w)
+    T.say(f"  workgroups={workgroups}")
+    T.compare(g.run(workgroups), T.oracle(inp), w)
+
+
 def test_mtp_fp4_paged_reduced():
     w = W.reduced(W.WORKLOADS["mtp_fp4"], 3, [200, 65, 64]).with_(paged=True)
     inp, g = _case(w)
