@@ -570,7 +570,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       lds_barrier();  // step k
       const bool active = rows_on && k < count;
       floatx4 s[2];
-      float mx[2], pmx[2];
+      float mx[2], pmx[2], esp[2][4];
       float sc_c = 1.0f;
       if (active) {
         if (k == 0 || sc.tile == 0) {
@@ -650,13 +650,36 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         // active step; the wait is bounded all the same.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0) *(lds_vint*)(pair_flag + wave) = k + 1;
-        const uint32_t a_flag = lds_addr(reinterpret_cast<const uint8_t*>(pair_flag + (wave ^ 1)));
-        const uint32_t a_max = (uint32_t)reinterpret_cast<uintptr_t>(
-            (const __attribute__((address_space(3))) float*)(tile_max + (rb * 2 + (th ^ 1)) * 32 + l16));
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-          const int f = poll_pair(a_flag, a_max, pmx[0], pmx[1]);
-          if (__builtin_amdgcn_readfirstlane(f) > k) break;
-          __builtin_amdgcn_s_sleep(1);
+        // First look: plain reads, whose latency the exponentials below cover;
+        // later looks (the partner not there yet) poll in one round trip each.
+        const float* const pmax = tile_max + (rb * 2 + (th ^ 1)) * 32 + l16;
+        int f0 = *(lds_vint*)(pair_flag + (wave ^ 1));
+        pmx[0] = *(lds_vfloat*)(pmax);
+        pmx[1] = *(lds_vfloat*)(pmax + 16);
+        if constexpr (kFp4) {
+          // FP4 (where the score chain bounds the step): exponentials against
+          // the current reference max while the reads are in flight. They
+          // stand unless the pair's tile max moves the reference (a row's
+          // first tile, a large jump), which is rare.
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) {
+            const float mu = m[rh] == -INFINITY ? 0.0f : m[rh];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -mu));
+          }
+          // (Keeps the exponentials ahead of the first use of the flag.)
+          asm volatile("" ::"v"(esp[0][0]), "v"(esp[0][1]), "v"(esp[0][2]), "v"(esp[0][3]), "v"(esp[1][0]),
+                       "v"(esp[1][1]), "v"(esp[1][2]), "v"(esp[1][3]));
+        }
+        if (__builtin_amdgcn_readfirstlane(f0) <= k) {
+          const uint32_t a_flag = lds_addr(reinterpret_cast<const uint8_t*>(pair_flag + (wave ^ 1)));
+          const uint32_t a_max = (uint32_t)reinterpret_cast<uintptr_t>(
+              (const __attribute__((address_space(3))) float*)(pmax));
+          for (int spin = 0; spin < (1 << 22); ++spin) {
+            __builtin_amdgcn_s_sleep(1);
+            const int f = poll_pair(a_flag, a_max, pmx[0], pmx[1]);
+            if (__builtin_amdgcn_readfirstlane(f) > k) break;
+          }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
       }
@@ -676,11 +699,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           const float m_new = upd[rh] ? mt : m[rh];
           alpha[rh] = upd[rh] ? __builtin_amdgcn_exp2f(m[rh] - m_new) : 1.0f;
           m[rh] = m_new;
-          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        }
+        if (!kFp4 || __any(upd[0] || upd[1])) {
+          // bf16: the exponentials; FP4: again for the rows whose reference
+          // moved.
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) {
+            if (!kFp4 || upd[rh]) {
+              const float m_use = m[rh] == -INFINITY ? 0.0f : m[rh];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
+            }
+          }
+        }
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
           float rs = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
+            const float e = esp[rh][i];
             rs += e;
             pk[rh][i] = (__bf16)e;
           }
