@@ -335,14 +335,14 @@ __device__ __forceinline__ void fp4_copy_pieces(const Fp4Copy& f, const uint8_t*
 
 // Two codes (byte e of w) times scale s as two bf16. The hardware conversion
 // takes only the exponent of its scale, so it runs at scale 1 (exact E2M1
-// values) and the E4M3 scale is applied in fp32; every product of an E2M1
-// value and an E4M3 scale fits in bf16, so taking the high halves is exact.
+// values, straight to fp32) and the E4M3 scale is applied in fp32; every
+// product of an E2M1 value and an E4M3 scale fits in bf16, so taking the high
+// halves is exact.
 template <int e>
 __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
-  const auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, e);
-  const uint32_t u = __builtin_bit_cast(uint32_t, r);
-  const float lo = __uint_as_float(u << 16) * s;
-  const float hi = __uint_as_float(u & 0xffff0000u) * s;
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, e);
+  const float lo = r[0] * s;
+  const float hi = r[1] * s;
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
