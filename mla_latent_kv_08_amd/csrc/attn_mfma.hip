@@ -826,17 +826,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     floatx16 o[8];        // [rb * 4 + cb]
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = floatx16{};
-    // P.V of 16 tokens (k-step kk) of tile kt.
+    // P.V of 16 tokens (k-step kk) of tile kt. All V fragments of the half
+    // are requested before its first matrix op, so the reads overlap each
+    // other instead of one LDS round trip per channel block.
     auto pv_half = [&](int kt, int kk) {
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
+      bf16x8 a[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
       const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
       const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 a = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, o[cb], 0, 0, 0);
-        o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, o[4 + cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb], p0, o[cb], 0, 0, 0);
+        o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb], p1, o[4 + cb], 0, 0, 0);
       }
     };
     for (int k = 0; k <= count; ++k) {
