@@ -121,9 +121,11 @@ typedef struct mla_kv_cache {
 
 /* Optional tuning of mla_decode_attn; pass NULL for the library's choice. */
 typedef struct mla_decode_opts {
-  /* Workgroups that share the token axis of one block of 64 query rows.
-   * 0 = chosen from the compute-unit count. The tokens of all sequences are
-   * dealt to them in equal contiguous runs of 64-token tiles. */
+  /* bf16 / FP4: workgroups that share the token axis of one block of 64
+   * query rows; the tokens of all sequences are dealt to them in equal
+   * contiguous runs of 32-token tiles. fp32: token splits per query row (at
+   * most 64), merged by log-sum-exp. 0 = chosen from the compute-unit count
+   * (bf16 / FP4) or from the batch and max_seq_len (fp32). */
   int32_t workgroups;
   int32_t reserved[3];
 } mla_decode_opts;

@@ -1,6 +1,9 @@
 // fp32 absorbed MLA decode attention (vector ALU, any latent / RoPE width).
 //
-// One workgroup per query row (b, h, q). Tokens are visited in chunks of 256:
+// One workgroup per query row (b, h, q) and token split (the visible tokens
+// are cut into S ranges of split_tokens; with S = 1 the workgroup writes x
+// and lse itself, otherwise a partial that attn_f32_merge_kernel combines by
+// log-sum-exp). Tokens are visited in chunks of 256:
 // each thread scores one token (dot product of [q_lat | q_pe] with the
 // token's [latent | rope] row, scaled), the chunk's maximum and sum update the
 // running softmax state, and the probability-weighted latent rows are summed
@@ -64,8 +67,39 @@ __device__ __forceinline__ float dot_row(const float* __restrict__ g, const floa
   return (d[0] + d[1]) + (d[2] + d[3]);
 }
 
-// KV: 16-byte chunks of a latent row per lane (Ckv <= 256 * KV).
-template <int KV>
+// Score of one token by a 16-lane group: lane j takes the 16-byte chunks
+// j, j + 16, ... of the token's [latent | rope] row, all requested together in
+// batches of kGroupBatch, and the group adds its partial sums by shuffles.
+constexpr int kGroupBatch = 9;
+__device__ __forceinline__ float dot_row_group(const float* __restrict__ cl, const float* __restrict__ cr,
+                                               const float* s_q, int nl, int nr, int j) {
+  float d = 0.0f;
+  for (int c0 = 0; c0 < nl + nr; c0 += 16 * kGroupBatch) {
+    float4 a[kGroupBatch];
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int c = c0 + j + 16 * u;
+      a[u] = c < nl ? reinterpret_cast<const float4*>(cl)[c]
+                    : (c < nl + nr ? reinterpret_cast<const float4*>(cr)[c - nl] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int c = c0 + j + 16 * u;
+      if (c < nl + nr) {
+        const float4 q = reinterpret_cast<const float4*>(s_q)[c];
+        d += q.x * a[u].x + q.y * a[u].y + q.z * a[u].z + q.w * a[u].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) d += __shfl_xor(d, m, 16);
+  return d;
+}
+
+// KV: 16-byte chunks of a latent row per lane (Ckv <= 256 * KV). kG16: splits
+// of at most 16 tokens, scored by 16-lane groups (one token each) instead of
+// one thread per token, so a token's row arrives in one round trip.
+template <int KV, bool kG16>
 __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   // [Ckv + Dr] query, [256] probabilities, [256] row indices; the wave sums
   // [4][Ckv] reuse the space at the end.
@@ -96,29 +130,42 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < KV; ++k) acc[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float m = -INFINITY, l = 0.0f;
+  const int split = blockIdx.z;
+  const int t_lo = split * p.split_tokens;
+  // (The last split runs to the row's end, whatever max_seq_len said.)
+  const int t_hi = split == (int)gridDim.z - 1 ? n : min(n, t_lo + p.split_tokens);
   __syncthreads();
 
-  for (int t0 = 0; t0 < n; t0 += kThreads) {
-    const int t = t0 + tid;
+  constexpr int kChunk = kG16 ? 16 : kThreads;  // tokens per pass
+  for (int t0 = t_lo; t0 < t_hi; t0 += kChunk) {
+    // slot: this thread's token of the pass; `mine`: the one thread that
+    // counts it in the block sum.
+    const int slot = kG16 ? tid >> 4 : tid;
+    const int t = t0 + slot;
+    const bool mine = t < t_hi && (!kG16 || (tid & 15) == 0);
     float sv = -INFINITY;
-    if (t < n) {
+    if (t < t_hi) {  // uniform within a 16-lane group
       bool bad = false;
       const int64_t r = phys_row(p.cache, b, t, bad);
-      if (bad) s_rows_bad = 1;
-      s_row[tid] = r;
+      if (bad && mine) s_rows_bad = 1;
+      if (mine) s_row[slot] = r;
       const float* cl = reinterpret_cast<const float*>(p.cache.latent + r * p.cache.latent_stride);
       const float* cr = reinterpret_cast<const float*>(p.cache.rope + r * p.cache.rope_stride);
-      sv = (dot_row(cl, s_q, p.Ckv) + dot_row(cr, s_q + p.Ckv, p.Dr)) * scale;
+      if constexpr (kG16) {
+        sv = dot_row_group(cl, cr, s_q, p.Ckv / 4, p.Dr / 4, tid & 15) * scale;
+      } else {
+        sv = (dot_row(cl, s_q, p.Ckv) + dot_row(cr, s_q + p.Ckv, p.Dr)) * scale;
+      }
     }
     const float mc = block_max(sv, s_tmp);
     const float m_new = fmaxf(m, mc);
     const float alpha = exp2f(m - m_new);
-    const float e = t < n ? exp2f(sv - m_new) : 0.0f;
-    s_p[tid] = e;
+    const float e = mine ? exp2f(sv - m_new) : 0.0f;
+    if (mine) s_p[slot] = e;
     const float lc = block_sum(e, s_tmp);  // includes a barrier after s_p/s_row writes
     l = l * alpha + lc;
     m = m_new;
-    const int cnt = min(kThreads, n - t0);
+    const int cnt = min(kChunk, t_hi - t0);
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
       acc[k].x *= alpha;
@@ -165,7 +212,10 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   const bool bad = s_rows_bad != 0;
   const float nanv = __uint_as_float(0x7fc00000u);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  float4* xo = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.x_lat) + grow * p.Ckv);
+  const bool whole = gridDim.z == 1;
+  const int64_t prow = grow * gridDim.z + split;
+  float4* xo = reinterpret_cast<float4*>(whole ? reinterpret_cast<float*>(p.x_lat) + grow * p.Ckv
+                                               : p.part_xf + prow * p.Ckv);
   for (int c = tid; c < nvec; c += kThreads) {
     float4 v = s_red[c];
 #pragma unroll
@@ -178,8 +228,54 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
     }
     xo[c] = bad ? make_float4(nanv, nanv, nanv, nanv) : make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
   }
+  if (tid == 0) {
+    const float lse2 = bad ? nanv : (l > 0.0f ? m + log2f(l) : -INFINITY);
+    if (!whole) {
+      p.part_lse[prow] = lse2;
+    } else if (p.lse != nullptr) {
+      p.lse[grow] = lse2 * 0.69314718055994530942f;
+    }
+  }
+}
+
+// Merge of the S token splits of each query row: with lse_s in the log2
+// domain, M = max_s lse_s, w_s = 2^(lse_s - M),
+//   x = sum_s w_s x_s / sum_s w_s,  lse = (M + log2 sum_s w_s) ln 2.
+// Splits without visible tokens have lse_s = -inf and weight 0; a NaN lse_s
+// (a page index outside the cache) makes the row NaN.
+__global__ void __launch_bounds__(kThreads) attn_f32_merge_kernel(AttnParams p) {
+  const int tid = threadIdx.x;
+  const int S = p.workgroups;
+  const int64_t grow = (int64_t)blockIdx.y * p.HQ + blockIdx.x;
+  const float* ls = p.part_lse + grow * S;
+  float M = -INFINITY;
+  bool any_nan = false;
+  for (int s = 0; s < S; ++s) {
+    const float v = ls[s];
+    any_nan |= v != v;
+    M = fmaxf(M, v);
+  }
+  float sw = 0.0f;
+  for (int s = 0; s < S; ++s) sw += ls[s] == -INFINITY ? 0.0f : exp2f(ls[s] - M);
+  const float nanv = __uint_as_float(0x7fc00000u);
+  const float inv = sw > 0.0f ? 1.0f / sw : 0.0f;
+  const int nvec = p.Ckv / 4;
+  float4* xo = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.x_lat) + grow * p.Ckv);
+  for (int c = tid; c < nvec; c += kThreads) {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s = 0; s < S; ++s) {
+      const float w = ls[s] == -INFINITY ? 0.0f : exp2f(ls[s] - M);
+      const float4 v = reinterpret_cast<const float4*>(p.part_xf + (grow * S + s) * p.Ckv)[c];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+    xo[c] = any_nan ? make_float4(nanv, nanv, nanv, nanv)
+                    : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
   if (p.lse != nullptr && tid == 0) {
-    p.lse[grow] = bad ? nanv : (l > 0.0f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY);
+    p.lse[grow] = any_nan ? nanv : (sw > 0.0f ? (M + log2f(sw)) * 0.69314718055994530942f : -INFINITY);
   }
 }
 
@@ -189,16 +285,24 @@ hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s) {
   const size_t main_bytes = (size_t)(p.Ckv + p.Dr + kThreads) * sizeof(float) + kThreads * sizeof(int64_t);
   const size_t red_bytes = (size_t)kWaves * p.Ckv * sizeof(float);
   const size_t lds = (main_bytes > red_bytes ? main_bytes : red_bytes) + 16;
-  const dim3 grid(p.HQ, p.B);
+  const dim3 grid(p.HQ, p.B, p.workgroups);
+  const bool g16 = p.split_tokens <= 16;
   if (p.Ckv <= 256) {
-    hipLaunchKernelGGL(attn_f32_kernel<1>, grid, dim3(kThreads), lds, s, p);
+    if (g16) hipLaunchKernelGGL((attn_f32_kernel<1, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((attn_f32_kernel<1, false>), grid, dim3(kThreads), lds, s, p);
   } else if (p.Ckv <= 512) {
-    hipLaunchKernelGGL(attn_f32_kernel<2>, grid, dim3(kThreads), lds, s, p);
+    if (g16) hipLaunchKernelGGL((attn_f32_kernel<2, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((attn_f32_kernel<2, false>), grid, dim3(kThreads), lds, s, p);
   } else if (p.Ckv <= 1024) {
-    hipLaunchKernelGGL(attn_f32_kernel<4>, grid, dim3(kThreads), lds, s, p);
+    if (g16) hipLaunchKernelGGL((attn_f32_kernel<4, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((attn_f32_kernel<4, false>), grid, dim3(kThreads), lds, s, p);
   } else {
-    hipLaunchKernelGGL(attn_f32_kernel<8>, grid, dim3(kThreads), lds, s, p);
+    if (g16) hipLaunchKernelGGL((attn_f32_kernel<8, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((attn_f32_kernel<8, false>), grid, dim3(kThreads), lds, s, p);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.workgroups == 1) return e;
+  hipLaunchKernelGGL(attn_f32_merge_kernel, dim3(p.HQ, p.B), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

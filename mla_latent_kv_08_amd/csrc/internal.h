@@ -28,11 +28,13 @@ struct AttnParams {
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
   uint16_t* part_x;  // [G, 2W, kRowsPerGroup, Ckv] bf16 partial results
-  float* part_lse;  // [G, 2W, kRowsPerGroup]
+  float* part_lse;  // [G, 2W, kRowsPerGroup] (fp32 path: [B, HQ, S] in the log2 domain)
+  float* part_xf;   // fp32 path with S > 1 token splits: [B, HQ, S, Ckv] partial results
+  int split_tokens;  // fp32 path: tokens per split
   int* plan;        // [B + 1]: run-order index of each sequence's first tile, then the total
   int B, H, Q, HQ, Ckv, Dr;
   int groups;      // G = ceil(HQ / kRowsPerGroup)
-  int workgroups;  // W per row group
+  int workgroups;  // W per row group (fp32 path: S token splits)
   float scale_log2;  // softmax_scale * log2(e)
 };
 

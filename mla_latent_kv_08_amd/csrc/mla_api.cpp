@@ -145,6 +145,25 @@ int check_attn(const mla_dims* dims, int32_t dtype, const mla_kv_cache* cache, i
   return MLA_OK;
 }
 
+// Token splits of the fp32 path: enough (query row, split) workgroups to
+// spread the cache reads over the GPU for small batches, at least 16 tokens
+// per split, at most 64 splits; opts->workgroups sets the count directly.
+constexpr int kF32MaxSplits = 64;
+int f32_splits(const mla_dims* d, int32_t max_seq_len, const mla_decode_opts* opts) {
+  if (opts != nullptr && opts->workgroups > 0) return std::min<int>(opts->workgroups, kF32MaxSplits);
+  const int64_t rows = std::max<int64_t>(1, (int64_t)d->batch * d->heads * d->q_len);
+  const int64_t by_len = (std::max(max_seq_len, 1) + 15) / 16;
+  const int64_t by_rows = (512 + rows - 1) / rows;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({by_len, by_rows, (int64_t)kF32MaxSplits}));
+}
+
+size_t f32_workspace_bytes(const mla_dims* d, int splits) {
+  if (splits <= 1) return 0;
+  const int64_t rows = (int64_t)d->batch * d->heads * d->q_len * splits;
+  // partial x [B, HQ, S, Ckv] fp32, partial lse [B, HQ, S] fp32
+  return (size_t)(rows * d->d_latent * 4 + rows * 4 + 256);
+}
+
 size_t attn_workspace_bytes(const mla_dims* d, int32_t dtype, int w) {
   if (dtype != MLA_BF16) return 0;
   const int64_t hq = (int64_t)d->heads * d->q_len;
@@ -211,7 +230,7 @@ MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32
   int st = check_attn(dims, dtype, nullptr, max_seq_len, opts);
   if (st) return st;
   if (dtype != MLA_BF16) {
-    *bytes = 0;
+    *bytes = f32_workspace_bytes(dims, f32_splits(dims, max_seq_len, opts));
     return MLA_OK;
   }
   int cus = 0;
@@ -252,8 +271,19 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MLA_F32) {
+    const int splits = f32_splits(dims, max_seq_len, opts);
+    const size_t need = f32_workspace_bytes(dims, splits);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) {
+      return MLA_ERR_WORKSPACE;
+    }
     p.groups = 1;
-    p.workgroups = 1;
+    p.workgroups = splits;
+    p.split_tokens = (std::max(max_seq_len, 1) + splits - 1) / splits;
+    if (splits > 1) {
+      const int64_t rows = (int64_t)p.B * p.HQ * splits;
+      p.part_xf = static_cast<float*>(workspace);
+      p.part_lse = p.part_xf + rows * p.Ckv;
+    }
     return hip_status(mla::launch_attn_f32(p, s));
   }
   int cus = 0;

@@ -32,6 +32,16 @@ def test_tiny_f32_ragged_causal_paged():
     T.compare(g.run(), T.oracle(inp), w)
 
 
+# The fp32 path cuts each row's tokens into splits merged by log-sum-exp;
+# 1 split writes x directly, many leave empty splits, and 64 is the cap.
+@pytest.mark.parametrize("workgroups", [1, 2, 5, 64, 100])
+def test_f32_split_counts(workgroups):
+    w = W.reduced(W.WORKLOADS["tiny_f32"], 3, [300, 1, 77]).with_(Q=2)
+    inp, g = _case(w)
+    T.say(f"  workgroups={workgroups}")
+    T.compare(g.run(workgroups), T.oracle(inp), w)
+
+
 def test_f32_other_dims():
     # The fp32 path is generic in its widths: the exercise page's demo sizes.
     w = W.Workload("demo", B=2, H=8, Q=1, Dn=64, Dr=32, Vd=128, Ckv=512, dtype="f32", seed=5, lk=10)
