@@ -6,9 +6,10 @@ accumulation: B=32 sequences, H=128 heads, Q=1 new token, Dn=128, Dr=64,
 Vd=128, Ckv=512, 4096 cached tokens per sequence in a contiguous
 [B, Lk, 512+64] cache; seeded synthetic inputs (seed 1).
 
-One step = the whole path: mla_cache_append (the new token's row),
-mla_absorb_q, mla_decode_attn (token-split attention + log-sum-exp merge) and
-mla_up_proj_v. Inputs are resident in HBM before timing starts; every step
+One step = the whole path: the cache append of the new token's row and the
+query absorption (mla_append_absorb: mla_cache_append and mla_absorb_q in one
+launch; --separate-append calls the two), mla_decode_attn (token-split
+attention + log-sum-exp merge) and mla_up_proj_v. Inputs are resident in HBM before timing starts; every step
 reads a different one of several cache copies so that the 256 MB Infinity
 Cache cannot serve the 151 MB cache from the previous step.
 
@@ -312,6 +313,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step (and the timed attention calls) from captured HIP "
                          "graphs instead of launching the calls one by one")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="call mla_cache_append and mla_absorb_q separately instead of mla_append_absorb")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (ragged paged, long context, FP4 MTP, tiny fp32) "
                          "and the context figures (copy rate, clocks)")
@@ -376,9 +379,15 @@ def main():
         ops.mla_decode_attn(q_lat, q_pe, caches[c], seq_lens, max_len, w.softmax_scale, x, lse,
                             workspace=workspace, workgroups=args.workgroups, stream=st)
 
+    def append_absorb(c, st):
+        if args.separate_append:
+            ops.mla_cache_append(c_new, r_new, caches[c], seq_lens, stream=st)
+            ops.mla_absorb_q(q_nope, wkv_b, q_lat, stream=st)
+        else:
+            ops.mla_append_absorb(c_new, r_new, caches[c], seq_lens, q_nope, wkv_b, q_lat, stream=st)
+
     def step_calls(c, st):
-        ops.mla_cache_append(c_new, r_new, caches[c], seq_lens, stream=st)
-        ops.mla_absorb_q(q_nope, wkv_b, q_lat, stream=st)
+        append_absorb(c, st)
         attend(c, st)
         ops.mla_up_proj_v(x, wkv_b, out, stream=st)
 
@@ -422,22 +431,20 @@ def main():
 
     # Each call's share of a step: a second eager pass with an event between
     # consecutive calls (so each call sees the cache state of a real step).
-    names = ("append", "absorb", "attn", "up_proj")
+    names = ("append_absorb", "attn", "up_proj")
     in_step = {k: 0.0 for k in names}
     if not args.graph:
         evs = []
         for i in range(args.steps):
             c = i % ncopy
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-            ops.mla_cache_append(c_new, r_new, caches[c], seq_lens, stream=stream)
+            append_absorb(c, stream)
             e[1].record(stream)
-            ops.mla_absorb_q(q_nope, wkv_b, q_lat, stream=stream)
-            e[2].record(stream)
             attend(c, stream)
-            e[3].record(stream)
+            e[2].record(stream)
             ops.mla_up_proj_v(x, wkv_b, out, stream=stream)
-            e[4].record(stream)
+            e[3].record(stream)
             evs.append(e)
         torch.cuda.synchronize()
         for e in evs:
@@ -486,9 +493,8 @@ def main():
     # The projections against their own weight-bandwidth roofline (bf16 weights
     # read once, activations in and out once).
     wt = H * w.Dn * w.Ckv * 2
-    proj_bytes = {"absorb": wt + B * H * Q * (w.Dn + w.Ckv) * 2,
-                  "up_proj": H * w.Vd * w.Ckv * 2 + B * H * Q * (w.Ckv + w.Vd) * 2,
-                  "append": 2 * B * Q * (w.Ckv + w.Dr) * 2}
+    proj_bytes = {"append_absorb": wt + B * H * Q * (w.Dn + w.Ckv) * 2 + 2 * B * Q * (w.Ckv + w.Dr) * 2,
+                  "up_proj": H * w.Vd * w.Ckv * 2 + B * H * Q * (w.Ckv + w.Vd) * 2}
     attn_s = attn_avg_ms / 1e3
     achieved_gbps = bytes_alg / attn_s / 1e9
     tflops = flops / attn_s / 1e12
@@ -523,7 +529,10 @@ def main():
         "config": {"workload": "DeepSeek-V3-shaped MLA decode, one layer: B=32, H=128, Q=1, Dn=128, "
                                "Dr=64, Vd=128, Ckv=512, Lk=4096, contiguous [B,Lk,576] bf16 cache",
                    "global_batch": B, "seq_len": max_len, "parallelism": "none (1 GPU)",
-                   "cache_copies": len(caches), "launch": "hip graph replay" if args.graph else "eager"},
+                   "cache_copies": len(caches),
+                   "launch": ("hip graph replay" if args.graph else "eager")
+                             + (", append and absorption as two calls" if args.separate_append
+                                else ", append fused into the absorption launch")},
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},

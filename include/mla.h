@@ -8,6 +8,7 @@
  *                     k_pe into the cache (contiguous or 64-token pages; an
  *                     FP4 latent cache is quantised on the way in)
  *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
+ *   mla_append_absorb the two calls above in one launch (bf16)
  *   mla_decode_attn   scores q_lat.c + q_pe.k_pe, scale, causal mask, softmax,
  *                     latent-weighted sum x (split over the tokens when that
  *                     helps, merged with a log-sum-exp combine)
@@ -201,6 +202,20 @@ MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat
 MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                              const void* k_pe_new, const mla_kv_cache* cache,
                              const int32_t* seq_lens, void* stream);
+
+/*
+ * mla_append_absorb -- mla_cache_append followed by mla_absorb_q, for a
+ * decode step whose new tokens are its queries (both use dims->q_len). The
+ * two operations touch disjoint memory, and the results are those of the two
+ * calls in sequence. With dtype MLA_BF16 both run in one kernel launch (the
+ * append costs no launch of its own); with MLA_F32 the two kernels are
+ * launched one after the other. Arguments, checks and errors are those of the
+ * two calls; nothing is enqueued unless both argument sets pass.
+ */
+MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
+                              const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
+                              int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
+                              void* stream);
 
 /*
  * mla_dequant_rows -- inspection aid: the latent of `n` physical cache rows

@@ -22,6 +22,7 @@ EXPORTS = (
     "mla_decode_attn",
     "mla_up_proj_v",
     "mla_cache_append",
+    "mla_append_absorb",
     "mla_dequant_rows",
     "mla_status_string",
 )
@@ -90,6 +91,9 @@ def load() -> ctypes.CDLL:
     lib.mla_up_proj_v.restype = ctypes.c_int
     lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P, P]
     lib.mla_cache_append.restype = ctypes.c_int
+    lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
+                                      I32, P, P, P, P]
+    lib.mla_append_absorb.restype = ctypes.c_int
     lib.mla_dequant_rows.argtypes = [ctypes.POINTER(MlaKvCache), I32, P, I32, P, P]
     lib.mla_dequant_rows.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]

@@ -63,6 +63,8 @@ struct AppendParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+// Cache append and bf16 query absorption of one decode step in one launch.
+hipError_t launch_append_absorb_bf16(const ProjParams& p, const AppendParams& a, hipStream_t s);
 hipError_t launch_dequant_rows(const CacheView& c, int latent_dtype, int Ckv, const int32_t* rows,
                                int n, float* out, hipStream_t s);
 

@@ -188,8 +188,11 @@ MLA_API const char* mla_status_string(int status) {
   }
 }
 
-MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b,
-                         void* q_lat, void* stream) {
+namespace {
+
+// Checks of mla_absorb_q; fills p.
+int prepare_absorb(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
+                   mla::ProjParams* p) {
   int st = check_dims(dims);
   if (st) return st;
   if (q_nope == nullptr || wkv_b == nullptr || q_lat == nullptr) return MLA_ERR_INVALID_ARG;
@@ -200,9 +203,19 @@ MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope
     return MLA_ERR_UNSUPPORTED;
   }
   if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  *p = mla::ProjParams{q_nope, wkv_b, q_lat, dims->batch, dims->heads, dims->q_len,
+                       dims->d_nope, dims->d_v, dims->d_latent};
+  return MLA_OK;
+}
+
+}  // namespace
+
+MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b,
+                         void* q_lat, void* stream) {
+  mla::ProjParams p{};
+  const int st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, &p);
+  if (st) return st;
   if (dims->batch == 0) return MLA_OK;
-  mla::ProjParams p{q_nope, wkv_b, q_lat, dims->batch, dims->heads, dims->q_len,
-                    dims->d_nope, dims->d_v, dims->d_latent};
   return hip_status(mla::launch_absorb(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -301,9 +314,11 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, s));
 }
 
-MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
-                             const void* k_pe_new, const mla_kv_cache* cache,
-                             const int32_t* seq_lens, void* stream) {
+namespace {
+
+// Checks of mla_cache_append; fills p.
+int prepare_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
+                   const mla_kv_cache* cache, const int32_t* seq_lens, mla::AppendParams* out) {
   int st = check_dims(dims);
   if (st) return st;
   st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
@@ -318,7 +333,6 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void
   }
   if (dims->d_latent % 8 || dims->d_rope % 8) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)dims->batch * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
-  if (dims->batch == 0) return MLA_OK;
   mla::AppendParams p{};
   p.c_kv = c_kv_new;
   p.k_pe = k_pe_new;
@@ -331,7 +345,38 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void
   p.src_dtype = src_dtype;
   p.latent_dtype = cache->latent_dtype;
   p.rope_dtype = cache->rope_dtype;
+  *out = p;
+  return MLA_OK;
+}
+
+}  // namespace
+
+MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
+                             const void* k_pe_new, const mla_kv_cache* cache,
+                             const int32_t* seq_lens, void* stream) {
+  mla::AppendParams p{};
+  const int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &p);
+  if (st) return st;
+  if (dims->batch == 0) return MLA_OK;
   return hip_status(mla::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
+                              const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
+                              int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
+                              void* stream) {
+  mla::AppendParams a{};
+  int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &a);
+  if (st) return st;
+  mla::ProjParams p{};
+  st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, &p);
+  if (st) return st;
+  if (dims->batch == 0) return MLA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MLA_BF16) return hip_status(mla::launch_append_absorb_bf16(p, a, s));
+  st = hip_status(mla::launch_append(a, s));
+  if (st) return st;
+  return hip_status(mla::launch_absorb(p, false, s));
 }
 
 MLA_API int mla_dequant_rows(const mla_kv_cache* cache, int32_t d_latent, const int32_t* rows,

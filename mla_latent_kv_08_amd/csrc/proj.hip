@@ -5,6 +5,7 @@
 // page: steps 1 and 5 of mla_decode_step.) Both stream each head's weight
 // slice once; the bf16 forms run on v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation, the fp32 forms on the vector ALU.
+#include "append_dev.h"
 #include "internal.h"
 
 namespace mla {
@@ -69,13 +70,18 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint16_t* a, const uint16_t* b) 
 // contiguous 16-byte stores.
 constexpr int kWPad = 144;  // W_UK block row pitch (elements)
 constexpr int kQPad = 136;  // query / output row pitch (elements)
-__global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[128 * kWPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[32 * kQPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * kQPad];
+struct AbsorbLds {
+  uint16_t w[128 * kWPad];
+  uint16_t q[32 * kQPad];
+  uint16_t o[32 * kQPad];
+};
+
+// Head h, latent channels c0 .. c0+127, by one 256-thread block.
+__device__ __forceinline__ void absorb_bf16_block(const ProjParams& p, int h, int c0, AbsorbLds& lds) {
+  uint16_t* const s_w = lds.w;
+  uint16_t* const s_q = lds.q;
+  uint16_t* const s_o = lds.o;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
-  const int h = blockIdx.x;
-  const int c0 = blockIdx.y * 128;
   const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)h * (p.Dn + p.Vd) * p.Ckv;
   const int M = p.B * p.Q;
   // Query rows are [B, H, Q, Dn]: row m = (b, q) of head h.
@@ -140,6 +146,27 @@ __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
       *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc);
       *reinterpret_cast<uint4*>(o + 8) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc + 8);
     }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
+  __shared__ __attribute__((aligned(16))) AbsorbLds lds;
+  absorb_bf16_block(p, blockIdx.x, blockIdx.y * 128, lds);
+}
+
+// Cache append and query absorption of one decode step in one launch: blocks
+// 0 .. H*Ckv/128-1 absorb as above (head = block / (Ckv/128)), the blocks
+// after them store four new tokens each, one per wave.
+__global__ void __launch_bounds__(kThreads) append_absorb_bf16_kernel(ProjParams p, AppendParams a) {
+  __shared__ __attribute__((aligned(16))) AbsorbLds lds;
+  const int nc = p.Ckv / 128;
+  const int n_absorb = p.H * nc;
+  const int bid = blockIdx.x;
+  if (bid < n_absorb) {
+    absorb_bf16_block(p, bid / nc, (bid % nc) * 128, lds);
+  } else {
+    const int token = (bid - n_absorb) * (kThreads / 64) + (int)(threadIdx.x >> 6);
+    if (token < a.B * a.Qn) append_token(a, token, threadIdx.x & 63);
   }
 }
 
@@ -247,6 +274,13 @@ hipError_t launch_absorb(const ProjParams& p, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(absorb_f32_kernel, dim3((unsigned)rows), dim3(kThreads),
                        (size_t)p.Dn * sizeof(float), s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_absorb_bf16(const ProjParams& p, const AppendParams& a, hipStream_t s) {
+  const int64_t tokens = (int64_t)a.B * a.Qn;
+  const int64_t blocks = (int64_t)p.H * (p.Ckv / 128) + (tokens + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(append_absorb_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLAError, MlaDecodeO
 __all__ = [
     "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLAError", "LatentCache",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_up_proj_v",
-    "mla_cache_append", "mla_dequant_rows",
+    "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
 
 
@@ -199,6 +199,26 @@ def mla_cache_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: Late
     _lib.check(_lib.load().mla_cache_append(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new),
                                             _ptr(k_pe_new), ctypes.byref(desc), _ptr(seq_lens),
                                             _stream(stream)), "mla_cache_append")
+
+
+def mla_append_absorb(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache,
+                      seq_lens: torch.Tensor, q_nope: torch.Tensor, wkv_b: torch.Tensor, q_lat: torch.Tensor,
+                      stream=None) -> None:
+    """mla_cache_append(c_kv_new, k_pe_new, cache, seq_lens) then mla_absorb_q(q_nope, wkv_b, q_lat),
+    in one launch for bf16. The new tokens are the queries: [B, Q, ...] and [B, H, Q, ...]."""
+    B, Qn, Ckv = c_kv_new.shape
+    Dr = k_pe_new.shape[-1]
+    _, H, Q, Dn = q_nope.shape
+    if Q != Qn:
+        raise ValueError("mla_append_absorb: the new tokens must be the queries (same Q)")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    Vd = wkv_b.shape[1] - Dn
+    d = _dims(B, H, Q, Dn, Dr, Vd, Ckv)
+    desc = cache.desc()
+    _lib.check(_lib.load().mla_append_absorb(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new), _ptr(k_pe_new),
+                                             ctypes.byref(desc), _ptr(seq_lens), _code(q_nope), _ptr(q_nope),
+                                             _ptr(wkv_b), _ptr(q_lat), _stream(stream)), "mla_append_absorb")
 
 
 def mla_dequant_rows(cache: LatentCache, rows: torch.Tensor, out: torch.Tensor, d_latent: int = 512,

@@ -109,3 +109,33 @@ def test_plain_append_bit_exact_and_positions(dtype):
     bb = before.cpu()[mask].float()
     assert torch.equal(torch.isnan(a), torch.isnan(bb))
     assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(bb))
+
+
+@pytest.mark.parametrize("dtype,paged", [("bf16", False), ("bf16", True), ("fp4", False), ("f32", False)])
+def test_append_absorb_equals_separate_calls(dtype, paged):
+    """mla_append_absorb leaves the same cache bytes and q_lat bits as
+    mla_cache_append followed by mla_absorb_q."""
+    o = T.ops()
+    Q = 2
+    lens = [130, 2, 65, 300]
+    base = {"bf16": "dsv3_bf16", "fp4": "mtp_fp4", "f32": "tiny_f32"}[dtype]
+    w = W.reduced(W.WORKLOADS[base], len(lens), lens).with_(Q=Q, paged=paged)
+    T.say(f"[case] append+absorb {dtype} paged={paged}")
+    inp = W.generate(w)
+    ga = T.GpuCase(inp)
+    gb = T.GpuCase(inp)
+    B = w.B
+    g = torch.Generator().manual_seed(11)
+    sd = torch.float32 if dtype == "f32" else torch.bfloat16
+    src = torch.float32 if dtype in ("f32", "fp4") else torch.bfloat16
+    c_new = torch.randn(B, Q, w.Ckv, generator=g).to(src).cuda()
+    r_new = torch.randn(B, Q, w.Dr, generator=g).to(inp.rope.dtype).cuda()
+    qa = torch.empty(B, w.H, Q, w.Ckv, dtype=sd, device="cuda")
+    qb = torch.empty_like(qa)
+    o.mla_cache_append(c_new, r_new, ga.cache, ga.seq_lens)
+    o.mla_absorb_q(ga.q_nope, ga.wkv_b, qa)
+    o.mla_append_absorb(c_new, r_new, gb.cache, gb.seq_lens, gb.q_nope, gb.wkv_b, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(ga.buf.view(torch.uint8), gb.buf.view(torch.uint8)), "cache bytes differ"
+    assert torch.equal(qa.view(torch.int16 if sd == torch.bfloat16 else torch.int32),
+                       qb.view(torch.int16 if sd == torch.bfloat16 else torch.int32)), "q_lat differs"
