@@ -8,13 +8,15 @@ Vd=128, Ckv=512, 4096 cached tokens per sequence in a contiguous
 
 One step = the whole path: the cache append of the new token's row and the
 query absorption (mla_append_absorb: mla_cache_append and mla_absorb_q in one
-launch; --separate-append calls the two), mla_decode_attn (token-split
-attention + log-sum-exp merge) and mla_up_proj_v. Inputs are resident in HBM before timing starts; every step
+launch; --separate-append calls the two), then attention and the value
+up-projection (mla_decode_attn_up: token-split attention, then the
+log-sum-exp merge and W_UV in one kernel; --separate-up calls mla_decode_attn
+and mla_up_proj_v). Inputs are resident in HBM before timing starts; every step
 reads a different one of several cache copies so that the 256 MB Infinity
 Cache cannot serve the 151 MB cache from the previous step.
 
 Prints one JSON line (see the keys below). --gpus N with N > 1 is refused:
-this build runs on one GPU.
+the benchmark measures one GPU's share.
 """
 from __future__ import annotations
 
@@ -305,7 +307,7 @@ def gpu_context(dev) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (>= 3 defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,6 +317,8 @@ def main():
                          "graphs instead of launching the calls one by one")
     ap.add_argument("--separate-append", action="store_true",
                     help="call mla_cache_append and mla_absorb_q separately instead of mla_append_absorb")
+    ap.add_argument("--separate-up", action="store_true",
+                    help="call mla_decode_attn and mla_up_proj_v separately instead of mla_decode_attn_up")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (ragged paged, long context, FP4 MTP, tiny fp32) "
                          "and the context figures (copy rate, clocks)")
@@ -328,8 +332,8 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU form of this "
-              "path is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; it measures one GPU's share of a sharded decode.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -386,12 +390,23 @@ def main():
         else:
             ops.mla_append_absorb(c_new, r_new, caches[c], seq_lens, q_nope, wkv_b, q_lat, stream=st)
 
-    def step_calls(c, st):
-        append_absorb(c, st)
-        attend(c, st)
+    def up_proj(c, st):
         ops.mla_up_proj_v(x, wkv_b, out, stream=st)
 
-    # A decode step is the same four library calls every time. By default they
+    def attend_up(c, st):
+        ops.mla_decode_attn_up(q_lat, q_pe, caches[c], seq_lens, max_len, w.softmax_scale, x, lse, wkv_b, out,
+                               workspace=workspace, workgroups=args.workgroups, stream=st)
+
+    if args.separate_up:
+        parts = (("append_absorb", append_absorb), ("attn", attend), ("up_proj", up_proj))
+    else:
+        parts = (("append_absorb", append_absorb), ("attn_up", attend_up))
+
+    def step_calls(c, st):
+        for _, fn in parts:
+            fn(c, st)
+
+    # A decode step is the same library calls every time. By default they
     # are launched one by one; with --graph they are captured once per cache
     # copy into HIP graphs and replayed (measured no faster on this stack: a
     # graph launch costs about what the separate launches do).
@@ -431,20 +446,17 @@ def main():
 
     # Each call's share of a step: a second eager pass with an event between
     # consecutive calls (so each call sees the cache state of a real step).
-    names = ("append_absorb", "attn", "up_proj")
+    names = tuple(k for k, _ in parts)
     in_step = {k: 0.0 for k in names}
     if not args.graph:
         evs = []
         for i in range(args.steps):
             c = i % ncopy
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
             e[0].record(stream)
-            append_absorb(c, stream)
-            e[1].record(stream)
-            attend(c, stream)
-            e[2].record(stream)
-            ops.mla_up_proj_v(x, wkv_b, out, stream=stream)
-            e[3].record(stream)
+            for j, (_, fn) in enumerate(parts):
+                fn(c, stream)
+                e[j + 1].record(stream)
             evs.append(e)
         torch.cuda.synchronize()
         for e in evs:
@@ -532,7 +544,9 @@ def main():
                    "cache_copies": len(caches),
                    "launch": ("hip graph replay" if args.graph else "eager")
                              + (", append and absorption as two calls" if args.separate_append
-                                else ", append fused into the absorption launch")},
+                                else ", append fused into the absorption launch")
+                             + (", attention and up-projection as two calls" if args.separate_up
+                                else ", split merge fused with the up-projection")},
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},

@@ -9,6 +9,8 @@
  *                     FP4 latent cache is quantised on the way in)
  *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
  *   mla_append_absorb the two calls above in one launch (bf16)
+ *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
+ *                     up-projection in one kernel (bf16)
  *   mla_decode_attn   scores q_lat.c + q_pe.k_pe, scale, causal mask, softmax,
  *                     latent-weighted sum x (split over the tokens when that
  *                     helps, merged with a log-sum-exp combine)
@@ -176,6 +178,21 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
                             int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
                             void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
                             void* stream);
+
+/*
+ * mla_decode_attn_up -- mla_decode_attn followed by mla_up_proj_v on its x
+ * (same arguments as the two calls; x_lat and lse are still written). The
+ * results are those of the two calls in sequence. With dtype MLA_BF16 the
+ * merge of the token splits and the up-projection run as one kernel, which
+ * takes the merged rows of each head straight to the matrix ops instead of
+ * reading x back; with MLA_F32 the two calls' kernels run one after the
+ * other. Nothing is enqueued unless both argument sets pass their checks.
+ */
+MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+                               const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                               float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
+                               void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
+                               void* stream);
 
 /*
  * mla_up_proj_v -- out[b,h,q,v] = sum_c W_UV[h,v,c] * x_lat[b,h,q,c]

@@ -20,6 +20,7 @@ EXPORTS = (
     "mla_absorb_q",
     "mla_decode_workspace_size",
     "mla_decode_attn",
+    "mla_decode_attn_up",
     "mla_up_proj_v",
     "mla_cache_append",
     "mla_append_absorb",
@@ -87,6 +88,10 @@ def load() -> ctypes.CDLL:
                                     I32, ctypes.c_float, P, P, P, ctypes.c_size_t,
                                     ctypes.POINTER(MlaDecodeOpts), P]
     lib.mla_decode_attn.restype = ctypes.c_int
+    lib.mla_decode_attn_up.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
+                                       I32, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t,
+                                       ctypes.POINTER(MlaDecodeOpts), P]
+    lib.mla_decode_attn_up.restype = ctypes.c_int
     lib.mla_up_proj_v.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P]
     lib.mla_up_proj_v.restype = ctypes.c_int
     lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P, P]

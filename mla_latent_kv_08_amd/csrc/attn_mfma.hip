@@ -998,56 +998,62 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   }
 }
 
-// Merge partial results of sequences whose tiles were split over workgroups,
-// and write x = 0 / lse = -inf for sequences without any cache rows.
-// Grid: (B, groups * 4); each block handles 16 query rows of one sequence.
-constexpr int kCombineThreads = 256;
-__global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParams p) {
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int g = blockIdx.y >> 2;
-  const int rb = blockIdx.y & 3;
-
-  // Run plan left by the attention kernel.
-  const int nb = tiles_of(seq_len(p, b));
-  const int cum_b = p.plan[b];
-  const int total_tiles = p.plan[p.B];
-
-  // 16 lanes per row; lane j of a row holds channels 8j + 128k .. +7 (k < 4),
-  // so each 16-byte load of the 16 lanes covers 256 contiguous bytes.
-  const int row_local = rb * 16 + (tid >> 4);
-  const int row = g * kRowsPerGroup + row_local;
-  const int c0 = (tid & 15) * 8;
-  if (row >= p.HQ) return;
+// Merged x of query row `row` (group layout, row = h * Q + q) of sequence b,
+// by L lanes (16 or 32): lane j gets channels 8j + 8Lk .. +7 (k < 64 / L) as
+// bf16 in xq, so each 16-byte load of the L lanes covers 16L contiguous bytes.
+// Every channel goes through the same operations for either L.
+//   - a sequence without cache rows: x = 0, lse = -inf (written here);
+//   - a sequence whose tiles were split over workgroups: its partials merged
+//     in batches of four, all loads of a batch in flight together, with a
+//     running max M, sum S and weighted sum acc (rescaled when M rises),
+//     lse = M + log S, x = acc / S (written here);
+//   - a sequence one workgroup took whole: x and lse were written by the
+//     attention kernel; xq is read back only if `need_x`.
+// The run plan (each sequence's first tile in run order) was left by the
+// attention kernel.
+template <int L>
+__device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, int j, bool need_x,
+                                          uint4 xq[64 / L]) {
+  constexpr int kC = 64 / L;  // 16-byte chunks per lane
+  const int g = row / kRowsPerGroup;
+  const int row_local = row % kRowsPerGroup;
   const int64_t grow = (int64_t)b * p.HQ + row;
   uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + grow * p.Ckv;
-
+  const int c0 = 8 * j;
+  const int nb = tiles_of(seq_len(p, b));
   if (nb == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(xo + c0 + 128 * k) = make_uint4(0, 0, 0, 0);
-    if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = -INFINITY;
+    for (int k = 0; k < kC; ++k) {
+      xq[k] = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(xo + c0 + 8 * L * k) = xq[k];
+    }
+    if (p.lse != nullptr && j == 0) p.lse[grow] = -INFINITY;
     return;
   }
+  const int cum_b = p.plan[b];
+  const int total_tiles = p.plan[p.B];
   const int per = (total_tiles + p.workgroups - 1) / p.workgroups;
   const int i_first = cum_b / per;
   const int i_last = (cum_b + nb - 1) / per;
-  if (i_first == i_last) return;  // the attention kernel wrote this sequence directly
-
+  if (i_first == i_last) {
+    if (need_x) {
+#pragma unroll
+      for (int k = 0; k < kC; ++k) xq[k] = *reinterpret_cast<const uint4*>(xo + c0 + 8 * L * k);
+    }
+    return;
+  }
   const int slots = 2 * p.workgroups;
   auto slot_of = [&](int i) { return 2 * i + ((i == i_first && cum_b != i_first * per) ? 1 : 0); };
   auto prow_of = [&](int i) { return ((int64_t)g * slots + slot_of(i)) * kRowsPerGroup + row_local; };
-  // Partials in batches of four, all loads of a batch in flight together;
-  // running max M, sum S and weighted sum acc (rescaled when M rises):
-  //   lse = M + log S,  x = acc / S.
   constexpr int kBatch = 4;
-  float acc[32];
+  float acc[8 * kC];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < 8 * kC; ++k) acc[k] = 0.0f;
   float M = -INFINITY, S = 0.0f;
   bool any_nan = false;
   for (int i0 = i_first; i0 <= i_last; i0 += kBatch) {
     float ls[kBatch];
-    uint4 xv[kBatch][4];
+    uint4 xv[kBatch][kC];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool in = i0 + u <= i_last;
@@ -1056,7 +1062,7 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
       if (!in) ls[u] = -INFINITY;
       const uint4* src = reinterpret_cast<const uint4*>(p.part_x + prow * 512 + c0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) xv[u][k] = src[16 * k];
+      for (int k = 0; k < kC; ++k) xv[u][k] = src[L * k];
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -1069,13 +1075,13 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
     const float sc = __expf(M - Mn);  // 0 while M is -inf
     S *= sc;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] *= sc;
+    for (int k = 0; k < 8 * kC; ++k) acc[k] *= sc;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const float w = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
       S += w;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kC; ++k) {
         const uint32_t wd[4] = {xv[u][k].x, xv[u][k].y, xv[u][k].z, xv[u][k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1090,27 +1096,93 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   if (any_nan) {
     lse_v = __uint_as_float(0x7fc00000u);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] = lse_v;
+    for (int k = 0; k < 8 * kC; ++k) acc[k] = lse_v;
   } else if (M == -INFINITY) {
     lse_v = -INFINITY;
   } else {
     lse_v = M + __logf(S);
     const float inv = 1.0f / S;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] *= inv;
+    for (int k = 0; k < 8 * kC; ++k) acc[k] *= inv;
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    *reinterpret_cast<uint4*>(xo + c0 + 128 * k) =
-        make_uint4(pack_bf16x2(acc[8 * k], acc[8 * k + 1]), pack_bf16x2(acc[8 * k + 2], acc[8 * k + 3]),
-                   pack_bf16x2(acc[8 * k + 4], acc[8 * k + 5]), pack_bf16x2(acc[8 * k + 6], acc[8 * k + 7]));
+  for (int k = 0; k < kC; ++k) {
+    xq[k] = make_uint4(pack_bf16x2(acc[8 * k], acc[8 * k + 1]), pack_bf16x2(acc[8 * k + 2], acc[8 * k + 3]),
+                       pack_bf16x2(acc[8 * k + 4], acc[8 * k + 5]), pack_bf16x2(acc[8 * k + 6], acc[8 * k + 7]));
+    *reinterpret_cast<uint4*>(xo + c0 + 8 * L * k) = xq[k];
   }
-  if (p.lse != nullptr && (tid & 15) == 0) p.lse[grow] = lse_v;
+  if (p.lse != nullptr && j == 0) p.lse[grow] = lse_v;
+}
+
+// Merge of the partials of sequences split over workgroups (and x = 0 /
+// lse = -inf for sequences without cache rows). Grid: (B, groups * 4); each
+// block handles 16 query rows of one sequence.
+constexpr int kCombineThreads = 256;
+__global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParams p) {
+  const int row = (blockIdx.y >> 2) * kRowsPerGroup + (blockIdx.y & 3) * 16 + (threadIdx.x >> 4);
+  if (row >= p.HQ) return;
+  uint4 xq[4];
+  merge_row<16>(p, blockIdx.x, row, threadIdx.x & 15, false, xq);
+}
+
+// The merge and the up-projection out[b,h,q,:] = W_UV[h] x[b,h,q,:] in one
+// launch. Block (h, y) takes query rows 16y .. 16y+15 of head h (rows ordered
+// m = b * Q + q). Wave w first requests its W_UV slice (value columns
+// 16w .. 16w+15, all 512 latent channels: 64 registers a lane), so that
+// those loads are in flight during the merge; the merged (or whole) x rows,
+// 32 lanes a row, go to x_lat and to LDS as bf16; then the wave forms out^T
+// for its 16 columns by v_mfma_f32_16x16x32_bf16 (A = the W_UV slice,
+// B = the x rows from LDS) with fp32 accumulation.
+constexpr int kMUThreads = 512;
+constexpr int kMURows = 16;
+constexpr int kMURow = 520;  // staged x row pitch (bf16): 1 KiB + 16 B
+__global__ void __launch_bounds__(kMUThreads) merge_up_kernel(AttnParams p, ProjParams u) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kMURows * kMURow];
+  const int h = blockIdx.x;
+  const int m0 = kMURows * blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4;
+  const int M = p.B * p.Q;
+  // A lane l: W_UV row 16w + l % 16, channels 32ks + 8(l / 16) .. +7.
+  const uint16_t* wv = reinterpret_cast<const uint16_t*>(u.w) +
+                       ((int64_t)h * (u.Dn + u.Vd) + u.Dn + 16 * wave + (lane & 15)) * u.Ckv + 8 * quad;
+  bf16x8 a[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wv + 32 * ks);
+  {
+    const int r = tid >> 5;
+    const int m = m0 + r;
+    uint4 xq[2];
+    if (m < M) {
+      merge_row<32>(p, m / p.Q, h * p.Q + m % p.Q, tid & 31, true, xq);
+    } else {
+      xq[0] = xq[1] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4*>(s_x + r * kMURow + 8 * (tid & 31) + 256 * k) = xq[k];
+  }
+  __syncthreads();
+  // B lane l: x row l % 16, the same channels as A. Even and odd k-steps
+  // accumulate separately so no matrix op waits on the one before.
+  const uint16_t* xb = s_x + (lane & 15) * kMURow + 8 * quad;
+  floatx4 acc[2] = {floatx4{}, floatx4{}};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], *reinterpret_cast<const bf16x8*>(xb + 32 * ks),
+                                                          acc[ks & 1], 0, 0, 0);
+  }
+  const floatx4 o4 = acc[0] + acc[1];
+  // D^T lane l: row m = m0 + l % 16, value columns 16w + 4(l / 16) .. +3.
+  const int m = m0 + (lane & 15);
+  if (m < M) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(u.out) +
+                  (((int64_t)(m / p.Q) * p.H + h) * p.Q + m % p.Q) * u.Vd + 16 * wave + 4 * quad;
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
+  }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, hipStream_t s) {
+hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, const ProjParams* up, hipStream_t s) {
   const int blocks = ((p.workgroups + 7) / 8) * 8 * p.groups;
   if (fp4_latent) {
     hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
@@ -1119,8 +1191,14 @@ hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, hipStream_t s)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B, p.groups * (kRowsPerGroup / 16)),
-                     dim3(kCombineThreads), 0, s, p);
+  if (up != nullptr) {
+    const int chunks = (p.B * p.Q + kMURows - 1) / kMURows;
+    if (chunks > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(merge_up_kernel, dim3(p.H, chunks), dim3(kMUThreads), 0, s, p, *up);
+  } else {
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(p.B, p.groups * (kRowsPerGroup / 16)),
+                       dim3(kCombineThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -38,15 +38,17 @@ struct AttnParams {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, hipStream_t s);
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s);
-
 struct ProjParams {
   const void* in;   // absorb: q_nope [B,H,Q,Dn]; up: x [B,H,Q,Ckv]
   const void* w;    // wkv_b [H, Dn+Vd, Ckv]
   void* out;        // absorb: q_lat [B,H,Q,Ckv]; up: out [B,H,Q,Vd]
   int B, H, Q, Dn, Vd, Ckv;
 };
+
+// Attention kernel, then either the merge (up == null) or the merge and the
+// up-projection `up` in one kernel.
+hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, const ProjParams* up, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t s);
 
 hipError_t launch_absorb(const ProjParams& p, bool bf16, hipStream_t s);
 hipError_t launch_up_proj(const ProjParams& p, bool bf16, hipStream_t s);

@@ -219,21 +219,17 @@ MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope
   return hip_status(mla::launch_absorb(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int prepare_up(const mla_dims* dims, int32_t dtype, const void* x_lat, const void* wkv_b, void* out,
+               mla::ProjParams* p);
+}  // namespace
+
 MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat, const void* wkv_b,
                           void* out, void* stream) {
-  int st = check_dims(dims);
+  mla::ProjParams p{};
+  const int st = prepare_up(dims, dtype, x_lat, wkv_b, out, &p);
   if (st) return st;
-  if (x_lat == nullptr || wkv_b == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(x_lat) || !aligned16(wkv_b) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
-  if (dtype == MLA_BF16) {
-    if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
-  } else if (dtype != MLA_F32) {
-    return MLA_ERR_UNSUPPORTED;
-  }
-  if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   if (dims->batch == 0) return MLA_OK;
-  mla::ProjParams p{x_lat, wkv_b, out, dims->batch, dims->heads, dims->q_len,
-                    dims->d_nope, dims->d_v, dims->d_latent};
   return hip_status(mla::launch_up_proj(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -253,10 +249,13 @@ MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32
   return MLA_OK;
 }
 
-MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
-                            const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                            float softmax_scale, void* x_lat, float* lse, void* workspace,
-                            size_t workspace_bytes, const mla_decode_opts* opts, void* stream) {
+namespace {
+
+// Checks of mla_decode_attn; fills p (a batch of 0 leaves p.B = 0).
+int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+                   const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                   void* x_lat, float* lse, void* workspace, size_t workspace_bytes,
+                   const mla_decode_opts* opts, mla::AttnParams* out) {
   int st = check_attn(dims, dtype, cache, max_seq_len, opts);
   if (st) return st;
   st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
@@ -266,6 +265,7 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   }
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(x_lat)) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale)) return MLA_ERR_INVALID_ARG;
+  *out = mla::AttnParams{};
   if (dims->batch == 0) return MLA_OK;
 
   mla::AttnParams p{};
@@ -282,7 +282,6 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   p.Ckv = dims->d_latent;
   p.Dr = dims->d_rope;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MLA_F32) {
     const int splits = f32_splits(dims, max_seq_len, opts);
     const size_t need = f32_workspace_bytes(dims, splits);
@@ -297,7 +296,8 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
       p.part_xf = static_cast<float*>(workspace);
       p.part_lse = p.part_xf + rows * p.Ckv;
     }
-    return hip_status(mla::launch_attn_f32(p, s));
+    *out = p;
+    return MLA_OK;
   }
   int cus = 0;
   st = num_cus(&cus);
@@ -311,7 +311,62 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
   p.part_x = static_cast<uint16_t*>(workspace);
   p.part_lse = reinterpret_cast<float*>(p.part_x + part_rows * p.Ckv);
   p.plan = reinterpret_cast<int*>(p.part_lse + part_rows);
-  return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, s));
+  *out = p;
+  return MLA_OK;
+}
+
+// Checks of mla_up_proj_v; fills p.
+int prepare_up(const mla_dims* dims, int32_t dtype, const void* x_lat, const void* wkv_b, void* out,
+               mla::ProjParams* p) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (x_lat == nullptr || wkv_b == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x_lat) || !aligned16(wkv_b) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (dtype == MLA_BF16) {
+    if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
+  } else if (dtype != MLA_F32) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  *p = mla::ProjParams{x_lat, wkv_b, out, dims->batch, dims->heads, dims->q_len,
+                       dims->d_nope, dims->d_v, dims->d_latent};
+  return MLA_OK;
+}
+
+}  // namespace
+
+MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+                            const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                            float softmax_scale, void* x_lat, float* lse, void* workspace,
+                            size_t workspace_bytes, const mla_decode_opts* opts, void* stream) {
+  mla::AttnParams p{};
+  const int st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat,
+                                lse, workspace, workspace_bytes, opts, &p);
+  if (st || p.B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MLA_F32) return hip_status(mla::launch_attn_f32(p, s));
+  return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, nullptr, s));
+}
+
+MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+                               const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                               float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
+                               void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
+                               void* stream) {
+  mla::AttnParams p{};
+  int st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat, lse,
+                          workspace, workspace_bytes, opts, &p);
+  if (st) return st;
+  mla::ProjParams u{};
+  st = prepare_up(dims, dtype, x_lat, wkv_b, out, &u);
+  if (st || p.B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MLA_F32) {
+    st = hip_status(mla::launch_attn_f32(p, s));
+    if (st) return st;
+    return hip_status(mla::launch_up_proj(u, false, s));
+  }
+  return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, &u, s));
 }
 
 namespace {

@@ -18,7 +18,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLAError, MlaDecodeO
 
 __all__ = [
     "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLAError", "LatentCache",
-    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_up_proj_v",
+    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
 
@@ -175,6 +175,33 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
         int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
         "mla_decode_attn")
+
+
+def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
+                       seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                       x_lat: torch.Tensor, lse: Optional[torch.Tensor], wkv_b: torch.Tensor, out: torch.Tensor,
+                       workspace: Optional[torch.Tensor] = None, workgroups: int = 0, stream=None) -> None:
+    """mla_decode_attn then mla_up_proj_v on its x; see mla_decode_attn_up in include/mla.h."""
+    B, H, Q, Ckv = q_lat.shape
+    Dr = q_pe.shape[-1]
+    Vd = out.shape[-1]
+    d_nope = wkv_b.shape[1] - Vd
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    code = _code(q_lat)
+    d = _dims(B, H, Q, d_nope, Dr, Vd, Ckv)
+    opts = MlaDecodeOpts(int(workgroups))
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(B, H, Q, code, max_seq_len, workgroups, d_nope, Dr, Vd, Ckv)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q_lat.device)
+    desc = cache.desc()
+    _lib.check(_lib.load().mla_decode_attn_up(
+        ctypes.byref(d), code, _ptr(q_lat), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
+        int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(wkv_b), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
+        "mla_decode_attn_up")
 
 
 def mla_up_proj_v(x_lat: torch.Tensor, wkv_b: torch.Tensor, out: torch.Tensor, stream=None) -> None:

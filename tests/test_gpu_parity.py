@@ -206,3 +206,43 @@ def test_full_long_splitkv_bf16_sampled():
 
 def test_full_mtp_fp4_sampled():
     _full_sampled("mtp_fp4", [(0, 0), (127, 127), (64, 31)])
+
+
+# mla_decode_attn_up runs the merge and the up-projection as one kernel on the
+# bf16 path; its x, lse and out must be the two calls' bits.
+@pytest.mark.parametrize("name,lens,workgroups", [
+    ("dsv3_bf16", [300, 129, 0, 4096], 0),
+    ("dsv3_bf16", [700, 33, 1, 260], 5),
+    ("mtp_fp4", [700, 33, 1, 260], 40),
+    ("ragged_paged_bf16", [1000, 64, 3], 0),
+    ("tiny_f32", [300, 1, 77], 5),
+])
+def test_decode_attn_up_equals_two_calls(name, lens, workgroups):
+    o = T.ops()
+    w = W.reduced(W.WORKLOADS[name], len(lens), lens)
+    if name == "dsv3_bf16":
+        w = w.with_(H=40)  # rows not a multiple of 64: a partly empty row group
+    inp, g = _case(w)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    B, H, Q = w.B, w.H, w.Q
+    q_lat = torch.empty(B, H, Q, w.Ckv, dtype=dt, device="cuda")
+    o.mla_absorb_q(g.q_nope, g.wkv_b, q_lat)
+    res = []
+    for fused in (False, True):
+        x = torch.full((B, H, Q, w.Ckv), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((B, H, Q), float("nan"), dtype=torch.float32, device="cuda")
+        out = torch.full((B, H, Q, w.Vd), float("nan"), dtype=dt, device="cuda")
+        if fused:
+            o.mla_decode_attn_up(q_lat, g.q_pe, g.cache, g.seq_lens, g.max_len, w.softmax_scale, x, lse,
+                                 g.wkv_b, out, workgroups=workgroups)
+        else:
+            o.mla_decode_attn(q_lat, g.q_pe, g.cache, g.seq_lens, g.max_len, w.softmax_scale, x, lse,
+                              workgroups=workgroups)
+            o.mla_up_proj_v(x, g.wkv_b, out)
+        torch.cuda.synchronize()
+        res.append((x, lse, out))
+    (x0, l0, u0), (x1, l1, u1) = res
+    iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(x0.view(iv), x1.view(iv)), "x differs"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "lse differs"
+    T.assert_close(T.to64(u1), T.to64(u0), 1e-6 if dt == torch.float32 else 2e-3, "out (fused vs two calls)")
