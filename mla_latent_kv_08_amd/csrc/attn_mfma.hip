@@ -21,12 +21,13 @@
 //                      registers, v_mfma_f32_32x32x16_bf16); each transposed
 //                      V fragment feeds both row blocks. They also start the
 //                      tile copies into LDS.
-// Step k has two phases split by barriers. Phase 1: score waves form S^T for
-// tile k and publish their 16-token row maxima; P.V waves start tile k+2 and
-// apply the first 16 tokens of tile k-1. Phase 2: each score wave takes the
-// tile max of both halves, so the two halves of a row block keep one running
-// max m and rescale decision, and writes bf16 probabilities and its own part
-// of the row sum; P.V waves apply the other 16 tokens of tile k-1.
+// One barrier starts step k. Score waves form S^T for tile k and write its
+// bf16 probabilities, their half's reference max and row sum; P.V waves
+// start the copy of tile k+2 and apply both halves of tile k-1. The two
+// halves of a row block need not wait for each other: each takes its
+// probabilities against its own reference max, which follows the partner's
+// from the step before and moves by itself only on a jump of more than 2^8,
+// and the P.V waves keep O at the largest reference applied so far.
 //
 // Tiles of 32 tokens (half a cache page) live in a ring of four LDS buffers:
 // the P.V tile, the score tile and two tiles in flight. bf16 rows are copied
@@ -63,12 +64,11 @@ constexpr int kRawCodeBytes = kTile * 256;
 constexpr int kRawScaleBase = kRawCodeBytes;
 constexpr int kRawRopeBase = kRawScaleBase + kTile * 32;
 constexpr int kRawBytes = kRawRopeBase + kTile * 128;  // 13312
+// Per tile and token half th (log2 domain): the reference max the half's
+// probabilities were taken against, and the half's running sum relative to it.
 struct Meta {
-  float alpha[kRowsPerGroup];  // factor on O before this tile's P.V
-  float m[kRowsPerGroup];      // running max after this tile
-  float l[2][kRowsPerGroup];   // running sum of each token half after this tile
-  int rescale[2];              // per row block: some alpha != 1
-  int pad[2];
+  float m[2][kRowsPerGroup];
+  float l[2][kRowsPerGroup];
 };
 constexpr int kDmaPerWave = kTile / 4 + 1;             // bf16 loads per P.V wave and tile
 constexpr int kFp4DmaPerWave = 4;                      // FP4 loads per P.V wave and tile
@@ -77,8 +77,7 @@ constexpr int kFp4DmaPerWave = 4;                      // FP4 loads per P.V wave
 // score tile, two tiles in flight). FP4 cache: a ring of three bf16 tile
 // buffers (P.V tile, score tile, the next tile being decoded) and three raw
 // slots, so three raw tiles are in flight while one is decoded. Then the
-// probability slots, the per-tile metadata, the tile row maxima [rb][th][32]
-// and the pair flags [rb][th].
+// probability slots and the per-tile metadata.
 // Query rows of a run's first sequence are staged once in two ring buffers
 // that stay free until step 0 (bf16: 2 and 3, whose tile copies start in
 // step 0; FP4: 1 and 2, whose decoding starts in step 0): latent row r
@@ -91,9 +90,7 @@ struct Lds {
   static constexpr int kRawBase = kRing * kTileBytes;
   static constexpr int kPBase = kRawBase + kRawSlots * kRawBytes;
   static constexpr int kMetaBase = kPBase + 2 * kPSlotBytes;
-  static constexpr int kMaxBase = kMetaBase + 2 * (int)sizeof(Meta);
-  static constexpr int kFlagBase = kMaxBase + 2 * 2 * 32 * (int)sizeof(float);
-  static constexpr int kBytes = kFlagBase + 4 * (int)sizeof(int);
+  static constexpr int kBytes = kMetaBase + 2 * (int)sizeof(Meta);
   static constexpr int kQBase = (kFp4 ? 1 : 2) * kTileBytes;
   static constexpr int kQRopeBase = kQBase + kRowsPerGroup * kLatRowBytes;
   static_assert(kBytes <= 160 * 1024, "LDS budget");
@@ -113,8 +110,6 @@ static_assert(2 * kStageBytes <= kTileBytes, "two P.V waves stage in one free bu
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-typedef __attribute__((address_space(3))) volatile int lds_vint;
-typedef __attribute__((address_space(3))) volatile float lds_vfloat;
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 // One buffer load of 16 bytes per lane straight into LDS: lane i's bytes land
@@ -131,23 +126,6 @@ __device__ __forceinline__ void lds_copy16(int32x4_t rsrc, uint32_t lds_base, in
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc)
                : "memory");
-}
-
-// One round trip for the row-max exchange: the partner's flag word, then its
-// maxima for rows l16 and 16 + l16 (64 bytes further), read in that order and
-// waited for inside the block (the results are complete when it ends). The
-// wait also covers this wave's own LDS writes issued before it.
-__device__ __forceinline__ int poll_pair(uint32_t a_flag, uint32_t a_max, float& m0, float& m1) {
-  int f;
-  asm volatile(
-      "ds_read_b32 %0, %3\n\t"
-      "ds_read_b32 %1, %4\n\t"
-      "ds_read_b32 %2, %4 offset:64\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(f), "=&v"(m0), "=&v"(m1)
-      : "v"(a_flag), "v"(a_max)
-      : "memory");
-  return f;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -480,8 +458,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 
   uint8_t* const ptiles = smem + L::kPBase;
   Meta* const metas = reinterpret_cast<Meta*>(smem + L::kMetaBase);
-  float* const tile_max = reinterpret_cast<float*>(smem + L::kMaxBase);
-  int* const pair_flag = reinterpret_cast<int*>(smem + L::kFlagBase);
 
   if (is_score) {
     // ================= score waves: S^T, softmax, probabilities =================
@@ -548,7 +524,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    if (lane == 0) pair_flag[wave] = 0;
     lds_barrier();  // query rows staged
     if (rows_on) {
 #pragma unroll
@@ -570,7 +545,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       lds_barrier();  // step k
       const bool active = rows_on && k < count;
       floatx4 s[2];
-      float mx[2], pmx[2], esp[2][4];
+      float mx[2], esp[2][4];
       float sc_c = 1.0f;
       if (active) {
         if (k == 0 || sc.tile == 0) {
@@ -638,79 +613,31 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           v = xor32_max(xor16_max(v));
           mx[rh] = whole_tile ? v * c : v;
         }
-        if (g4 == 0) {
-#pragma unroll
-          for (int rh = 0; rh < 2; ++rh) tile_max[(rb * 2 + th) * 32 + 16 * rh + l16] = mx[rh];
-        }
-        // Publish this half's maxima for step k (the maxima, then the flag),
-        // and read the other half's flag and maxima in one round trip until
-        // the flag shows step k. LDS operations of one wave complete in issue
-        // order, so maxima read after a flag showing step k are the ones
-        // written before it. Both waves of the pair reach this point in every
-        // active step; the wait is bounded all the same.
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) *(lds_vint*)(pair_flag + wave) = k + 1;
-        // First look: plain reads, whose latency the exponentials below cover;
-        // later looks (the partner not there yet) poll in one round trip each.
-        const float* const pmax = tile_max + (rb * 2 + (th ^ 1)) * 32 + l16;
-        int f0 = *(lds_vint*)(pair_flag + (wave ^ 1));
-        pmx[0] = *(lds_vfloat*)(pmax);
-        pmx[1] = *(lds_vfloat*)(pmax + 16);
-        if constexpr (kFp4) {
-          // FP4 (where the score chain bounds the step): exponentials against
-          // the current reference max while the reads are in flight. They
-          // stand unless the pair's tile max moves the reference (a row's
-          // first tile, a large jump), which is rare.
-#pragma unroll
-          for (int rh = 0; rh < 2; ++rh) {
-            const float mu = m[rh] == -INFINITY ? 0.0f : m[rh];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -mu));
-          }
-          // (Keeps the exponentials ahead of the first use of the flag.)
-          asm volatile("" ::"v"(esp[0][0]), "v"(esp[0][1]), "v"(esp[0][2]), "v"(esp[0][3]), "v"(esp[1][0]),
-                       "v"(esp[1][1]), "v"(esp[1][2]), "v"(esp[1][3]));
-        }
-        if (__builtin_amdgcn_readfirstlane(f0) <= k) {
-          const uint32_t a_flag = lds_addr(reinterpret_cast<const uint8_t*>(pair_flag + (wave ^ 1)));
-          const uint32_t a_max = (uint32_t)reinterpret_cast<uintptr_t>(
-              (const __attribute__((address_space(3))) float*)(pmax));
-          for (int spin = 0; spin < (1 << 22); ++spin) {
-            __builtin_amdgcn_s_sleep(1);
-            const int f = poll_pair(a_flag, a_max, pmx[0], pmx[1]);
-            if (__builtin_amdgcn_readfirstlane(f) > k) break;
-          }
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
       }
       if (active) {
         // ---- online softmax in the log2 domain ----
-        // Both halves see the same tile max, so their running max m and
-        // rescale decisions stay identical. The reference m moves only when
-        // the tile max exceeds it by more than kRescaleLog2, so O is rarely
-        // rescaled and p stays <= 2^kRescaleLog2.
+        // Each token half keeps its own reference max per row and takes its
+        // probabilities against it. The reference moves when the partner half
+        // had a larger one at the previous step (read here, with no wait: it
+        // was written before this step's barrier) or when this half's tile
+        // max exceeds it by more than kRescaleLog2, so p stays <= 2^kRescaleLog2
+        // and the references of the two halves part only for the step after
+        // one of them jumps. O keeps its own scale (see the P.V waves).
+        const bool seg_first = k == 0 || sc.tile == 0;
+        const Meta* prev = metas + ((k + 1) & 1);  // step k - 1
         float alpha[2];
-        bool upd[2];
         bf16x4 pk[2];
 #pragma unroll
         for (int rh = 0; rh < 2; ++rh) {
-          const float mt = fmaxf(mx[rh], pmx[rh]);
-          upd[rh] = mt > m[rh] + kRescaleLog2;
-          const float m_new = upd[rh] ? mt : m[rh];
-          alpha[rh] = upd[rh] ? __builtin_amdgcn_exp2f(m[rh] - m_new) : 1.0f;
+          const int rl = rb * 32 + 16 * rh + l16;
+          const float pm = seg_first ? -INFINITY : prev->m[th ^ 1][rl];
+          const float ref = fmaxf(m[rh], pm);
+          const float m_new = mx[rh] > ref + kRescaleLog2 ? mx[rh] : ref;
+          alpha[rh] = m_new == m[rh] ? 1.0f : __builtin_amdgcn_exp2f(m[rh] - m_new);
           m[rh] = m_new;
-        }
-        if (!kFp4 || __any(upd[0] || upd[1])) {
-          // bf16: the exponentials; FP4: again for the rows whose reference
-          // moved.
+          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
 #pragma unroll
-          for (int rh = 0; rh < 2; ++rh) {
-            if (!kFp4 || upd[rh]) {
-              const float m_use = m[rh] == -INFINITY ? 0.0f : m[rh];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
-            }
-          }
+          for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
         }
 #pragma unroll
         for (int rh = 0; rh < 2; ++rh) {
@@ -737,15 +664,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh) {
             const int rl = rb * 32 + 16 * rh + l16;
-            if (th == 0) {
-              mt->alpha[rl] = alpha[rh];
-              mt->m[rl] = m[rh];
-            }
+            mt->m[th][rl] = m[rh];
             mt->l[th][rl] = l[rh];
           }
         }
-        const bool any_upd = __any(upd[0] || upd[1]);
-        if (th == 0 && lane == 0) mt->rescale[rb] = any_upd ? 1 : 0;
       }
       if constexpr (kFp4) {
         // Second half of P.V wave `wave`'s tokens of tile k+1 (its raw bytes
@@ -826,17 +748,47 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     floatx16 o[8];        // [rb * 4 + cb]
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+    // Scale of O (log2 domain) for rows lane % 32 of each row block: the
+    // largest reference of the halves applied so far in the segment.
+    float oref[2] = {-INFINITY, -INFINITY};
     // P.V of 16 tokens (k-step kk) of tile kt. All V fragments of the half
     // are requested before its first matrix op, so the reads overlap each
     // other instead of one LDS round trip per channel block.
-    auto pv_half = [&](int kt, int kk) {
+    // Before a half: O moves to the larger of its scale and the half's
+    // reference; a half whose reference is below O's scale (its partner
+    // jumped in this tile) has its probabilities scaled down to O's in
+    // registers (factor < 2^-kRescaleLog2; rare).
+    auto pv_half = [&](int kt, int kk, float r0, float r1) {
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
       bf16x8 a[4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
-      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
-      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+      bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
+      bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+      const float t0 = fmaxf(oref[0], r0), t1 = fmaxf(oref[1], r1);
+      const bool up0 = t0 != oref[0], up1 = t1 != oref[1];
+      if (__any(up0 || up1)) {
+        const float a0 = up0 ? __builtin_amdgcn_exp2f(oref[0] - t0) : 1.0f;
+        const float a1 = up1 ? __builtin_amdgcn_exp2f(oref[1] - t1) : 1.0f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          o[cb] *= a0;
+          o[4 + cb] *= a1;
+        }
+        oref[0] = t0;
+        oref[1] = t1;
+      }
+      const bool lo0 = r0 != -INFINITY && r0 < t0, lo1 = r1 != -INFINITY && r1 < t1;
+      if (__any(lo0 || lo1)) {
+        const float f0 = lo0 ? __builtin_amdgcn_exp2f(r0 - t0) : 1.0f;
+        const float f1 = lo1 ? __builtin_amdgcn_exp2f(r1 - t1) : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p0[e] = (__bf16)((float)p0[e] * f0);
+          p1[e] = (__bf16)((float)p1[e] * f1);
+        }
+      }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb], p0, o[cb], 0, 0, 0);
@@ -870,6 +822,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       stored = false;
       lds_barrier();  // step k
+      // References of both halves of tile k-1, read before the copies are
+      // issued so that their latency is covered.
+      float ref[2][2];
+      if (k > 0) {
+        const Meta* mt = metas + ((k + 1) & 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          ref[kk][0] = mt->m[kk][lane & 31];
+          ref[kk][1] = mt->m[kk][32 + (lane & 31)];
+        }
+      }
       if constexpr (kFp4) {
         // Raw tile k+3 goes to the slot tile k left (decoded in step k-1);
         // then the first half of this wave's tokens of tile k+1 is decoded
@@ -894,19 +857,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         bool bad = false;
         (void)tile_row0(p.cache, pc.b, pc.tile, bad);
         seg_bad |= bad ? 1 : 0;
-        const Meta* mt = metas + (kt & 1);
-        if (mt->rescale[0] | mt->rescale[1]) {
-          const float a0 = mt->alpha[lane & 31];
-          const float a1 = mt->alpha[32 + (lane & 31)];
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            o[cb] *= a0;
-            o[4 + cb] *= a1;
-          }
-        }
-        pv_half(kt, 0);
       }
-      pv_half(kt, 1);
+      pv_half(kt, 0, ref[0][0], ref[0][1]);
+      pv_half(kt, 1, ref[1][0], ref[1][1]);
 
       const int nt = tiles_of(pc.L);
       if (pc.tile == nt - 1 || k == count) {
@@ -926,8 +879,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         for (int rb = 0; rb < 2; ++rb) {
           const int row_local = rb * 32 + (lane & 31);
           const bool row_ok = g * kRowsPerGroup + row_local < p.HQ;
-          const float l = mt->l[0][row_local] + mt->l[1][row_local];
-          const float m = mt->m[row_local];
+          // Each half's sum, moved to O's scale (factors <= 1).
+          const float m = oref[rb];
+          float l = 0.0f;
+#pragma unroll
+          for (int th = 0; th < 2; ++th) {
+            const float mh = mt->m[th][row_local];
+            if (mh != -INFINITY) l += mt->l[th][row_local] * __builtin_amdgcn_exp2f(mh - m);
+          }
           const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
           float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
           if (seg_bad) lse_v = nanv;
@@ -988,6 +947,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = floatx16{};
+        oref[0] = oref[1] = -INFINITY;
         first_seg = false;
         seg_bad = 0;
         seg_lo = 0;
