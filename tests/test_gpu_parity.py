@@ -1,10 +1,12 @@
 """GPU parity of the HIP path against the fp64 oracle (through the C ABI).
 
 Reduced cases keep each workload's structure (dtype, paging, spikes, Q) at
-sizes the oracle evaluates in seconds, with several 64-token tiles and ragged
+sizes the oracle evaluates in seconds, with several 32-token tiles and ragged
 tails; full-size cases run the exact benchmark launch and compare sampled
 (sequence, head) pairs, which the oracle evaluates one by one.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -246,3 +248,79 @@ def test_decode_attn_up_equals_two_calls(name, lens, workgroups):
     assert torch.equal(x0.view(iv), x1.view(iv)), "x differs"
     assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "lse differs"
     T.assert_close(T.to64(u1), T.to64(u0), 1e-6 if dt == torch.float32 else 2e-3, "out (fused vs two calls)")
+
+
+# ---------------------------------------------------------------------------
+# Planted score jumps
+# ---------------------------------------------------------------------------
+
+# The latent rows of chosen tokens carry a multiple of a unit vector u that
+# every query row also carries (q_lat = 4u + noise), so those tokens' logits
+# sit at planted levels (log2 domain) above the rest. The plans put jumps of
+# more than 2^8 at the start of either 16-token half of a 32-token tile, with
+# and without the other half of the tile following, in a segment's first
+# tile, and up to 2^240 (earlier weights underflow in fp32); runs that fall
+# back below the top level keep a share of the weight. All inputs are
+# bf16-exact, so the reference is the fp64 softmax over exactly the values
+# the kernel reads.
+JUMP_PLANS = {
+    # seq: (length, [(first token, last token + 1, level)])
+    0: (700, [(100, 700, 12.0), (250, 700, 40.0), (301, 302, 60.0), (420, 700, 240.0), (520, 700, 236.0)]),
+    1: (333, [(17, 333, 200.0), (40, 41, 9.0)]),
+    2: (500, [(50, 500, 9.5), (130, 131, 20.0), (300, 500, 21.0)]),
+    3: (300, [(40, 60, 9.0)]),
+    4: (64, []),
+}
+
+
+def _jump_inputs(H=40, seed=11):
+    rng = np.random.default_rng(seed)
+    B, Ckv, Dr = len(JUMP_PLANS), 512, 64
+    scale = 1.0 / math.sqrt(192.0)
+    a = 4.0
+    per_unit = scale * math.log2(math.e) * a  # log2 level per unit of u in a latent row
+    bf = lambda t: torch.from_numpy(np.asarray(t, dtype=np.float32)).to(torch.bfloat16)  # noqa: E731
+    u = rng.standard_normal(Ckv)
+    u /= np.linalg.norm(u)
+    q_lat = bf(a * u + 0.05 * rng.standard_normal((B, H, 1, Ckv)))
+    q_pe = bf(0.05 * rng.standard_normal((B, H, 1, Dr)))
+    cap = max(n for n, _ in JUMP_PLANS.values())
+    lat = 0.3 * rng.standard_normal((B, cap, Ckv))
+    for b, (n, plan) in JUMP_PLANS.items():
+        lam = np.zeros(cap)
+        for t0, t1, level in plan:
+            lam[t0:t1] = level / per_unit
+        lat[b] += lam[:, None] * u[None, :]
+    lat = bf(lat)
+    rope = bf(0.3 * rng.standard_normal((B, cap, Dr)))
+    lens = torch.tensor([n for n, _ in JUMP_PLANS.values()], dtype=torch.int32)
+    return q_lat, q_pe, lat, rope, lens, scale, cap
+
+
+@pytest.mark.parametrize("workgroups", [0, 1, 7])
+def test_planted_score_jumps(workgroups):
+    from oracle import mla_ref
+    o = T.ops()
+    q_lat, q_pe, lat, rope, lens, scale, cap = _jump_inputs()
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    T.say(f"[case] planted jumps B={B} H={H} lens={lens.tolist()} workgroups={workgroups}")
+    buf = torch.cat([lat, rope], 2).reshape(B * cap, -1).cuda()
+    cache = o.LatentCache.combined(buf, 512, cap)
+    x = torch.empty(B, H, 1, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, 1, dtype=torch.float32, device="cuda")
+    o.mla_decode_attn(q_lat.cuda(), q_pe.cuda(), cache, lens.cuda(), int(lens.max()), scale, x, lse,
+                      workgroups=workgroups)
+    torch.cuda.synchronize()
+    xg, lg = T.to64(x), T.to64(lse)
+    for b in range(B):
+        n = int(lens[b])
+        xr = np.zeros((H, 512))
+        lr = np.zeros(H)
+        for h in range(H):
+            xr[h], lr[h] = mla_ref.attend_subset(q_lat[b, h, 0], q_pe[b, h, 0], lat[b, :n], rope[b, :n], scale,
+                                                 range(n))
+        T.assert_close(xg[b, :, 0], xr, T.TOL["bf16"], f"x (sequence {b})")
+        err = np.abs(lg[b, :, 0] - lr)
+        lim = 2e-3 + 1e-4 * np.abs(lr)
+        T.say(f"  lse (sequence {b}): max|err| = {err.max():.3e}")
+        assert np.all(err <= lim), f"lse (sequence {b})"
