@@ -858,8 +858,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         (void)tile_row0(p.cache, pc.b, pc.tile, bad);
         seg_bad |= bad ? 1 : 0;
       }
+      // bf16: the matrix ops of the P.V chain, which sets the step, go
+      // ahead of the score wave sharing the SIMD (FP4, whose score chain
+      // sets the step, keeps them behind it).
+      if constexpr (!kFp4) __builtin_amdgcn_s_setprio(2);
       pv_half(kt, 0, ref[0][0], ref[0][1]);
       pv_half(kt, 1, ref[1][0], ref[1][1]);
+      if constexpr (!kFp4) __builtin_amdgcn_s_setprio(0);
 
       const int nt = tiles_of(pc.L);
       if (pc.tile == nt - 1 || k == count) {
