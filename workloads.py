@@ -226,3 +226,15 @@ def reduced(w: Workload, B: int, lens: Sequence[int], seed: Optional[int] = None
     """A smaller workload with the same structure (for parity at oracle-friendly sizes)."""
     return w.with_(B=B, lens=tuple(int(x) for x in lens), lk=None, lk_range=None,
                    seed=w.seed if seed is None else seed)
+
+
+def rope_table(n_pos: int, d: int, base: float = 10000.0) -> torch.Tensor:
+    """A caller's cosine/sine table for the rotary embedding: fp32 [n_pos, d],
+    row p = [cos(p w_0) .. cos(p w_{d/2-1}), sin(p w_0) .. sin(p w_{d/2-1})]
+    with the usual schedule w_i = base^(-2i/d). The angles are formed in fp64
+    and the values rounded once to fp32; the library applies whatever table
+    it is given, so this is input data like any other."""
+    i = torch.arange(d // 2, dtype=torch.float64)
+    w = base ** (-2.0 * i / d)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * w[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], 1).to(torch.float32)
