@@ -463,6 +463,31 @@ def main():
             for j, k in enumerate(names):
                 in_step[k] += e[j].elapsed_time(e[j + 1]) / args.steps
 
+    # The append with the rotary embedding on the way in (mla_rope_append:
+    # the new RoPE keys turned to their positions and stored, the step's 128
+    # heads of q_pe turned in place, one pass) against the plain append
+    # (mla_cache_append); each as `steps` back-to-back calls between one pair
+    # of HIP events. The cos/sin table is input data (the usual 10000-base
+    # schedule, fp32); the rotation runs on a copy of q_pe.
+    rope_table = W.rope_table(max_len + 1, w.Dr).to(dev)
+    q_pe_rot = q_pe.clone()
+
+    def batched_ms(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    rope_ms = batched_ms(lambda i: ops.mla_rope_append(c_new, r_new, caches[i % ncopy], seq_lens, rope_table,
+                                                       q_pe=q_pe_rot, stream=stream))
+    plain_append_ms = batched_ms(lambda i: ops.mla_cache_append(c_new, r_new, caches[i % ncopy], seq_lens,
+                                                                stream=stream))
+
     # The attention call alone (attention kernel + merge), over the cache
     # copies in turn, on its stream: one pair of HIP events around `steps`
     # back-to-back calls gives the average (the host enqueues ahead, so no
@@ -557,6 +582,10 @@ def main():
                  "mfma_TFLOPs": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                  "kernel_source_hash": kernel_source_hash()},
         "calls_in_step": calls or None,
+        "rope_append": {"call": "mla_rope_append (k_pe rotated and appended, q_pe [B,128,1,64] rotated in place)",
+                        "ms": rope_ms, "plain_append_ms": plain_append_ms,
+                        "bytes": B * Q * (w.Ckv + w.Dr) * 2 * 2 + B * w.H * Q * w.Dr * 2 * 2 + B * Q * w.Dr * 4,
+                        "bound": "launch latency"},
         "workloads": others,
         "context": context,
         "cpu_baseline": cpu,

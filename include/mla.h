@@ -8,6 +8,8 @@
  *                     k_pe into the cache (contiguous or 64-token pages; an
  *                     FP4 latent cache is quantised on the way in)
  *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
+ *   mla_rope_append   mla_cache_append that first turns the new RoPE keys
+ *                     (and, in place, the step's q_pe) to their positions
  *   mla_append_absorb the two calls above in one launch (bf16)
  *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
  *                     up-projection in one kernel (bf16)
@@ -73,6 +75,10 @@ extern "C" {
 #define MLA_F32 0
 #define MLA_BF16 1
 #define MLA_FP4_E2M1_E4M3X16 2 /* latent only: 4-bit E2M1 codes + one E4M3 scale per 16 channels */
+
+/* Pairing of the rotary embedding (mla_rope_append). */
+#define MLA_ROPE_INTERLEAVED 0 /* pair i = elements (2i, 2i+1) */
+#define MLA_ROPE_HALVES 1      /* pair i = elements (i, i + Dr/2) */
 
 typedef struct mla_dims {
   int32_t batch;    /* B */
@@ -219,6 +225,36 @@ MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat
 MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                              const void* k_pe_new, const mla_kv_cache* cache,
                              const int32_t* seq_lens, void* stream);
+
+/*
+ * mla_rope_append -- mla_cache_append with the rotary position embedding
+ * applied on the way in, in the same pass (and, for an FP4 cache, the same
+ * quantisation of the latent). (Deep-dive page, forward_inference: the new
+ * token's RoPE key is the rotated projection, stored beside the latent;
+ * DeepSeek-V4.1-Flash course page, block 4A: rotation by the cosine and sine
+ * of the position's angle, checked by hand on a few elements.)
+ *   k_pe_new   [B, Q, Dr] RoPE key of the new tokens BEFORE rotation, in the
+ *              cache's rope dtype; stored rotated to the token's position
+ *              seq_lens[b] - Q + j.
+ *   q_pe       [B, H, Q, Dr] in the cache's rope dtype, or NULL: the step's
+ *              queries, rotated in place to the same positions (query j of a
+ *              sequence is its new token j). Rotated whether or not the
+ *              token's row lies inside the cache.
+ *   cos_sin    device fp32 [n_pos, Dr]: row p holds cos(a_{p,0..Dr/2-1})
+ *              then sin(a_{p,0..Dr/2-1}); the caller chooses the angles
+ *              (for example a_{p,i} = p * 10000^(-2i/Dr)).
+ *   style      MLA_ROPE_INTERLEAVED or MLA_ROPE_HALVES.
+ *   Pair i = (x, y) becomes (x cos a_i - y sin a_i, x sin a_i + y cos a_i),
+ *   computed in fp32 and rounded once (RNE) to the stored dtype. The latent
+ *   is stored exactly as mla_cache_append stores it. A position outside
+ *   [0, n_pos) (device data, not checkable on the host) gives NaN in that
+ *   token's rotated key and queries.
+ *   Errors: those of mla_cache_append; cos_sin NULL or n_pos <= 0 ->
+ *   MLA_ERR_INVALID_ARG; an unknown style -> MLA_ERR_UNSUPPORTED.
+ */
+MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
+                            void* q_pe, const float* cos_sin, int32_t n_pos, int32_t style,
+                            const mla_kv_cache* cache, const int32_t* seq_lens, void* stream);
 
 /*
  * mla_append_absorb -- mla_cache_append followed by mla_absorb_q, for a

@@ -15,6 +15,8 @@ MLA_ERR_HIP = -4
 MLA_F32 = 0
 MLA_BF16 = 1
 MLA_FP4_E2M1_E4M3X16 = 2
+MLA_ROPE_INTERLEAVED = 0
+MLA_ROPE_HALVES = 1
 
 EXPORTS = (
     "mla_absorb_q",
@@ -23,6 +25,7 @@ EXPORTS = (
     "mla_decode_attn_up",
     "mla_up_proj_v",
     "mla_cache_append",
+    "mla_rope_append",
     "mla_append_absorb",
     "mla_dequant_rows",
     "mla_status_string",
@@ -96,6 +99,9 @@ def load() -> ctypes.CDLL:
     lib.mla_up_proj_v.restype = ctypes.c_int
     lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P, P]
     lib.mla_cache_append.restype = ctypes.c_int
+    lib.mla_rope_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P, I32, I32, ctypes.POINTER(MlaKvCache),
+                                    P, P]
+    lib.mla_rope_append.restype = ctypes.c_int
     lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
                                       I32, P, P, P, P]
     lib.mla_append_absorb.restype = ctypes.c_int

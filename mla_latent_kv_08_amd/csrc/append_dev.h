@@ -9,6 +9,15 @@
 // RNE(fp32(amax / 6)), each channel the nearest E2M1 value of x/scale with
 // ties to the even code (DeepSeek-V4.1-Flash course page, block 4A: FP4 latent
 // with an E4M3 scale per 16 channels).
+//
+// With a cosine/sine table the RoPE key is turned to its position before it is
+// stored, and the step's queries (q_pe, the same positions) are turned in
+// place (deep-dive page, forward_inference: the new token's RoPE key is the
+// rotated projection; course page, block 4A: rotation by the cosine and sine
+// of the position's angle). Pair i of the Dr/2 pairs, (2i, 2i+1) interleaved
+// or (i, i + Dr/2) in halves, turns by angle a_i of the position's table row:
+// (x, y) -> (x cos a_i - y sin a_i, x sin a_i + y cos a_i) in fp32, rounded
+// once to the stored dtype. A position outside the table gives NaN.
 #pragma once
 
 #include "internal.h"
@@ -21,6 +30,87 @@ __device__ __forceinline__ float load_src(const void* base, int64_t idx, int dty
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
+__device__ __forceinline__ void store_dst(void* base, int64_t idx, int dtype, float v) {
+  if (dtype == MLA_F32) {
+    reinterpret_cast<float*>(base)[idx] = v;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// Elements of rotated pair i of a Dr-wide vector.
+__device__ __forceinline__ void rope_pair(const AppendParams& p, int i, int& i0, int& i1) {
+  if (p.rope_style == MLA_ROPE_INTERLEAVED) {
+    i0 = 2 * i;
+    i1 = 2 * i + 1;
+  } else {
+    i0 = i;
+    i1 = i + p.Dr / 2;
+  }
+}
+
+// Pair i of src (element offset `so`, dtype `sd`) turned to position `pos`,
+// stored to dst (offset `dof`, dtype `dd`); NaN outside the table.
+__device__ __forceinline__ void rope_rotate_pair(const AppendParams& p, int pos, int i, const void* src, int64_t so,
+                                                 int sd, void* dst, int64_t dof, int dd) {
+  int i0, i1;
+  rope_pair(p, i, i0, i1);
+  const float x = load_src(src, so + i0, sd);
+  const float y = load_src(src, so + i1, sd);
+  float c = __uint_as_float(0x7fc00000u), s = c;
+  if (pos >= 0 && pos < p.n_pos) {
+    const float* row = p.cos_sin + (int64_t)pos * p.Dr;
+    c = row[i];
+    s = row[p.Dr / 2 + i];
+  }
+  store_dst(dst, dof + i0, dd, __builtin_fmaf(x, c, -(y * s)));
+  store_dst(dst, dof + i1, dd, __builtin_fmaf(x, s, y * c));
+}
+
+// The step's queries q_pe [B, H, Qn, Dr], turned in place: one 64-lane wave
+// takes pairs 512 * chunk .. +511 of all B*H*Qn*Dr/2 pairs (row (b, h, j),
+// pair i), reads all of them before it writes any (the rotation is in place,
+// so loads could not otherwise move above earlier stores), whatever the cache
+// does with the token. Query j of sequence b has the position of new token j.
+constexpr int kRopePairsPerLane = 8;
+constexpr int kRopePairsPerChunk = 64 * kRopePairsPerLane;
+__device__ __forceinline__ void rope_queries(const AppendParams& p, int64_t chunk, int lane) {
+  const int half = p.Dr / 2;
+  const int64_t total = (int64_t)p.B * p.H * p.Qn * half;
+  float x[kRopePairsPerLane], y[kRopePairsPerLane], cs[kRopePairsPerLane], sn[kRopePairsPerLane];
+  int64_t o0[kRopePairsPerLane], o1[kRopePairsPerLane];
+  bool on[kRopePairsPerLane];
+#pragma unroll
+  for (int k = 0; k < kRopePairsPerLane; ++k) {
+    const int64_t t = chunk * kRopePairsPerChunk + lane + 64 * k;
+    on[k] = t < total;
+    const int64_t row = on[k] ? t / half : 0;
+    const int i = (int)(t - row * half);
+    int i0, i1;
+    rope_pair(p, on[k] ? i : 0, i0, i1);
+    o0[k] = row * p.Dr + i0;
+    o1[k] = row * p.Dr + i1;
+    const int b = (int)(row / ((int64_t)p.H * p.Qn));
+    const int j = (int)(row % p.Qn);
+    const int pos = p.seq_lens[b] - p.Qn + j;
+    x[k] = load_src(p.q_pe, o0[k], p.rope_dtype);
+    y[k] = load_src(p.q_pe, o1[k], p.rope_dtype);
+    cs[k] = __uint_as_float(0x7fc00000u);
+    sn[k] = cs[k];
+    if (pos >= 0 && pos < p.n_pos) {
+      const float* r = p.cos_sin + (int64_t)pos * p.Dr;
+      cs[k] = r[on[k] ? i : 0];
+      sn[k] = r[half + (on[k] ? i : 0)];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kRopePairsPerLane; ++k) {
+    if (!on[k]) continue;
+    store_dst(p.q_pe, o0[k], p.rope_dtype, __builtin_fmaf(x[k], cs[k], -(y[k] * sn[k])));
+    store_dst(p.q_pe, o1[k], p.rope_dtype, __builtin_fmaf(x[k], sn[k], y[k] * cs[k]));
+  }
+}
+
 // One 64-lane wave stores new token `token` (= b * Qn + j). The source row is
 // read into registers before the length (and the page table) is looked at, so
 // the row's load and the position lookup overlap instead of following each
@@ -31,7 +121,9 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
   const int j = token % p.Qn;
   const int64_t src_row = (int64_t)b * p.Qn + j;
   const CacheView& c = p.cache;
-  const int rope_words = p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
+  const bool rotate = p.cos_sin != nullptr;
+  // Words copied as they are (the RoPE key only when it is not rotated).
+  const int rope_words = rotate ? 0 : p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
   const bool fp4 = p.latent_dtype == MLA_FP4_E2M1_E4M3X16;
   const int lat_words = fp4 ? 0 : p.Ckv * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
   const uint32_t* __restrict__ src_pe = reinterpret_cast<const uint32_t*>(p.k_pe) + src_row * rope_words;
@@ -67,6 +159,12 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
       const int i = base + lane + 64 * k;
       if (i < rope_words) dst_pe[i] = v[k];
       else if (i < total) dst_lat[i - rope_words] = v[k];
+    }
+  }
+  if (rotate) {
+    for (int i = lane; i < p.Dr / 2; i += 64) {
+      rope_rotate_pair(p, pos, i, p.k_pe, src_row * p.Dr, p.rope_dtype, const_cast<uint8_t*>(c.rope) + r * c.rope_stride,
+                       0, p.rope_dtype);
     }
   }
   if (!fp4) return;

@@ -9,7 +9,16 @@ namespace mla {
 namespace {
 
 // grid (B * Qn); one 64-lane wave per new token.
-__global__ void __launch_bounds__(64) append_kernel(AppendParams p) { append_token(p, blockIdx.x, threadIdx.x); }
+// grid (B*Qn [+ query chunks]): block i < B*Qn stores new token i; the blocks
+// after them turn the step's queries (mla_rope_append with q_pe).
+__global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
+  const int n_tok = p.B * p.Qn;
+  if ((int)blockIdx.x < n_tok) {
+    append_token(p, blockIdx.x, threadIdx.x);
+  } else {
+    rope_queries(p, (int64_t)blockIdx.x - n_tok, threadIdx.x);
+  }
+}
 
 // grid (n); latent of physical row rows[i] as fp32.
 __global__ void __launch_bounds__(256) dequant_kernel(CacheView c, int latent_dtype, int Ckv,
@@ -39,8 +48,13 @@ __global__ void __launch_bounds__(256) dequant_kernel(CacheView c, int latent_dt
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
-  const int64_t n = (int64_t)p.B * p.Qn;
+  int64_t n = (int64_t)p.B * p.Qn;
   if (n == 0) return hipSuccess;
+  if (p.cos_sin != nullptr && p.q_pe != nullptr) {
+    const int64_t pairs = (int64_t)p.B * p.H * p.Qn * (p.Dr / 2);
+    n += (pairs + kRopePairsPerChunk - 1) / kRopePairsPerChunk;
+  }
+  if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)n), dim3(64), 0, s, p);
   return hipGetLastError();
 }

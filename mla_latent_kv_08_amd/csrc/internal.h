@@ -62,6 +62,12 @@ struct AppendParams {
   int src_dtype;     // MLA_F32 / MLA_BF16
   int latent_dtype;  // cache latent dtype
   int rope_dtype;
+  // Rotary embedding on the way in; null cos_sin: k_pe stored as given.
+  const float* cos_sin;  // [n_pos, Dr]: cosines of the Dr/2 angles, then their sines
+  int n_pos;
+  int rope_style;        // MLA_ROPE_INTERLEAVED / MLA_ROPE_HALVES
+  void* q_pe;            // [B, H, Qn, Dr] in the rope dtype, rotated in place; or null
+  int H;
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);

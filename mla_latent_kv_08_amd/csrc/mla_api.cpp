@@ -416,6 +416,25 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void
   return hip_status(mla::launch_append(p, static_cast<hipStream_t>(stream)));
 }
 
+MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
+                            void* q_pe, const float* cos_sin, int32_t n_pos, int32_t style,
+                            const mla_kv_cache* cache, const int32_t* seq_lens, void* stream) {
+  mla::AppendParams p{};
+  const int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &p);
+  if (st) return st;
+  if (cos_sin == nullptr || n_pos <= 0 || !aligned16(cos_sin)) return MLA_ERR_INVALID_ARG;
+  if (q_pe != nullptr && !aligned16(q_pe)) return MLA_ERR_INVALID_ARG;
+  if (style != MLA_ROPE_INTERLEAVED && style != MLA_ROPE_HALVES) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)dims->batch * dims->heads * dims->q_len * dims->d_rope > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  p.cos_sin = cos_sin;
+  p.n_pos = n_pos;
+  p.rope_style = style;
+  p.q_pe = q_pe;
+  p.H = dims->heads;
+  if (dims->batch == 0) return MLA_OK;
+  return hip_status(mla::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
 MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                               const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
                               int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,

@@ -13,11 +13,12 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLAError, MlaDecodeOpts, MlaDims,
-                   MlaKvCache)
+from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLA_ROPE_HALVES, MLA_ROPE_INTERLEAVED, MLAError,
+                   MlaDecodeOpts, MlaDims, MlaKvCache)
 
 __all__ = [
-    "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLAError", "LatentCache",
+    "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLA_ROPE_INTERLEAVED", "MLA_ROPE_HALVES", "MLAError",
+    "LatentCache", "mla_rope_append",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
@@ -226,6 +227,32 @@ def mla_cache_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: Late
     _lib.check(_lib.load().mla_cache_append(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new),
                                             _ptr(k_pe_new), ctypes.byref(desc), _ptr(seq_lens),
                                             _stream(stream)), "mla_cache_append")
+
+
+def mla_rope_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache, seq_lens: torch.Tensor,
+                    cos_sin: torch.Tensor, style: int = MLA_ROPE_INTERLEAVED, q_pe: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """mla_cache_append with k_pe_new (unrotated) turned to each token's position on the way in, and
+    q_pe [B, H, Qn, Dr] (optional) turned in place; cos_sin: fp32 [n_pos, Dr]. See mla_rope_append in
+    include/mla.h."""
+    B, Qn, Ckv = c_kv_new.shape
+    Dr = k_pe_new.shape[-1]
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != Dr:
+        raise TypeError("cos_sin must be float32 [n_pos, Dr]")
+    H = 1
+    if q_pe is not None:
+        if q_pe.shape[0] != B or q_pe.shape[2] != Qn or q_pe.shape[3] != Dr or q_pe.dtype != k_pe_new.dtype:
+            raise TypeError("q_pe must be [B, H, Qn, Dr] in the dtype of k_pe_new")
+        if not q_pe.is_contiguous():
+            raise TypeError("q_pe must be contiguous")
+        H = q_pe.shape[1]
+    d = _dims(B, H, Qn, 128, Dr, 128, Ckv)
+    desc = cache.desc()
+    _lib.check(_lib.load().mla_rope_append(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new), _ptr(k_pe_new),
+                                           _ptr(q_pe), _ptr(cos_sin), int(cos_sin.shape[0]), int(style),
+                                           ctypes.byref(desc), _ptr(seq_lens), _stream(stream)), "mla_rope_append")
 
 
 def mla_append_absorb(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache,
