@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -281,6 +282,71 @@ def measure_other_workloads(dev, stream, reps: int) -> dict:
     return out
 
 
+def measure_v4_form(dev, stream, reps: int) -> dict:
+    """The DeepSeek-V4.1-Flash form at the headline's cache size: 64 query heads over one bf16 latent
+    whose last 64 dims carry the rotation, B=32, Lk=4096, Q=1, two rotated cache copies (302 MB, past the
+    MALL). Each call alone and the chain of the three, back to back: mla_rope_append in latent-tail mode
+    (the step's new token and its 64 query rows), mla_decode_attn with an all-zero q_pe,
+    mla_sink_inverse_rope (sink column, x's tail turned back)."""
+    import torch
+    import workloads as W
+    from mla_latent_kv_08_amd import ops
+    print("bench: workload v4_form_bf16", file=sys.stderr, flush=True)
+    B, H, Q, L, C, R = 32, 64, 1, 4096, 512, 64
+    g = torch.Generator().manual_seed(5)
+    hist = torch.randn(B, L, C, generator=g).to(torch.bfloat16).to(dev)
+    sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    table = W.rope_table(L, R).to(dev)
+    caches = []
+    for _ in range(2):
+        buf = torch.zeros(B * L, C + R, dtype=torch.bfloat16, device=dev)
+        cache = ops.LatentCache.combined(buf, C, L)
+        ops.mla_rope_append(hist, None, cache, sl, table, latent_tail=True, stream=stream)
+        caches.append(cache)
+    new = hist[:, L - Q:].contiguous()
+    del hist
+    q = torch.randn(B, H, Q, C, generator=g).to(torch.bfloat16).to(dev)
+    zero_pe = torch.zeros(B, H, Q, R, dtype=torch.bfloat16, device=dev)
+    sinks = torch.randn(H, generator=g).to(dev)
+    x = torch.empty(B, H, Q, C, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, Q, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, ops.mla_decode_workspace_size(B, H, Q, ops.MLA_BF16, L)), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(C)
+
+    def rope(i):
+        ops.mla_rope_append(new, None, caches[i % 2], sl, table, q_pe=q, latent_tail=True, stream=stream)
+
+    def attn(i):
+        ops.mla_decode_attn(q, zero_pe, caches[i % 2], sl, L, scale, x, lse, workspace=ws, stream=stream)
+
+    def sink(i):
+        ops.mla_sink_inverse_rope(x, lse, sl, sinks, table, stream=stream)
+
+    def chain(i):
+        rope(i)
+        attn(i)
+        sink(i)
+
+    rec = {"B": B, "H": H, "Q": Q, "Lk": L, "cache": "contiguous, bf16 latent (tail rotated), zero RoPE slot"}
+    for name, fn in (("rope_append_ms", rope), ("attn_ms", attn), ("sink_inverse_rope_ms", sink),
+                     ("chain_ms", chain)):
+        rec[name] = time_back_to_back(fn, reps, stream)
+    if not torch.isfinite(x.float()).all():
+        raise SystemExit("v4_form_bf16: non-finite output")
+    cache_b = B * L * (C + R) * 2
+    io_b = B * H * Q * ((C + R) * 2 + C * 2 + 4)
+    flops = B * H * Q * L * 2 * (C + R + C)
+    t = rec["attn_ms"] / 1e3
+    t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
+    rec.update({"cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops, "kv_GBps": cache_b / t / 1e9,
+                "bound": "hbm", "t_roofline_us": t_hbm * 1e6, "roofline_frac": t_hbm / t,
+                "tokens_per_s": B * Q / (rec["chain_ms"] / 1e3)})
+    del caches, x, q
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def copy_gbps(dev, stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Device-to-device copy rate (bytes read + written per second) as context for the roofline."""
     import torch
@@ -472,21 +538,10 @@ def main():
     rope_table = W.rope_table(max_len + 1, w.Dr).to(dev)
     q_pe_rot = q_pe.clone()
 
-    def batched_ms(fn):
-        fn(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    rope_ms = batched_ms(lambda i: ops.mla_rope_append(c_new, r_new, caches[i % ncopy], seq_lens, rope_table,
-                                                       q_pe=q_pe_rot, stream=stream))
-    plain_append_ms = batched_ms(lambda i: ops.mla_cache_append(c_new, r_new, caches[i % ncopy], seq_lens,
-                                                                stream=stream))
+    rope_ms = time_back_to_back(lambda i: ops.mla_rope_append(c_new, r_new, caches[i % ncopy], seq_lens, rope_table,
+                                                              q_pe=q_pe_rot, stream=stream), args.steps, stream)
+    plain_append_ms = time_back_to_back(lambda i: ops.mla_cache_append(c_new, r_new, caches[i % ncopy], seq_lens,
+                                                                       stream=stream), args.steps, stream)
 
     # The attention call alone (attention kernel + merge), over the cache
     # copies in turn, on its stream: one pair of HIP events around `steps`
@@ -547,6 +602,7 @@ def main():
     others, context = None, None
     if not args.headline_only:
         others = measure_other_workloads(dev, stream, max(10, args.steps))
+        others["v4_form_bf16"] = measure_v4_form(dev, stream, max(10, args.steps))
         context = gpu_context(dev)
         context["copy_GBps"] = copy_gbps(dev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)

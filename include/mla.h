@@ -9,7 +9,10 @@
  *                     FP4 latent cache is quantised on the way in)
  *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
  *   mla_rope_append   mla_cache_append that first turns the new RoPE keys
- *                     (and, in place, the step's q_pe) to their positions
+ *                     (and, in place, the step's q_pe) to their positions;
+ *                     or, in the V4.1-Flash form, the latent's tail
+ *   mla_sink_inverse_rope the V4.1-Flash output side: sink column folded into
+ *                     x / lse, x's tail turned back
  *   mla_append_absorb the two calls above in one launch (bf16)
  *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
  *                     up-projection in one kernel (bf16)
@@ -79,6 +82,9 @@ extern "C" {
 /* Pairing of the rotary embedding (mla_rope_append). */
 #define MLA_ROPE_INTERLEAVED 0 /* pair i = elements (2i, 2i+1) */
 #define MLA_ROPE_HALVES 1      /* pair i = elements (i, i + Dr/2) */
+/* Flag added to the pairing: the rotated part is the last Dr dims of the
+ * latent (DeepSeek-V4.1-Flash form) instead of a separate RoPE key. */
+#define MLA_ROPE_LATENT_TAIL 2
 
 typedef struct mla_dims {
   int32_t batch;    /* B */
@@ -251,10 +257,46 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void
  *   token's rotated key and queries.
  *   Errors: those of mla_cache_append; cos_sin NULL or n_pos <= 0 ->
  *   MLA_ERR_INVALID_ARG; an unknown style -> MLA_ERR_UNSUPPORTED.
+ *
+ *   With MLA_ROPE_LATENT_TAIL in `style` (the DeepSeek-V4.1-Flash form,
+ *   course page block 4A: the rotary position sits on the tail of the latent,
+ *   which serves as key and value) the last Dr dims of each new latent are
+ *   turned instead, before an FP4 latent is quantised; k_pe_new may be NULL
+ *   and the row's RoPE slot is filled with zeros; `q_pe` is then the query
+ *   rows [B, H, Q, Ckv] (in the cache's rope dtype) whose last Dr dims are
+ *   turned in place. Attention over such a cache runs through
+ *   mla_decode_attn with an all-zero q_pe; mla_sink_inverse_rope finishes it.
+ *   A position outside the table gives the token's rotated tail NaN (FP4:
+ *   the E4M3 NaN scale on the groups it touches).
  */
 MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
                             void* q_pe, const float* cos_sin, int32_t n_pos, int32_t style,
                             const mla_kv_cache* cache, const int32_t* seq_lens, void* stream);
+
+/*
+ * mla_sink_inverse_rope -- the output side of the DeepSeek-V4.1-Flash form
+ * (course page, block 4A: attention with an attention-sink score column; the
+ * output's rotated part turned back before the output projection), applied
+ * in place to the x_lat / lse that mla_decode_attn wrote.
+ *   sinks    fp32 [H] or NULL: head h's sink logit, in the units of the
+ *            scaled scores; it enters the softmax normaliser and carries no
+ *            value, so lse <- log(exp(lse) + exp(sinks[h])) and
+ *            x <- x * exp(lse_old - lse_new) (a row with lse = -inf gets
+ *            lse = sinks[h] and keeps x = 0). Needs lse.
+ *   cos_sin  fp32 [n_pos, Dr] or NULL (no rotation): the last Dr dims of
+ *            every x row are turned back by the row's query position
+ *            seq_lens[b] - Q + q (table and pairing `style` as in
+ *            mla_rope_append, the sines negated). Needs seq_lens. A position
+ *            outside the table gives NaN in the row's tail.
+ *   dims     batch, heads, q_len, d_latent (the x row width, <= 8192) and
+ *            d_rope (the rotated tail width, even, <= d_latent); the other
+ *            fields are not used.
+ *   dtype    dtype of x_lat: MLA_BF16 or MLA_F32; fp32 arithmetic, one RNE
+ *            rounding at the end.
+ */
+MLA_API int mla_sink_inverse_rope(const mla_dims* dims, int32_t dtype, void* x_lat, float* lse, const float* sinks,
+                                  const float* cos_sin, int32_t n_pos, int32_t style, const int32_t* seq_lens,
+                                  void* stream);
 
 /*
  * mla_append_absorb -- mla_cache_append followed by mla_absorb_q, for a

@@ -17,6 +17,7 @@ MLA_BF16 = 1
 MLA_FP4_E2M1_E4M3X16 = 2
 MLA_ROPE_INTERLEAVED = 0
 MLA_ROPE_HALVES = 1
+MLA_ROPE_LATENT_TAIL = 2
 
 EXPORTS = (
     "mla_absorb_q",
@@ -26,6 +27,7 @@ EXPORTS = (
     "mla_up_proj_v",
     "mla_cache_append",
     "mla_rope_append",
+    "mla_sink_inverse_rope",
     "mla_append_absorb",
     "mla_dequant_rows",
     "mla_status_string",
@@ -102,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.mla_rope_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P, I32, I32, ctypes.POINTER(MlaKvCache),
                                     P, P]
     lib.mla_rope_append.restype = ctypes.c_int
+    lib.mla_sink_inverse_rope.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P, I32, I32, P, P]
+    lib.mla_sink_inverse_rope.restype = ctypes.c_int
     lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
                                       I32, P, P, P, P]
     lib.mla_append_absorb.restype = ctypes.c_int

@@ -18,6 +18,12 @@
 // or (i, i + Dr/2) in halves, turns by angle a_i of the position's table row:
 // (x, y) -> (x cos a_i - y sin a_i, x sin a_i + y cos a_i) in fp32, rounded
 // once to the stored dtype. A position outside the table gives NaN.
+//
+// Latent-tail mode (DeepSeek-V4.1-Flash course page, block 4A: the rotary
+// position sits on the tail of the latent, which serves as key and value):
+// the last Dr dims of the new latent are turned instead of a separate key,
+// before an FP4 latent is quantised; the row's RoPE slot is filled with zeros;
+// the query rows are [B, H, Qn, Ckv] with their last Dr dims turned.
 #pragma once
 
 #include "internal.h"
@@ -47,6 +53,36 @@ __device__ __forceinline__ void rope_pair(const AppendParams& p, int i, int& i0,
     i0 = i;
     i1 = i + p.Dr / 2;
   }
+}
+
+// Element u (< Dr) of the turned tail of the new latent row `src_row`: the
+// first or second output of its pair, from the source row (the pair's partner
+// may belong to another lane).
+__device__ __forceinline__ float tail_value(const AppendParams& p, int64_t src_row, int u, int pos) {
+  const int half = p.Dr / 2;
+  int i, first, second;
+  bool is_second;
+  if (p.rope_style == MLA_ROPE_INTERLEAVED) {
+    i = u >> 1;
+    is_second = u & 1;
+    first = 2 * i;
+    second = 2 * i + 1;
+  } else {
+    is_second = u >= half;
+    i = is_second ? u - half : u;
+    first = i;
+    second = i + half;
+  }
+  const int64_t base = src_row * p.Ckv + (p.Ckv - p.Dr);
+  const float x = load_src(p.c_kv, base + first, p.src_dtype);
+  const float y = load_src(p.c_kv, base + second, p.src_dtype);
+  float c = __uint_as_float(0x7fc00000u), s = c;
+  if (pos >= 0 && pos < p.n_pos) {
+    const float* row = p.cos_sin + (int64_t)pos * p.Dr;
+    c = row[i];
+    s = row[half + i];
+  }
+  return is_second ? __builtin_fmaf(x, s, y * c) : __builtin_fmaf(x, c, -(y * s));
 }
 
 // Pair i of src (element offset `so`, dtype `sd`) turned to position `pos`,
@@ -88,8 +124,8 @@ __device__ __forceinline__ void rope_queries(const AppendParams& p, int64_t chun
     const int i = (int)(t - row * half);
     int i0, i1;
     rope_pair(p, on[k] ? i : 0, i0, i1);
-    o0[k] = row * p.Dr + i0;
-    o1[k] = row * p.Dr + i1;
+    o0[k] = row * p.q_stride + p.q_off + i0;
+    o1[k] = row * p.q_stride + p.q_off + i1;
     const int b = (int)(row / ((int64_t)p.H * p.Qn));
     const int j = (int)(row % p.Qn);
     const int pos = p.seq_lens[b] - p.Qn + j;
@@ -122,12 +158,15 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
   const int64_t src_row = (int64_t)b * p.Qn + j;
   const CacheView& c = p.cache;
   const bool rotate = p.cos_sin != nullptr;
-  // Words copied as they are (the RoPE key only when it is not rotated).
+  const bool tail = rotate && p.rope_tail;
+  // Words copied as they are: the RoPE key only when it is not rotated; the
+  // latent, without its tail in latent-tail mode.
   const int rope_words = rotate ? 0 : p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
   const bool fp4 = p.latent_dtype == MLA_FP4_E2M1_E4M3X16;
-  const int lat_words = fp4 ? 0 : p.Ckv * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
+  const int lat_words = fp4 ? 0 : (tail ? p.Ckv - p.Dr : p.Ckv) * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
+  const int64_t lat_src_words = fp4 ? 0 : p.Ckv * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
   const uint32_t* __restrict__ src_pe = reinterpret_cast<const uint32_t*>(p.k_pe) + src_row * rope_words;
-  const uint32_t* __restrict__ src_lat = reinterpret_cast<const uint32_t*>(p.c_kv) + src_row * lat_words;
+  const uint32_t* __restrict__ src_lat = reinterpret_cast<const uint32_t*>(p.c_kv) + src_row * lat_src_words;
 
   // First pass of the row (RoPE words, then latent words) into registers.
   const int total = rope_words + lat_words;
@@ -161,10 +200,16 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
       else if (i < total) dst_lat[i - rope_words] = v[k];
     }
   }
-  if (rotate) {
+  if (rotate && !tail) {
     for (int i = lane; i < p.Dr / 2; i += 64) {
       rope_rotate_pair(p, pos, i, p.k_pe, src_row * p.Dr, p.rope_dtype, const_cast<uint8_t*>(c.rope) + r * c.rope_stride,
                        0, p.rope_dtype);
+    }
+  }
+  if (tail) {
+    for (int u = lane; u < p.Dr; u += 64) {
+      store_dst(const_cast<uint8_t*>(c.rope) + r * c.rope_stride, u, p.rope_dtype, 0.0f);
+      if (!fp4) store_dst(lat, (p.Ckv - p.Dr) + u, p.latent_dtype, tail_value(p, src_row, u, pos));
     }
   }
   if (!fp4) return;
@@ -174,16 +219,23 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
   for (int c0 = lane * 8; c0 < p.Ckv; c0 += 64 * 8) {
     float v[8];
     float amax = 0.0f;
+    int nan = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = load_src(p.c_kv, src_row * p.Ckv + c0 + e, p.src_dtype);
+      const int ch = c0 + e;
+      v[e] = tail && ch >= p.Ckv - p.Dr ? tail_value(p, src_row, ch - (p.Ckv - p.Dr), pos)
+                                        : load_src(p.c_kv, src_row * p.Ckv + ch, p.src_dtype);
       amax = fmaxf(amax, fabsf(v[e]));
+      nan |= v[e] != v[e] ? 1 : 0;
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    const uint32_t sc = e4m3_encode_rne(__fdiv_rn(amax, 6.0f));  // correctly rounded fp32 division
+    nan |= __shfl_xor(nan, 1, 64);
+    // (A NaN element, from a position outside the RoPE table, gives the
+    // group the E4M3 NaN scale, so the group decodes as NaN.)
+    const uint32_t sc = nan ? 0x7fu : e4m3_encode_rne(__fdiv_rn(amax, 6.0f));  // correctly rounded fp32 division
     const float s = e4m3_to_f32(sc);
     uint32_t word = 0;
-    if (s > 0.0f) {
+    if (!nan && s > 0.0f) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) word |= e2m1_encode(v[e], s) << (4 * e);
     }

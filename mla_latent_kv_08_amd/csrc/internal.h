@@ -66,9 +66,23 @@ struct AppendParams {
   const float* cos_sin;  // [n_pos, Dr]: cosines of the Dr/2 angles, then their sines
   int n_pos;
   int rope_style;        // MLA_ROPE_INTERLEAVED / MLA_ROPE_HALVES
-  void* q_pe;            // [B, H, Qn, Dr] in the rope dtype, rotated in place; or null
+  int rope_tail;         // 1: turn the last Dr latent dims (no separate key; its slot gets zeros)
+  void* q_pe;            // query rows in the rope dtype, rotated in place; or null
+  int q_stride, q_off;   // elements per query row, offset of its rotated part
   int H;
 };
+
+// mla_sink_inverse_rope: per (b, h, q) row of x [B, H, Q, Ckv], the sink
+// logit folded into x and lse, then the last Dr dims turned back.
+struct SinkParams {
+  void* x;
+  float* lse;
+  const float* sinks;    // [H] or null
+  const float* cos_sin;  // [n_pos, Dr] or null
+  const int32_t* seq_lens;
+  int B, H, Q, Ckv, Dr, n_pos, style, dtype;
+};
+hipError_t launch_sink_inverse_rope(const SinkParams& p, hipStream_t s);
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // Cache append and bf16 query absorption of one decode step in one launch.

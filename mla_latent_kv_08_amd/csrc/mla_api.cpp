@@ -373,12 +373,14 @@ namespace {
 
 // Checks of mla_cache_append; fills p.
 int prepare_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
-                   const mla_kv_cache* cache, const int32_t* seq_lens, mla::AppendParams* out) {
+                   const mla_kv_cache* cache, const int32_t* seq_lens, mla::AppendParams* out,
+                   bool pe_optional = false) {
   int st = check_dims(dims);
   if (st) return st;
   st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
   if (st) return st;
-  if (c_kv_new == nullptr || k_pe_new == nullptr || seq_lens == nullptr) return MLA_ERR_INVALID_ARG;
+  if (c_kv_new == nullptr || seq_lens == nullptr) return MLA_ERR_INVALID_ARG;
+  if (k_pe_new == nullptr && !pe_optional) return MLA_ERR_INVALID_ARG;
   if (!aligned16(c_kv_new) || !aligned16(k_pe_new)) return MLA_ERR_INVALID_ARG;
   if (src_dtype != MLA_F32 && src_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   if (cache->latent_dtype == MLA_FP4_E2M1_E4M3X16) {
@@ -419,20 +421,61 @@ MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void
 MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new, const void* k_pe_new,
                             void* q_pe, const float* cos_sin, int32_t n_pos, int32_t style,
                             const mla_kv_cache* cache, const int32_t* seq_lens, void* stream) {
+  if (style & ~(MLA_ROPE_HALVES | MLA_ROPE_LATENT_TAIL)) return MLA_ERR_UNSUPPORTED;
+  const bool tail = (style & MLA_ROPE_LATENT_TAIL) != 0;
   mla::AppendParams p{};
-  const int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &p);
+  const int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &p, tail);
   if (st) return st;
   if (cos_sin == nullptr || n_pos <= 0 || !aligned16(cos_sin)) return MLA_ERR_INVALID_ARG;
   if (q_pe != nullptr && !aligned16(q_pe)) return MLA_ERR_INVALID_ARG;
-  if (style != MLA_ROPE_INTERLEAVED && style != MLA_ROPE_HALVES) return MLA_ERR_UNSUPPORTED;
-  if ((int64_t)dims->batch * dims->heads * dims->q_len * dims->d_rope > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (dims->d_rope % 2 || dims->d_rope > dims->d_latent) return MLA_ERR_UNSUPPORTED;
+  const int q_stride = tail ? dims->d_latent : dims->d_rope;
+  if ((int64_t)dims->batch * dims->heads * dims->q_len * q_stride > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   p.cos_sin = cos_sin;
   p.n_pos = n_pos;
-  p.rope_style = style;
+  p.rope_style = style & MLA_ROPE_HALVES;
+  p.rope_tail = tail ? 1 : 0;
   p.q_pe = q_pe;
+  p.q_stride = q_stride;
+  p.q_off = tail ? dims->d_latent - dims->d_rope : 0;
   p.H = dims->heads;
   if (dims->batch == 0) return MLA_OK;
   return hip_status(mla::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+MLA_API int mla_sink_inverse_rope(const mla_dims* dims, int32_t dtype, void* x_lat, float* lse, const float* sinks,
+                                  const float* cos_sin, int32_t n_pos, int32_t style, const int32_t* seq_lens,
+                                  void* stream) {
+  if (dims == nullptr) return MLA_ERR_INVALID_ARG;
+  if (dims->batch < 0 || dims->heads <= 0 || dims->q_len <= 0 || dims->d_latent <= 0) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_BF16 && dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (dims->d_latent > 8192 || dims->d_latent % 8) return MLA_ERR_UNSUPPORTED;
+  if (x_lat == nullptr || !aligned16(x_lat)) return MLA_ERR_INVALID_ARG;
+  if (sinks != nullptr && (lse == nullptr || !aligned16(sinks) || !aligned16(lse))) return MLA_ERR_INVALID_ARG;
+  if (cos_sin != nullptr) {
+    if (n_pos <= 0 || seq_lens == nullptr || !aligned16(cos_sin)) return MLA_ERR_INVALID_ARG;
+    if (style != MLA_ROPE_INTERLEAVED && style != MLA_ROPE_HALVES) return MLA_ERR_UNSUPPORTED;
+    if (dims->d_rope <= 0 || dims->d_rope % 2 || dims->d_rope > dims->d_latent) return MLA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)dims->batch * dims->heads * dims->q_len * dims->d_latent > ((int64_t)1 << 40)) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (dims->batch == 0 || (sinks == nullptr && cos_sin == nullptr)) return MLA_OK;
+  mla::SinkParams p{};
+  p.x = x_lat;
+  p.lse = lse;
+  p.sinks = sinks;
+  p.cos_sin = cos_sin;
+  p.seq_lens = seq_lens;
+  p.B = dims->batch;
+  p.H = dims->heads;
+  p.Q = dims->q_len;
+  p.Ckv = dims->d_latent;
+  p.Dr = dims->d_rope;
+  p.n_pos = n_pos;
+  p.style = style;
+  p.dtype = dtype;
+  return hip_status(mla::launch_sink_inverse_rope(p, static_cast<hipStream_t>(stream)));
 }
 
 MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,

@@ -13,12 +13,12 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLA_ROPE_HALVES, MLA_ROPE_INTERLEAVED, MLAError,
-                   MlaDecodeOpts, MlaDims, MlaKvCache)
+from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLA_ROPE_HALVES, MLA_ROPE_INTERLEAVED,
+                   MLA_ROPE_LATENT_TAIL, MLAError, MlaDecodeOpts, MlaDims, MlaKvCache)
 
 __all__ = [
-    "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLA_ROPE_INTERLEAVED", "MLA_ROPE_HALVES", "MLAError",
-    "LatentCache", "mla_rope_append",
+    "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLA_ROPE_INTERLEAVED", "MLA_ROPE_HALVES",
+    "MLA_ROPE_LATENT_TAIL", "MLAError", "LatentCache", "mla_rope_append", "mla_sink_inverse_rope",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
@@ -229,30 +229,55 @@ def mla_cache_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: Late
                                             _stream(stream)), "mla_cache_append")
 
 
-def mla_rope_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache, seq_lens: torch.Tensor,
-                    cos_sin: torch.Tensor, style: int = MLA_ROPE_INTERLEAVED, q_pe: Optional[torch.Tensor] = None,
+def mla_rope_append(c_kv_new: torch.Tensor, k_pe_new: Optional[torch.Tensor], cache: LatentCache,
+                    seq_lens: torch.Tensor, cos_sin: torch.Tensor, style: int = MLA_ROPE_INTERLEAVED,
+                    q_pe: Optional[torch.Tensor] = None, latent_tail: bool = False, d_rope: int = 64,
                     stream=None) -> None:
     """mla_cache_append with k_pe_new (unrotated) turned to each token's position on the way in, and
-    q_pe [B, H, Qn, Dr] (optional) turned in place; cos_sin: fp32 [n_pos, Dr]. See mla_rope_append in
-    include/mla.h."""
+    q_pe [B, H, Qn, Dr] (optional) turned in place; cos_sin: fp32 [n_pos, Dr]. With latent_tail (the
+    V4.1-Flash form) the last d_rope dims of the latent are turned instead, k_pe_new may be None and q_pe
+    is the query rows [B, H, Qn, Ckv]. See mla_rope_append in include/mla.h."""
     B, Qn, Ckv = c_kv_new.shape
-    Dr = k_pe_new.shape[-1]
+    Dr = d_rope if latent_tail else k_pe_new.shape[-1]
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != Dr:
         raise TypeError("cos_sin must be float32 [n_pos, Dr]")
     H = 1
     if q_pe is not None:
-        if q_pe.shape[0] != B or q_pe.shape[2] != Qn or q_pe.shape[3] != Dr or q_pe.dtype != k_pe_new.dtype:
-            raise TypeError("q_pe must be [B, H, Qn, Dr] in the dtype of k_pe_new")
+        width = Ckv if latent_tail else Dr
+        if q_pe.dim() != 4 or q_pe.shape[0] != B or q_pe.shape[2] != Qn or q_pe.shape[3] != width:
+            raise TypeError(f"q_pe must be [B, H, Qn, {width}]")
         if not q_pe.is_contiguous():
             raise TypeError("q_pe must be contiguous")
         H = q_pe.shape[1]
     d = _dims(B, H, Qn, 128, Dr, 128, Ckv)
     desc = cache.desc()
+    st = int(style) | (MLA_ROPE_LATENT_TAIL if latent_tail else 0)
     _lib.check(_lib.load().mla_rope_append(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new), _ptr(k_pe_new),
-                                           _ptr(q_pe), _ptr(cos_sin), int(cos_sin.shape[0]), int(style),
+                                           _ptr(q_pe), _ptr(cos_sin), int(cos_sin.shape[0]), st,
                                            ctypes.byref(desc), _ptr(seq_lens), _stream(stream)), "mla_rope_append")
+
+
+def mla_sink_inverse_rope(x_lat: torch.Tensor, lse: Optional[torch.Tensor], seq_lens: Optional[torch.Tensor] = None,
+                          sinks: Optional[torch.Tensor] = None, cos_sin: Optional[torch.Tensor] = None,
+                          style: int = MLA_ROPE_INTERLEAVED, stream=None) -> None:
+    """In place on x_lat [B, H, Q, Ckv] / lse [B, H, Q]: fold per-head sink logits (fp32 [H]) into them,
+    then turn x's last cos_sin.shape[1] dims back by each query's position. See mla_sink_inverse_rope in
+    include/mla.h."""
+    B, H, Q, Ckv = x_lat.shape
+    Dr = cos_sin.shape[1] if cos_sin is not None else 0
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != H):
+        raise TypeError("sinks must be float32 [H]")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    if seq_lens is not None and seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    d = _dims(B, H, Q, 128, Dr, 128, Ckv)
+    n_pos = int(cos_sin.shape[0]) if cos_sin is not None else 0
+    _lib.check(_lib.load().mla_sink_inverse_rope(ctypes.byref(d), _code(x_lat), _ptr(x_lat), _ptr(lse), _ptr(sinks),
+                                                 _ptr(cos_sin), n_pos, int(style), _ptr(seq_lens), _stream(stream)),
+               "mla_sink_inverse_rope")
 
 
 def mla_append_absorb(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache,

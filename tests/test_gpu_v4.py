@@ -1,0 +1,125 @@
+"""GPU parity of the DeepSeek-V4.1-Flash form of latent attention against the
+fp64 reference oracle/v4_ref.py, through the C ABI: mla_rope_append in
+latent-tail mode (the cache and the query rows), mla_decode_attn with an
+all-zero q_pe, then mla_sink_inverse_rope (sink column and inverse rotation
+of x's tail)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import rope_ref as RR
+from oracle import v4_ref as V
+from tests import mla_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+CKV, DR = 512, 64
+
+
+def _inputs(B, H, Q, lens, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, Q, CKV, generator=g).to(dtype)
+    lat = [torch.randn(n, CKV, generator=g).to(dtype) for n in lens]
+    sinks = (2 * torch.randn(H, generator=g)).float()
+    return q, lat, sinks
+
+
+def _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups=0):
+    B, H = q.shape[0], q.shape[1]
+    cap = max(64, -(-max(lens) // 64) * 64)
+    buf = torch.zeros(B * cap, CKV + DR, dtype=dtype, device="cuda")
+    cache = o.LatentCache.combined(buf, CKV, cap)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    n = max(lens)
+    hist = torch.zeros(B, n, CKV, dtype=dtype)
+    for b, rows in enumerate(lat):
+        if len(rows):
+            hist[b, n - len(rows):] = rows
+    tab = table.cuda()
+    # Every token (right-aligned: token j of a length-L sequence lands at L - n + j).
+    o.mla_rope_append(hist.cuda(), None, cache, sl, tab, style=style, latent_tail=True)
+    # The step: its Q new tokens again (same rows, same values) and the query rows.
+    new = torch.stack([hist[b, n - Q:] for b in range(B)]).contiguous()
+    qg = q.cuda().contiguous()
+    o.mla_rope_append(new.cuda(), None, cache, sl, tab, style=style, q_pe=qg, latent_tail=True)
+    x = torch.empty(B, H, Q, CKV, dtype=dtype, device="cuda")
+    lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
+    zero_pe = torch.zeros(B, H, Q, DR, dtype=dtype, device="cuda")
+    scale = 1.0 / math.sqrt(CKV)
+    o.mla_decode_attn(qg, zero_pe, cache, sl, n, scale, x, lse, workgroups=workgroups)
+    o.mla_sink_inverse_rope(x, lse, sl, sinks.cuda(), tab, style)
+    torch.cuda.synchronize()
+    return x, lse, scale, buf
+
+
+@pytest.mark.parametrize("style", [RR.INTERLEAVED, RR.HALVES])
+@pytest.mark.parametrize("dtype,Q,workgroups", [(torch.bfloat16, 1, 0), (torch.bfloat16, 2, 7),
+                                                (torch.float32, 2, 0)])
+def test_v4_form_against_oracle(style, dtype, Q, workgroups):
+    o = T.ops()
+    B, H = 3, 64  # the V4.1-Flash form has 64 query heads over one latent
+    lens = [300, 2, 129]
+    q, lat, sinks = _inputs(B, H, Q, lens, dtype, seed=31 + Q)
+    table = W.rope_table(512, DR)
+    T.say(f"[case] v4 form style={style} dtype={dtype} Q={Q} lens={lens} workgroups={workgroups}")
+    x, lse, scale, _ = _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups)
+    ref = V.decode_v4(q.double().numpy(), [r.double().numpy() for r in lat], lens, table.double().numpy(), style,
+                      scale, sinks.double().numpy(), r=DR)
+    tol = T.TOL["f32" if dtype == torch.float32 else "bf16"]
+    T.assert_close(T.to64(x), ref["x"], tol, "x")
+    T.assert_lse_close(T.to64(lse), ref["lse"], tol)
+
+
+def test_v4_fp4_tail_quantises_the_rotated_latent():
+    # The FP4 cache in latent-tail mode holds exactly the codes and scales that
+    # quantising the fp32 latent-tail rows would give (same rotation, then the
+    # FP4 codec), and a zero RoPE slot.
+    o = T.ops()
+    B, n, cap = 2, 70, 128
+    lens = [70, 33]
+    g = torch.Generator().manual_seed(9)
+    hist = torch.randn(B, n, CKV, generator=g)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    table = W.rope_table(256, DR).cuda()
+    for style in (RR.INTERLEAVED, RR.HALVES):
+        f32 = torch.zeros(B * cap, CKV + DR, dtype=torch.float32, device="cuda")
+        o.mla_rope_append(hist.cuda(), None, o.LatentCache.combined(f32, CKV, cap), sl, table, style=style,
+                          latent_tail=True)
+        row_bytes = o.LatentCache.fp4_row_bytes(CKV, DR)
+        a = torch.zeros(B * cap, row_bytes, dtype=torch.uint8, device="cuda")
+        o.mla_rope_append(hist.cuda(), None, o.LatentCache.fp4(a, CKV, cap), sl, table, style=style,
+                          latent_tail=True)
+        # The rotated rows, read back, appended as they are into a second FP4 cache.
+        rot = torch.zeros(B, n, CKV, dtype=torch.float32, device="cuda")
+        for b in range(B):
+            rot[b, n - lens[b]:] = f32[b * cap: b * cap + lens[b], :CKV]
+        bref = torch.zeros_like(a)
+        o.mla_cache_append(rot, torch.zeros(B, n, DR, dtype=torch.bfloat16, device="cuda"),
+                           o.LatentCache.fp4(bref, CKV, cap), sl)
+        torch.cuda.synchronize()
+        assert torch.equal(a.cpu(), bref.cpu()), f"style {style}"
+        assert torch.all(f32[:, CKV:] == 0)
+
+
+def test_sink_inverse_rope_positions_outside_table_and_no_sink():
+    o = T.ops()
+    B, H, Q = 2, 4, 2
+    g = torch.Generator().manual_seed(13)
+    x0 = torch.randn(B, H, Q, CKV, generator=g).to(torch.bfloat16)
+    lse0 = torch.randn(B, H, Q, generator=g)
+    lens = [10, 40]  # positions [8, 9] and [38, 39]; the table has 39 rows
+    table = W.rope_table(39, DR)
+    x = x0.cuda()
+    lse = lse0.cuda()
+    o.mla_sink_inverse_rope(x, lse, torch.tensor(lens, dtype=torch.int32, device="cuda"), None, table.cuda(),
+                            RR.HALVES)
+    torch.cuda.synchronize()
+    xr = x.cpu().double().numpy()
+    assert torch.equal(lse.cpu(), lse0), "lse changes only with sinks"
+    assert np.isnan(xr[1, :, 1, -DR:]).all() and np.isfinite(xr[1, :, 1, :-DR]).all()
+    assert np.array_equal(xr[..., :-DR], x0.double().numpy()[..., :-DR]), "the head of x is untouched"
+    ref = V.rotate_tail(x0[0, :, 1].double().numpy(), table[9].double().numpy(), RR.HALVES, DR, inverse=True)
+    T.assert_close(xr[0, :, 1], ref, 1e-2, "tail turned back")
