@@ -77,3 +77,29 @@ def decode_v4(q, latent_rows, seq_lens, cos_sin, style: int, softmax_scale: floa
                 x[b, h, j] = rotate_tail(xv, table[pos], style, r, inverse=True)
                 lse[b, h, j] = m + np.log(den)
     return {"x": x, "lse": lse}
+
+
+def grouped_out_proj(x, w_o) -> np.ndarray:
+    """The grouped output projection that follows the V4.1-Flash form (course
+    page, block 4A: the head outputs go through W_O by groups, each group with
+    its own small matrix, the results joined into the hidden dimension; the
+    figure gives 8 groups x 1024). Readings: with G groups of H/G heads, group
+    g holds heads g*H/G .. (g+1)*H/G - 1; their rows (after the inverse
+    rotation) are joined head after head into one vector of (H/G)*C; W_O[g]
+    [N, (H/G)*C] maps it to hidden columns g*N .. g*N + N - 1.
+
+    x [B, H, Q, C]; w_o [G, N, (H/G)*C] -> out [B, Q, G*N], in fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_o, dtype=np.float64)
+    B, H, Q, C = x.shape
+    G, N, K = w.shape
+    if H % G or K != (H // G) * C:
+        raise ValueError("w_o must be [G, N, (H/G)*C] with G dividing H")
+    hg = H // G
+    out = np.zeros((B, Q, G * N))
+    for g in range(G):
+        # [B, Q, hg*C]: the group's heads joined, head after head.
+        xg = x[:, g * hg:(g + 1) * hg].transpose(0, 2, 1, 3).reshape(B, Q, hg * C)
+        out[:, :, g * N:(g + 1) * N] = xg @ w[g].T
+    return out

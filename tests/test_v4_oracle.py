@@ -90,3 +90,34 @@ def test_query_without_visible_token():
     np.testing.assert_array_equal(out["lse"][1, :, 1], sinks)
     none = V.decode_v4(q, lat, [1, 0], table, RR.INTERLEAVED, 0.2, None, r=RDIM)
     assert np.all(np.isneginf(none["lse"][1]))
+
+
+def test_grouped_out_proj_bruteforce_and_structure():
+    rng = np.random.default_rng(6)
+    B, H, Q, Cc, G, N = 2, 6, 2, 4, 3, 5
+    x = rng.standard_normal((B, H, Q, Cc))
+    w = rng.standard_normal((G, N, (H // G) * Cc))
+    out = V.grouped_out_proj(x, w)
+    # Scalar loops straight from the reading.
+    ref = np.zeros((B, Q, G * N))
+    for b in range(B):
+        for q in range(Q):
+            for g in range(G):
+                for n in range(N):
+                    acc = 0.0
+                    for j in range(H // G):
+                        for c in range(Cc):
+                            acc += w[g, n, j * Cc + c] * x[b, g * (H // G) + j, q, c]
+                    ref[b, q, g * N + n] = acc
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+    # A change to one group's heads moves only that group's columns.
+    x2 = x.copy()
+    x2[:, 2:4] += 1.0  # heads of group 1
+    d = V.grouped_out_proj(x2, w) - out
+    assert np.all(d[:, :, :N] == 0) and np.all(d[:, :, 2 * N:] == 0) and np.any(d[:, :, N:2 * N] != 0)
+    # A selector matrix returns the group's second head.
+    sel = np.zeros((G, Cc, (H // G) * Cc))
+    sel[:, :, Cc:2 * Cc] = np.eye(Cc)
+    s = V.grouped_out_proj(x, sel)
+    for g in range(G):
+        np.testing.assert_array_equal(s[:, :, g * Cc:(g + 1) * Cc], x[:, g * (H // G) + 1].transpose(0, 1, 2))
