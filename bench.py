@@ -287,7 +287,8 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
     whose last 64 dims carry the rotation, B=32, Lk=4096, Q=1, two rotated cache copies (302 MB, past the
     MALL). Each call alone and the chain of the three, back to back: mla_rope_append in latent-tail mode
     (the step's new token and its 64 query rows), mla_decode_attn with an all-zero q_pe,
-    mla_sink_inverse_rope (sink column, x's tail turned back)."""
+    mla_sink_inverse_rope (sink column, x's tail turned back), mla_grouped_out_proj (8 groups x 1024,
+    random bf16 W_O, 67 MB)."""
     import torch
     import workloads as W
     from mla_latent_kv_08_amd import ops
@@ -322,14 +323,22 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
     def sink(i):
         ops.mla_sink_inverse_rope(x, lse, sl, sinks, table, stream=stream)
 
+    G, N = 8, 1024
+    w_o = (torch.randn(G, N, (H // G) * C, generator=g) / 64.0).to(torch.bfloat16).to(dev)
+    hidden = torch.empty(B, Q, G * N, dtype=torch.bfloat16, device=dev)
+
+    def out_proj(i):
+        ops.mla_grouped_out_proj(x, w_o, hidden, stream=stream)
+
     def chain(i):
         rope(i)
         attn(i)
         sink(i)
+        out_proj(i)
 
     rec = {"B": B, "H": H, "Q": Q, "Lk": L, "cache": "contiguous, bf16 latent (tail rotated), zero RoPE slot"}
     for name, fn in (("rope_append_ms", rope), ("attn_ms", attn), ("sink_inverse_rope_ms", sink),
-                     ("chain_ms", chain)):
+                     ("grouped_out_proj_ms", out_proj), ("chain_ms", chain)):
         rec[name] = time_back_to_back(fn, reps, stream)
     if not torch.isfinite(x.float()).all():
         raise SystemExit("v4_form_bf16: non-finite output")
@@ -340,8 +349,10 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
     t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
     rec.update({"cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops, "kv_GBps": cache_b / t / 1e9,
                 "bound": "hbm", "t_roofline_us": t_hbm * 1e6, "roofline_frac": t_hbm / t,
-                "tokens_per_s": B * Q / (rec["chain_ms"] / 1e3)})
-    del caches, x, q
+                "tokens_per_s": B * Q / (rec["chain_ms"] / 1e3),
+                "grouped_out_proj": {"groups": G, "group_out": N, "weight_bytes": G * N * (H // G) * C * 2,
+                                     "GBps": G * N * (H // G) * C * 2 / (rec["grouped_out_proj_ms"] / 1e3) / 1e9}})
+    del caches, x, q, w_o, hidden
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec

@@ -13,6 +13,8 @@
  *                     or, in the V4.1-Flash form, the latent's tail
  *   mla_sink_inverse_rope the V4.1-Flash output side: sink column folded into
  *                     x / lse, x's tail turned back
+ *   mla_grouped_out_proj the V4.1-Flash grouped W_O (one matrix per group of
+ *                     heads, outputs joined into the hidden dimension)
  *   mla_append_absorb the two calls above in one launch (bf16)
  *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
  *                     up-projection in one kernel (bf16)
@@ -297,6 +299,24 @@ MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void*
 MLA_API int mla_sink_inverse_rope(const mla_dims* dims, int32_t dtype, void* x_lat, float* lse, const float* sinks,
                                   const float* cos_sin, int32_t n_pos, int32_t style, const int32_t* seq_lens,
                                   void* stream);
+
+/*
+ * mla_grouped_out_proj -- the grouped output projection that follows the
+ * DeepSeek-V4.1-Flash form (course page, block 4A: the head outputs go
+ * through W_O by groups, each group with its own small matrix, the results
+ * joined into the hidden dimension; the figure gives 8 groups x 1024).
+ *   out[b, q, g*N + n] = sum_{j < H/G, c < C} w_o[g, n, j*C + c] * x[b, g*H/G + j, q, c]
+ *   x      [B, H, Q, C] bf16 (C = dims->d_latent; the rows after
+ *          mla_sink_inverse_rope)
+ *   w_o    [G, N, (H/G)*C] bf16, G = groups, N = group_out
+ *   out    [B, Q, G*N] bf16
+ *   bf16 matrix ops with fp32 accumulation, one RNE rounding of the result.
+ *   Errors: MLA_ERR_UNSUPPORTED unless dtype == MLA_BF16, G divides H,
+ *   N is a multiple of 32, C a multiple of 16 and (H/G)*C a multiple of 1024;
+ *   MLA_ERR_INVALID_ARG for NULL / misaligned pointers or non-positive sizes.
+ */
+MLA_API int mla_grouped_out_proj(const mla_dims* dims, int32_t dtype, int32_t groups, int32_t group_out,
+                                 const void* x, const void* w_o, void* out, void* stream);
 
 /*
  * mla_append_absorb -- mla_cache_append followed by mla_absorb_q, for a

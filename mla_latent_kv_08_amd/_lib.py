@@ -28,6 +28,7 @@ EXPORTS = (
     "mla_cache_append",
     "mla_rope_append",
     "mla_sink_inverse_rope",
+    "mla_grouped_out_proj",
     "mla_append_absorb",
     "mla_dequant_rows",
     "mla_status_string",
@@ -106,6 +107,8 @@ def load() -> ctypes.CDLL:
     lib.mla_rope_append.restype = ctypes.c_int
     lib.mla_sink_inverse_rope.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P, I32, I32, P, P]
     lib.mla_sink_inverse_rope.restype = ctypes.c_int
+    lib.mla_grouped_out_proj.argtypes = [ctypes.POINTER(MlaDims), I32, I32, I32, P, P, P, P]
+    lib.mla_grouped_out_proj.restype = ctypes.c_int
     lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
                                       I32, P, P, P, P]
     lib.mla_append_absorb.restype = ctypes.c_int

@@ -84,6 +84,15 @@ struct SinkParams {
 };
 hipError_t launch_sink_inverse_rope(const SinkParams& p, hipStream_t s);
 
+// mla_grouped_out_proj: x [B, H, Q, C], w [G, N, (H/G)*C], out [B, Q, G*N], bf16.
+struct GroupOutParams {
+  const void* x;
+  const void* w;
+  void* out;
+  int B, H, Q, C, G, N;
+};
+hipError_t launch_grouped_out(const GroupOutParams& p, hipStream_t s);
+
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // Cache append and bf16 query absorption of one decode step in one launch.
 hipError_t launch_append_absorb_bf16(const ProjParams& p, const AppendParams& a, hipStream_t s);

@@ -478,6 +478,24 @@ MLA_API int mla_sink_inverse_rope(const mla_dims* dims, int32_t dtype, void* x_l
   return hip_status(mla::launch_sink_inverse_rope(p, static_cast<hipStream_t>(stream)));
 }
 
+MLA_API int mla_grouped_out_proj(const mla_dims* dims, int32_t dtype, int32_t groups, int32_t group_out,
+                                 const void* x, const void* w_o, void* out, void* stream) {
+  if (dims == nullptr) return MLA_ERR_INVALID_ARG;
+  if (dims->batch < 0 || dims->heads <= 0 || dims->q_len <= 0 || dims->d_latent <= 0) return MLA_ERR_INVALID_ARG;
+  if (groups <= 0 || group_out <= 0) return MLA_ERR_INVALID_ARG;
+  if (x == nullptr || w_o == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_o) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (dims->heads % groups || group_out % 32 || dims->d_latent % 16) return MLA_ERR_UNSUPPORTED;
+  const int64_t K = (int64_t)(dims->heads / groups) * dims->d_latent;
+  if (K % 1024 || K > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)dims->batch * dims->q_len * groups * group_out > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)groups * group_out * K > ((int64_t)1 << 40)) return MLA_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return MLA_OK;
+  mla::GroupOutParams p{x, w_o, out, dims->batch, dims->heads, dims->q_len, dims->d_latent, groups, group_out};
+  return hip_status(mla::launch_grouped_out(p, static_cast<hipStream_t>(stream)));
+}
+
 MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                               const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
                               int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,

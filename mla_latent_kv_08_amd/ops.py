@@ -19,6 +19,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLA_ROPE_HALVES, MLA
 __all__ = [
     "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLA_ROPE_INTERLEAVED", "MLA_ROPE_HALVES",
     "MLA_ROPE_LATENT_TAIL", "MLAError", "LatentCache", "mla_rope_append", "mla_sink_inverse_rope",
+    "mla_grouped_out_proj",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
@@ -309,3 +310,15 @@ def mla_dequant_rows(cache: LatentCache, rows: torch.Tensor, out: torch.Tensor, 
     _lib.check(_lib.load().mla_dequant_rows(ctypes.byref(desc), int(d_latent), _ptr(rows),
                                             int(rows.numel()), _ptr(out), _stream(stream)),
                "mla_dequant_rows")
+
+
+def mla_grouped_out_proj(x: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out [B, Q, G*N] = grouped W_O of x [B, H, Q, C] with w_o [G, N, (H/G)*C]; see mla_grouped_out_proj in
+    include/mla.h."""
+    B, H, Q, C = x.shape
+    G, N, _ = w_o.shape
+    if out.shape != (B, Q, G * N):
+        raise TypeError("out must be [B, Q, G*N]")
+    d = _dims(B, H, Q, 128, 64, 128, C)
+    _lib.check(_lib.load().mla_grouped_out_proj(ctypes.byref(d), _code(x), G, N, _ptr(x), _ptr(w_o), _ptr(out),
+                                                _stream(stream)), "mla_grouped_out_proj")

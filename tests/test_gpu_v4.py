@@ -123,3 +123,26 @@ def test_sink_inverse_rope_positions_outside_table_and_no_sink():
     assert np.array_equal(xr[..., :-DR], x0.double().numpy()[..., :-DR]), "the head of x is untouched"
     ref = V.rotate_tail(x0[0, :, 1].double().numpy(), table[9].double().numpy(), RR.HALVES, DR, inverse=True)
     T.assert_close(xr[0, :, 1], ref, 1e-2, "tail turned back")
+
+
+@pytest.mark.parametrize("B,H,Q,G,N", [(3, 64, 2, 8, 1024), (20, 16, 2, 4, 64)])
+def test_grouped_out_proj_against_oracle(B, H, Q, G, N):
+    o = T.ops()
+    g = torch.Generator().manual_seed(B * 100 + H)
+    x = torch.randn(B, H, Q, CKV, generator=g).to(torch.bfloat16)
+    w = (torch.randn(G, N, (H // G) * CKV, generator=g) / math.sqrt((H // G) * CKV)).to(torch.bfloat16)
+    T.say(f"[case] grouped W_O B={B} H={H} Q={Q} G={G} N={N}")
+    out = torch.full((B, Q, G * N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o.mla_grouped_out_proj(x.cuda(), w.cuda(), out)
+    torch.cuda.synchronize()
+    ref = V.grouped_out_proj(x.double().numpy(), w.double().numpy())
+    T.assert_close(T.to64(out), ref, T.TOL["bf16"], "grouped W_O")
+
+
+def test_grouped_out_proj_rejects_bad_shapes():
+    o = T.ops()
+    x = torch.zeros(1, 6, 1, CKV, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(4, 32, 1024, dtype=torch.bfloat16, device="cuda")  # 4 does not divide 6
+    out = torch.zeros(1, 1, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(o.MLAError):
+        o.mla_grouped_out_proj(x, w, out)
