@@ -540,20 +540,6 @@ def main():
             for j, k in enumerate(names):
                 in_step[k] += e[j].elapsed_time(e[j + 1]) / args.steps
 
-    # The append with the rotary embedding on the way in (mla_rope_append:
-    # the new RoPE keys turned to their positions and stored, the step's 128
-    # heads of q_pe turned in place, one pass) against the plain append
-    # (mla_cache_append); each as `steps` back-to-back calls between one pair
-    # of HIP events. The cos/sin table is input data (the usual 10000-base
-    # schedule, fp32); the rotation runs on a copy of q_pe.
-    rope_table = W.rope_table(max_len + 1, w.Dr).to(dev)
-    q_pe_rot = q_pe.clone()
-
-    rope_ms = time_back_to_back(lambda i: ops.mla_rope_append(c_new, r_new, caches[i % ncopy], seq_lens, rope_table,
-                                                              q_pe=q_pe_rot, stream=stream), args.steps, stream)
-    plain_append_ms = time_back_to_back(lambda i: ops.mla_cache_append(c_new, r_new, caches[i % ncopy], seq_lens,
-                                                                       stream=stream), args.steps, stream)
-
     # The attention call alone (attention kernel + merge), over the cache
     # copies in turn, on its stream: one pair of HIP events around `steps`
     # back-to-back calls gives the average (the host enqueues ahead, so no
@@ -586,6 +572,22 @@ def main():
     torch.cuda.synchronize()
     attn_ms = sorted(a.elapsed_time(b) for a, b in ev_attn)
     pct = lambda p: attn_ms[min(len(attn_ms) - 1, int(p * len(attn_ms)))]  # noqa: E731
+    # (Timed after the attention passes: 400 short launches before them would
+    # leave the clocks low for the batched attention timing.)
+    # The append with the rotary embedding on the way in (mla_rope_append:
+    # the new RoPE keys turned to their positions and stored, the step's 128
+    # heads of q_pe turned in place, one pass) against the plain append
+    # (mla_cache_append); each as `steps` back-to-back calls between one pair
+    # of HIP events. The cos/sin table is input data (the usual 10000-base
+    # schedule, fp32); the rotation runs on a copy of q_pe.
+    rope_table = W.rope_table(max_len + 1, w.Dr).to(dev)
+    q_pe_rot = q_pe.clone()
+
+    rope_ms = time_back_to_back(lambda i: ops.mla_rope_append(c_new, r_new, caches[i % ncopy], seq_lens, rope_table,
+                                                              q_pe=q_pe_rot, stream=stream), args.steps, stream)
+    plain_append_ms = time_back_to_back(lambda i: ops.mla_cache_append(c_new, r_new, caches[i % ncopy], seq_lens,
+                                                                       stream=stream), args.steps, stream)
+
     if not torch.isfinite(out.float()).all():
         print("non-finite output", file=sys.stderr)
         sys.exit(3)
