@@ -154,19 +154,25 @@ __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
   absorb_bf16_block(p, blockIdx.x, blockIdx.y * 128, lds);
 }
 
-// Cache append and query absorption of one decode step in one launch: blocks
-// 0 .. H*Ckv/128-1 absorb as above (head = block / (Ckv/128)), the blocks
-// after them store four new tokens each, one per wave.
+// Cache append and query absorption of one decode step in one launch: the
+// first ceil(B*Qn/4) blocks store four new tokens each, one per wave; the
+// blocks after them absorb as above (head = i / (Ckv/128) for absorb block i).
+// The append blocks come first so that they are dispatched with the absorb
+// blocks rather than after them: two absorb blocks fill a compute unit's
+// LDS, so blocks placed after all H*Ckv/128 absorb blocks wait for one of
+// those to finish.
 __global__ void __launch_bounds__(kThreads) append_absorb_bf16_kernel(ProjParams p, AppendParams a) {
   __shared__ __attribute__((aligned(16))) AbsorbLds lds;
   const int nc = p.Ckv / 128;
-  const int n_absorb = p.H * nc;
+  const int tokens = a.B * a.Qn;
+  const int n_append = (tokens + kThreads / 64 - 1) / (kThreads / 64);
   const int bid = blockIdx.x;
-  if (bid < n_absorb) {
-    absorb_bf16_block(p, bid / nc, (bid % nc) * 128, lds);
+  if (bid < n_append) {
+    const int token = bid * (kThreads / 64) + (int)(threadIdx.x >> 6);
+    if (token < tokens) append_token(a, token, threadIdx.x & 63);
   } else {
-    const int token = (bid - n_absorb) * (kThreads / 64) + (int)(threadIdx.x >> 6);
-    if (token < a.B * a.Qn) append_token(a, token, threadIdx.x & 63);
+    const int i = bid - n_append;
+    absorb_bf16_block(p, i / nc, (i % nc) * 128, lds);
   }
 }
 
