@@ -353,12 +353,13 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
                                float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
                                void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
                                void* stream) {
-  mla::AttnParams p{};
-  int st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat, lse,
-                          workspace, workspace_bytes, opts, &p);
-  if (st) return st;
+  // The up-projection's arguments first: they need no device query.
   mla::ProjParams u{};
-  st = prepare_up(dims, dtype, x_lat, wkv_b, out, &u);
+  int st = prepare_up(dims, dtype, x_lat, wkv_b, out, &u);
+  if (st) return st;
+  mla::AttnParams p{};
+  st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat, lse,
+                      workspace, workspace_bytes, opts, &p);
   if (st || p.B == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MLA_F32) {

@@ -117,3 +117,74 @@ def test_append_validation(lib):
                                 None) == E.MLA_ERR_UNSUPPORTED
     assert lib.mla_cache_append(byref(_dims(batch=0)), E.MLA_F32, P, P, byref(fp4), P, None) == E.MLA_OK
     assert lib.mla_dequant_rows(byref(c), 512, None, 4, P, None) == E.MLA_ERR_INVALID_ARG
+
+
+def test_rope_append_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+    c = _cache()
+
+    def call(dims=None, k_pe=P, q=None, cs=P, n_pos=4096, style=0):
+        return lib.mla_rope_append(byref(dims or _dims()), E.MLA_BF16, P, k_pe, q, cs, n_pos, style, byref(c), P,
+                                   None)
+    assert call(style=7) == E.MLA_ERR_UNSUPPORTED
+    assert call(style=4) == E.MLA_ERR_UNSUPPORTED
+    assert call(cs=None) == E.MLA_ERR_INVALID_ARG
+    assert call(n_pos=0) == E.MLA_ERR_INVALID_ARG
+    assert call(q=P + 4) == E.MLA_ERR_INVALID_ARG
+    assert call(k_pe=None) == E.MLA_ERR_INVALID_ARG  # a separate key is needed unless latent-tail
+    assert call(dims=_dims(batch=0), k_pe=None, style=E.MLA_ROPE_LATENT_TAIL) == E.MLA_OK
+    assert call(dims=_dims(batch=0), style=E.MLA_ROPE_HALVES) == E.MLA_OK
+
+
+def test_sink_inverse_rope_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+
+    def call(dims=None, dtype=E.MLA_BF16, x=P, lse=P, sinks=P, cs=P, n_pos=64, style=0, seq=P):
+        return lib.mla_sink_inverse_rope(byref(dims or _dims()), dtype, x, lse, sinks, cs, n_pos, style, seq, None)
+    assert call(dtype=E.MLA_FP4_E2M1_E4M3X16) == E.MLA_ERR_UNSUPPORTED
+    assert call(x=None) == E.MLA_ERR_INVALID_ARG
+    assert call(lse=None) == E.MLA_ERR_INVALID_ARG  # sinks need lse
+    assert call(seq=None) == E.MLA_ERR_INVALID_ARG  # the rotation needs positions
+    assert call(n_pos=0) == E.MLA_ERR_INVALID_ARG
+    assert call(style=2) == E.MLA_ERR_UNSUPPORTED
+    assert call(dims=_dims(d_rope=63)) == E.MLA_ERR_UNSUPPORTED
+    assert call(dims=_dims(d_latent=16384)) == E.MLA_ERR_UNSUPPORTED
+    assert call(dims=_dims(batch=0)) == E.MLA_OK
+    assert call(sinks=None, cs=None, lse=None, seq=None) == E.MLA_OK  # nothing to do
+
+
+def test_grouped_out_proj_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+
+    def call(dims=None, dtype=E.MLA_BF16, g=8, n=1024, x=P, w=P, out=P):
+        return lib.mla_grouped_out_proj(byref(dims or _dims(heads=64)), dtype, g, n, x, w, out, None)
+    assert call(dtype=E.MLA_F32) == E.MLA_ERR_UNSUPPORTED
+    assert call(g=6) == E.MLA_ERR_UNSUPPORTED   # does not divide 64 heads
+    assert call(n=48) == E.MLA_ERR_UNSUPPORTED  # not a multiple of 32
+    assert call(g=64) == E.MLA_ERR_UNSUPPORTED  # (H/G)*C = 512, not a multiple of 1024
+    assert call(g=0) == E.MLA_ERR_INVALID_ARG
+    assert call(w=None) == E.MLA_ERR_INVALID_ARG
+    assert call(out=P + 8) == E.MLA_ERR_INVALID_ARG
+    assert call(dims=_dims(heads=64, batch=0)) == E.MLA_OK
+
+
+def test_attn_up_and_append_absorb_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+    c = _cache()
+    d = _dims()
+
+    def up(wkv=P, out=P, dims=None):
+        return lib.mla_decode_attn_up(byref(dims or d), E.MLA_BF16, P, P, byref(c), P, 4096, 0.072, P, P, wkv, out,
+                                      P, 1 << 30, None, None)
+    assert up(wkv=None) == E.MLA_ERR_INVALID_ARG
+    assert up(out=None) == E.MLA_ERR_INVALID_ARG
+    assert up(dims=_dims(d_v=64)) == E.MLA_ERR_UNSUPPORTED
+    assert up(dims=_dims(batch=0)) == E.MLA_OK
+    assert lib.mla_append_absorb(byref(d), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, None, P, P,
+                                 None) == E.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb(byref(_dims(batch=0)), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, P, P, P,
+                                 None) == E.MLA_OK
