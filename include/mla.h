@@ -2,26 +2,32 @@
  * mla.h -- C ABI of an MI355X (gfx950) library for Multi-head Latent Attention
  * (MLA) decode with weight absorption.
  *
- * One decode step over a compressed latent cache is four calls:
+ * One decode step over a compressed latent cache is four calls, in order:
  *
- *   mla_cache_append  write the new tokens' latent c_kv and rotated RoPE key
- *                     k_pe into the cache (contiguous or 64-token pages; an
- *                     FP4 latent cache is quantised on the way in)
- *   mla_absorb_q      q_lat = W_UK^T q_nope per head (absorb W_UK into q)
- *   mla_rope_append   mla_cache_append that first turns the new RoPE keys
- *                     (and, in place, the step's q_pe) to their positions;
- *                     or, in the V4.1-Flash form, the latent's tail
- *   mla_sink_inverse_rope the V4.1-Flash output side: sink column folded into
- *                     x / lse, x's tail turned back
- *   mla_grouped_out_proj the V4.1-Flash grouped W_O (one matrix per group of
- *                     heads, outputs joined into the hidden dimension)
- *   mla_append_absorb the two calls above in one launch (bf16)
+ *   mla_cache_append   write the new tokens' latent c_kv and rotated RoPE key
+ *                      k_pe into the cache (contiguous or 64-token pages; an
+ *                      FP4 latent cache is quantised on the way in)
+ *   mla_absorb_q       q_lat = W_UK^T q_nope per head (absorb W_UK into q)
+ *   mla_decode_attn    scores q_lat.c + q_pe.k_pe, scale, causal mask,
+ *                      softmax, latent-weighted sum x (split over the tokens
+ *                      when that helps, merged with a log-sum-exp combine)
+ *   mla_up_proj_v      out = W_UV x per head
+ *
+ * Fused forms of the same step:
+ *   mla_append_absorb  mla_cache_append + mla_absorb_q in one launch (bf16)
  *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
- *                     up-projection in one kernel (bf16)
- *   mla_decode_attn   scores q_lat.c + q_pe.k_pe, scale, causal mask, softmax,
- *                     latent-weighted sum x (split over the tokens when that
- *                     helps, merged with a log-sum-exp combine)
- *   mla_up_proj_v     out = W_UV x per head
+ *                      up-projection in one kernel (bf16)
+ *
+ * Around the step:
+ *   mla_rope_append    mla_cache_append that first turns the new RoPE keys
+ *                      (and, in place, the step's q_pe) to their positions;
+ *                      or, in the DeepSeek-V4.1-Flash form, the latent's tail
+ *   mla_sink_inverse_rope  V4.1-Flash output side: the sink column folded
+ *                      into x / lse, x's tail turned back
+ *   mla_grouped_out_proj   V4.1-Flash grouped W_O (one matrix per group of
+ *                      heads, outputs joined into the hidden dimension)
+ *
+ * Helpers: mla_decode_workspace_size, mla_dequant_rows, mla_status_string.
  *
  * Sources of the operations: the "MLA decode step" exercise page (6547.cn):
  * the prose on the two score streams, scaling, masking and the low-rank
