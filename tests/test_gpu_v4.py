@@ -2,7 +2,8 @@
 fp64 reference oracle/v4_ref.py, through the C ABI: mla_rope_append in
 latent-tail mode (the cache and the query rows), mla_decode_attn with an
 all-zero q_pe, then mla_sink_inverse_rope (sink column and inverse rotation
-of x's tail)."""
+of x's tail); and of the grouped output projection that follows it
+(mla_grouped_out_proj against v4_ref.grouped_out_proj)."""
 import math
 
 import numpy as np
