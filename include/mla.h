@@ -18,6 +18,10 @@
  *   mla_decode_attn_up mla_decode_attn + mla_up_proj_v, the merge and the
  *                      up-projection in one kernel (bf16)
  *
+ * Many new tokens per sequence (prefill):
+ *   mla_prefill_attn   attention with K and V decompressed from the latent
+ *                      chunk by chunk on chip (bf16)
+ *
  * Around the step:
  *   mla_rope_append    mla_cache_append that first turns the new RoPE keys
  *                      (and, in place, the step's q_pe) to their positions;
@@ -213,6 +217,35 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
                                float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
                                void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
                                void* stream);
+
+/*
+ * mla_prefill_attn -- attention for many new tokens per sequence in the
+ * non-absorbed form: per chunk of 32 cached tokens the per-head keys
+ * K = C W_UK^T and values V = C W_UV^T are formed from the latent rows on
+ * chip and never written to memory (CANN fused-operator page, section 2: the
+ * chunk loop that up-projects K into local memory; exercise page: scores,
+ * scaling, causal mask, softmax, values).
+ *   For query row (b, h, q) with L = seq_lens[b] (the Q new tokens included),
+ *   the visible positions are t = 0 .. L-Q+q and
+ *     s_t  = softmax_scale * (q_nope[b,h,q,:] . K[t] + q_pe[b,h,q,:] . k_pe_t)
+ *     out  = sum_t softmax(s)_t * V[t]          -> out[b,h,q,:]
+ *     lse  = log sum_t exp(s_t) (natural log)   -> lse[b,h,q] (may be NULL)
+ *   with K[t] = W_UK[h] c_t and V[t] = W_UV[h] c_t. A row with no visible
+ *   position gets out = 0 and lse = -inf. The result equals mla_absorb_q +
+ *   mla_decode_attn + mla_up_proj_v up to rounding; this form pays off when
+ *   Q is large (each decompressed chunk serves 64 queries of a head).
+ *   dtype    MLA_BF16 only, DeepSeek dimensions (Dn = Vd = 128, Dr = 64,
+ *            Ckv = 512); fp32 accumulation, bf16 K, V and probabilities
+ *   q_nope   [B, H, Q, Dn];  q_pe [B, H, Q, Dr] (already rotated)
+ *   cache    bf16 latent and bf16 rope (contiguous or paged); any Q
+ *   wkv_b    [H, Dn+Vd, Ckv] bf16;  out [B, H, Q, Vd] bf16
+ *   A page index outside the cache turns the outputs of the blocks that read
+ *   it into NaN. Returns MLA_ERR_UNSUPPORTED for other dtypes or dimensions.
+ *   Device pointers; nothing is allocated; stream-ordered.
+ */
+MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* q_pe,
+                             const mla_kv_cache* cache, const int32_t* seq_lens, const void* wkv_b,
+                             float softmax_scale, void* out, float* lse, void* stream);
 
 /*
  * mla_up_proj_v -- out[b,h,q,v] = sum_c W_UV[h,v,c] * x_lat[b,h,q,c]

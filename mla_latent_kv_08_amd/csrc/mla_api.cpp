@@ -370,6 +370,41 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
   return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, &u, s));
 }
 
+MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* q_pe,
+                             const mla_kv_cache* cache, const int32_t* seq_lens, const void* wkv_b,
+                             float softmax_scale, void* out, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dtype != MLA_BF16 || !deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
+  if (cache == nullptr) return MLA_ERR_INVALID_ARG;
+  if (cache->latent_dtype != MLA_BF16 || cache->rope_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
+  if (st) return st;
+  if (q_nope == nullptr || q_pe == nullptr || seq_lens == nullptr || wkv_b == nullptr || out == nullptr) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(wkv_b) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL || dims->heads > 65535 ||
+      dims->batch > 65535) {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (dims->batch == 0) return MLA_OK;
+  mla::PrefillParams p{};
+  p.q_nope = q_nope;
+  p.q_pe = q_pe;
+  p.cache = view_of(cache);
+  p.seq_lens = seq_lens;
+  p.wkv_b = wkv_b;
+  p.out = out;
+  p.lse = lse;
+  p.B = dims->batch;
+  p.H = dims->heads;
+  p.Q = dims->q_len;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return hip_status(mla::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Checks of mla_cache_append; fills p.

@@ -19,7 +19,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FP4_E2M1_E4M3X16, MLA_ROPE_HALVES, MLA
 __all__ = [
     "MLA_F32", "MLA_BF16", "MLA_FP4_E2M1_E4M3X16", "MLA_ROPE_INTERLEAVED", "MLA_ROPE_HALVES",
     "MLA_ROPE_LATENT_TAIL", "MLAError", "LatentCache", "mla_rope_append", "mla_sink_inverse_rope",
-    "mla_grouped_out_proj",
+    "mla_grouped_out_proj", "mla_prefill_attn",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
@@ -177,6 +177,26 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
         int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
         "mla_decode_attn")
+
+
+def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache, seq_lens: torch.Tensor,
+                     wkv_b: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                     lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Non-absorbed attention with K and V formed from the latent on chip; see mla_prefill_attn in
+    include/mla.h."""
+    B, H, Q, Dn = q_nope.shape
+    Dr = q_pe.shape[-1]
+    Vd = out.shape[-1]
+    Ckv = wkv_b.shape[-1]
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    d = _dims(B, H, Q, Dn, Dr, Vd, Ckv)
+    desc = cache.desc()
+    _lib.check(_lib.load().mla_prefill_attn(
+        ctypes.byref(d), _code(q_nope), _ptr(q_nope), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
+        _ptr(wkv_b), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)), "mla_prefill_attn")
 
 
 def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,

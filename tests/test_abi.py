@@ -188,3 +188,22 @@ def test_attn_up_and_append_absorb_validation(lib):
                                  None) == E.MLA_ERR_INVALID_ARG
     assert lib.mla_append_absorb(byref(_dims(batch=0)), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, P, P, P,
                                  None) == E.MLA_OK
+
+
+def test_prefill_attn_validation(lib):
+    E = _lib
+    byref = ctypes.byref
+
+    def call(dims=None, dtype=E.MLA_BF16, cache=None, qn=P, qp=P, sl=P, wkv=P, out=P):
+        c = cache or _cache()
+        return lib.mla_prefill_attn(byref(dims or _dims(q_len=256)), dtype, qn, qp, byref(c), sl, wkv, 0.1, out,
+                                    None, None)
+    assert call(dtype=E.MLA_F32) == E.MLA_ERR_UNSUPPORTED
+    assert call(dims=_dims(q_len=256, d_v=64)) == E.MLA_ERR_UNSUPPORTED
+    assert call(cache=_cache(latent_dtype=E.MLA_F32, latent_stride=2048)) == E.MLA_ERR_UNSUPPORTED
+    assert call(dims=_dims(q_len=0)) == E.MLA_ERR_INVALID_ARG
+    assert call(wkv=None) == E.MLA_ERR_INVALID_ARG
+    assert call(out=P + 8) == E.MLA_ERR_INVALID_ARG
+    assert call(sl=None) == E.MLA_ERR_INVALID_ARG
+    assert call(cache=_cache(num_rows=100)) == E.MLA_ERR_INVALID_ARG  # 2 x 4096 rows do not fit
+    assert call(dims=_dims(q_len=256, batch=0)) == E.MLA_OK
