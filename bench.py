@@ -282,6 +282,49 @@ def measure_other_workloads(dev, stream, reps: int) -> dict:
     return out
 
 
+def measure_prefill(dev, stream, reps: int) -> dict:
+    """mla_prefill_attn (non-absorbed, K and V formed per 32-token chunk in LDS) at DeepSeek-V3 dimensions
+    (H=128, Dn=Vd=128, Dr=64, Ckv=512, bf16): chunked prefill, 64 new tokens on a 4096-token cache, B=8;
+    and a full prefill of 4096 tokens, B=1. alg_flops counts each head's K and V made once per token plus
+    the causal score and value products; exec_flops what the kernel issues (the chunks are decompressed
+    again for every 64-query tile)."""
+    import torch
+    from mla_latent_kv_08_amd import ops
+    out = {}
+    for name, B, Q, L, n in (("chunked_q64_lk4096_b8", 8, 64, 4096, reps), ("full_q4096_b1", 1, 4096, 4096, 3)):
+        print(f"bench: prefill {name}", file=sys.stderr, flush=True)
+        H, C, R, D = 128, 512, 64, 128
+        g = torch.Generator().manual_seed(11)
+        buf = torch.randn(B * L, C + R, generator=g).to(torch.bfloat16).to(dev)
+        cache = ops.LatentCache.combined(buf, C, L)
+        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        qn = torch.randn(B, H, Q, D, generator=g).to(torch.bfloat16).to(dev)
+        qp = torch.randn(B, H, Q, R, generator=g).to(torch.bfloat16).to(dev)
+        wkv = (torch.randn(H, 2 * D, C, generator=g) / math.sqrt(C)).to(torch.bfloat16).to(dev)
+        o = torch.empty(B, H, Q, D, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, H, Q, dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(D + R)
+        ms = time_back_to_back(lambda i: ops.mla_prefill_attn(qn, qp, cache, sl, wkv, scale, o, lse, stream=stream),
+                               n, stream)
+        if not torch.isfinite(o.float()).all():
+            raise SystemExit(f"prefill {name}: non-finite output")
+        pairs = sum(L - Q + q + 1 for q in range(Q))
+        alg = B * H * (L * 2 * D * C * 2 + pairs * (D + R + D) * 2)
+        tiles = 0
+        for q0 in range(0, Q, 64):
+            last = L - Q + min(q0 + 63, Q - 1)
+            tiles += last // 32 + 1
+        execf = B * H * tiles * (32 * 2 * D * C * 2 + 64 * 32 * (D + R + D) * 2)
+        t = ms / 1e3
+        out[name] = {"B": B, "H": H, "Q": Q, "Lk": L, "ms": ms, "alg_flops": alg, "exec_flops": execf,
+                     "alg_TFLOPs": alg / t / 1e12, "exec_TFLOPs": execf / t / 1e12,
+                     "mfma_frac_exec": execf / t / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        del buf, cache, qn, qp, wkv, o, lse
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_v4_form(dev, stream, reps: int) -> dict:
     """The DeepSeek-V4.1-Flash form at the headline's cache size: 64 query heads over one bf16 latent
     whose last 64 dims carry the rotation, B=32, Lk=4096, Q=1, two rotated cache copies (302 MB, past the
@@ -616,6 +659,7 @@ def main():
     if not args.headline_only:
         others = measure_other_workloads(dev, stream, max(10, args.steps))
         others["v4_form_bf16"] = measure_v4_form(dev, stream, max(10, args.steps))
+        others["prefill_bf16"] = measure_prefill(dev, stream, 20)
         context = gpu_context(dev)
         context["copy_GBps"] = copy_gbps(dev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)

@@ -37,8 +37,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 struct PrefillLds {
   uint16_t q[kPfQ * kKPitch];
-  uint16_t c[kPfT * kCPitch];
-  uint16_t k[kPfT * kKPitch];
+  uint16_t c[2][kPfT * kCPitch];
+  uint16_t k[2][kPfT * kKPitch];
   uint16_t vt[128 * kVPitch];
   uint16_t p[4][16 * kPPitch];
   int bad;
@@ -91,43 +91,61 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   // Tiles up to the last position any query of the block sees.
   const int pos_max = len - Q + min(q0 + kPfQ - 1, Q - 1);
   const int n_tiles = pos_max < 0 ? 0 : min(pos_max / kPfT + 1, (len + kPfT - 1) / kPfT);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int t0 = tile * kPfT;
-    __syncthreads();  // the previous tile's LDS is no longer read
-    // ---- 1. latent rows to LDS (4 chunks of 16 B per thread), RoPE keys to the key tile ----
+  // Tile i uses buffers i % 2 of the latent rows and the keys. Waves 4..7
+  // fetch tile i+1 into the other buffers while waves 0..3 run tile i's
+  // attention: chunk j < 8 of thread u = tid - 256 is latent row
+  // (u + 256j) / 64, 16-byte chunk (u + 256j) % 64; chunk 8 is RoPE row u / 8,
+  // chunk u % 8. Rows at or past len read as zeros.
+  const int u = tid - 256;
+  auto fetch = [&](int t0, int buf) {
+    // Three rounds of three loads, each stored before the next round: the
+    // loads of a round are in flight together without holding 36 registers.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int sidx = tid + kPfThreads * j;
-      const int row = sidx >> 6, ch = sidx & 63;
-      const int t = t0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < len) {
-        bool bad = false;
-        const int64_t r = phys_row(c, b, t, bad);
-        if (bad) {
-          s.bad = 1;
+    for (int j0 = 0; j0 < 9; j0 += 3) {
+      bf16x8 pf[3];
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) {
+        const int j = j0 + jj;
+        const int row = j < 8 ? (u + 256 * j) >> 6 : u >> 3;
+        const int t = t0 + row;
+        bf16x8 v = {};
+        if (t < len) {
+          bool bad = false;
+          const int64_t r = phys_row(c, b, t, bad);
+          if (bad) {
+            s.bad = 1;
+          } else if (j < 8) {
+            v = *reinterpret_cast<const bf16x8*>(c.latent + r * c.latent_stride + ((u + 256 * j) & 63) * 16);
+          } else {
+            v = *reinterpret_cast<const bf16x8*>(c.rope + r * c.rope_stride + (u & 7) * 16);
+          }
+        }
+        pf[jj] = v;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) {
+        const int j = j0 + jj;
+        const int sidx = u + 256 * j;
+        if (j < 8) {
+          *reinterpret_cast<bf16x8*>(&s.c[buf][(sidx >> 6) * kCPitch + (sidx & 63) * 8]) = pf[jj];
         } else {
-          v = *reinterpret_cast<const uint4*>(c.latent + r * c.latent_stride + ch * 16);
+          *reinterpret_cast<bf16x8*>(&s.k[buf][(u >> 3) * kKPitch + 128 + (u & 7) * 8]) = pf[jj];
         }
       }
-      *reinterpret_cast<uint4*>(&s.c[row * kCPitch + ch * 8]) = v;
     }
-    if (tid < kPfT * 8) {
-      const int row = tid >> 3, ch = tid & 7;
-      const int t = t0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < len) {
-        bool bad = false;
-        const int64_t r = phys_row(c, b, t, bad);
-        if (!bad) v = *reinterpret_cast<const uint4*>(c.rope + r * c.rope_stride + ch * 16);
-      }
-      *reinterpret_cast<uint4*>(&s.k[row * kKPitch + 128 + ch * 8]) = v;
-    }
+  };
+  __syncthreads();  // the flag is cleared before any fetch can set it
+  if (wave >= 4 && n_tiles > 0) fetch(0, 0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int t0 = tile * kPfT;
+    const int buf = tile & 1;
+    // Tile `tile` is in buffers `buf`; the previous tile's attention is done
+    // with the transposed values.
     __syncthreads();
     // ---- 2. decompress: D[token][n] = sum_k C[token][k] W[n][k] for this wave's 32 rows n ----
     {
       floatx16 acc = floatx16{};
-      const uint16_t* a = &s.c[(lane & 31) * kCPitch + 8 * hi];
+      const uint16_t* a = &s.c[buf][(lane & 31) * kCPitch + 8 * hi];
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0,
@@ -140,7 +158,7 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
       const int n = 32 * (wave & 3) + (lane & 31);
       if (wave < 4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s.k[(8 * (i >> 2) + 4 * hi + (i & 3)) * kKPitch + n] = to_bf16(acc[i]);
+        for (int i = 0; i < 16; ++i) s.k[buf][(8 * (i >> 2) + 4 * hi + (i & 3)) * kKPitch + n] = to_bf16(acc[i]);
       } else {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
@@ -150,14 +168,16 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
       }
     }
     __syncthreads();
-    // ---- 3. attention for 16 queries per wave (waves 0..3) ----
-    if (wave < 4) {
+    // ---- 3. attention for 16 queries per wave (waves 0..3); the next tile's fetch (4..7) ----
+    if (wave >= 4) {
+      if (tile + 1 < n_tiles) fetch(t0 + kPfT, buf ^ 1);
+    } else {
       floatx4 sc[2] = {floatx4{}, floatx4{}};
       // A lane l: query q0 + 16w + l%16, dims 32ks + 8(l/16) .. +7.
       const uint16_t* qr = &s.q[(16 * wave + l16) * kKPitch + 8 * g4];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const uint16_t* kr = &s.k[(16 * tb + l16) * kKPitch + 8 * g4];
+        const uint16_t* kr = &s.k[buf][(16 * tb + l16) * kKPitch + 8 * g4];
 #pragma unroll
         for (int ks = 0; ks < 6; ++ks) {
           sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qr + 32 * ks),
