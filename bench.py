@@ -442,6 +442,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (ragged paged, long context, FP4 MTP, tiny fp32) "
                          "and the context figures (copy rate, clocks)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time mla_prefill_attn (chunked and full prefill) and print that record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device-to-device copy of COPY_BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -464,6 +466,9 @@ def main():
     inp = W.generate(w)
     pl = W.place(inp)
     dev = torch.device("cuda", 0)
+    if args.prefill_only:
+        print(json.dumps({"prefill_bf16": measure_prefill(dev, torch.cuda.current_stream(dev), 20)}))
+        return
     torch.cuda.set_device(dev)
     B, H, Q = w.B, w.H, w.Q
     phys = W.combined_rows(inp.latent, inp.rope, pl, fill=0.0)
