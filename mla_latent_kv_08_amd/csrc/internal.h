@@ -93,22 +93,6 @@ struct GroupOutParams {
 };
 hipError_t launch_grouped_out(const GroupOutParams& p, hipStream_t s);
 
-// mla_prefill_attn (bf16, Dn = Vd = 128, Dr = 64, Ckv = 512): q_nope
-// [B, H, Q, 128], q_pe [B, H, Q, 64], wkv_b [H, 256, 512] -> out [B, H, Q, 128],
-// lse [B, H, Q] (natural log) or null.
-struct PrefillParams {
-  const void* q_nope;
-  const void* q_pe;
-  CacheView cache;
-  const int32_t* seq_lens;
-  const void* wkv_b;
-  void* out;
-  float* lse;
-  int B, H, Q;
-  float scale_log2;  // softmax_scale * log2(e)
-};
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
-
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // Cache append and bf16 query absorption of one decode step in one launch.
 hipError_t launch_append_absorb_bf16(const ProjParams& p, const AppendParams& a, hipStream_t s);

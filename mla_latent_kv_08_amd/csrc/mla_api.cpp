@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "internal.h"
+#include "prefill.h"
 #include "mla.h"
 
 namespace {

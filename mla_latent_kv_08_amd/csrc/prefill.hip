@@ -21,7 +21,7 @@
 // Query j of a sequence with `len` cached tokens (the Q new ones included) sees
 // positions 0 .. len - Q + j. A query that sees nothing gets out = 0 and
 // lse = -inf; a page index outside the cache makes the block's outputs NaN.
-#include "internal.h"
+#include "prefill.h"
 
 namespace mla {
 namespace {
