@@ -81,3 +81,17 @@ def test_prefill_bad_page_gives_nan_and_rejects_fp32():
     with pytest.raises(o.MLAError):
         o.mla_prefill_attn(case.q_nope.float(), case.q_pe.float(), cache, case.seq_lens, case.wkv_b.float(),
                            w.softmax_scale, out.float())
+
+
+@pytest.mark.parametrize("B,Q,L,heads,batch", [(8, 64, 4096, [0, 77], [0, 5]), (1, 4096, 4096, [3, 100], [0])])
+def test_prefill_full_size_sampled(B, Q, L, heads, batch):
+    # The two prefill shapes bench.py times (H = 128), in the same launch
+    # configuration; the oracle evaluates the sampled (sequence, head) pairs.
+    w = W.reduced(W.WORKLOADS["dsv3_bf16"], B, [L] * B, seed=900 + Q).with_(Q=Q)
+    inp = W.generate(w)
+    T.say(f"[case] prefill full size B={B} H={w.H} Q={Q} L={L} heads={heads} batch={batch}")
+    out, lse = _run(inp)
+    ref = T.oracle(inp, heads=heads, batch=batch)
+    got = T.to64(out[batch][:, heads])
+    T.assert_close(got, ref["out"], T.TOL["bf16"], "out")
+    T.assert_lse_close(T.to64(lse[batch][:, heads]), ref["lse"], T.TOL["bf16"])
