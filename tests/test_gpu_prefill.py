@@ -4,7 +4,8 @@ oracle mla_ref.decode_nonabsorbed, through the C ABI.
 
 Cases span several 64-query tiles with a ragged last one, several 32-token
 chunks with a ragged tail, sequences shorter than Q (leading queries that see
-nothing: out 0, lse -inf), Q = 1, the paged layout and the contiguous one."""
+nothing: out 0, lse -inf), Q = 1, the paged layout and the contiguous one; and, at the two sizes bench.py
+times, sampled (sequence, head) pairs."""
 import math
 
 import numpy as np
