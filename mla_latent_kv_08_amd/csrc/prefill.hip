@@ -94,45 +94,48 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   // Tile i uses buffers i % 2 of the latent rows and the keys. Waves 4..7
   // fetch tile i+1 into the other buffers while waves 0..3 run tile i's
   // attention: chunk j < 8 of thread u = tid - 256 is latent row
-  // (u + 256j) / 64, 16-byte chunk (u + 256j) % 64; chunk 8 is RoPE row u / 8,
-  // chunk u % 8. Rows at or past len read as zeros.
+  // u / 64 + 4j, 16-byte chunk u % 64; chunk 8 is RoPE row u / 8, chunk u % 8.
   const int u = tid - 256;
   auto fetch = [&](int t0, int buf) {
-    // Three rounds of three loads, each stored before the next round: the
-    // loads of a round are in flight together without holding 36 registers.
-#pragma unroll
-    for (int j0 = 0; j0 < 9; j0 += 3) {
-      bf16x8 pf[3];
-#pragma unroll
-      for (int jj = 0; jj < 3; ++jj) {
-        const int j = j0 + jj;
-        const int row = j < 8 ? (u + 256 * j) >> 6 : u >> 3;
-        const int t = t0 + row;
-        bf16x8 v = {};
-        if (t < len) {
-          bool bad = false;
-          const int64_t r = phys_row(c, b, t, bad);
-          if (bad) {
-            s.bad = 1;
-          } else if (j < 8) {
-            v = *reinterpret_cast<const bf16x8*>(c.latent + r * c.latent_stride + ((u + 256 * j) & 63) * 16);
-          } else {
-            v = *reinterpret_cast<const bf16x8*>(c.rope + r * c.rope_stride + (u & 7) * 16);
-          }
-        }
-        pf[jj] = v;
-      }
-#pragma unroll
-      for (int jj = 0; jj < 3; ++jj) {
-        const int j = j0 + jj;
-        const int sidx = u + 256 * j;
-        if (j < 8) {
-          *reinterpret_cast<bf16x8*>(&s.c[buf][(sidx >> 6) * kCPitch + (sidx & 63) * 8]) = pf[jj];
-        } else {
-          *reinterpret_cast<bf16x8*>(&s.k[buf][(u >> 3) * kKPitch + 128 + (u & 7) * 8]) = pf[jj];
-        }
-      }
+    // A 32-token tile lies inside one 64-token page: one page lookup and one
+    // bounds check per tile (the same for every thread). Rows past len are
+    // read at the last row (always in bounds) and replaced by zeros, so the
+    // nine loads carry no branches and are in flight together.
+    const int last = min(kPfT - 1, len - 1 - t0);
+    int64_t base;
+    bool bad = false;
+    if (c.page_size == 0) {
+      base = (int64_t)b * c.capacity + t0;
+    } else {
+      const int page = c.page_table[(int64_t)b * c.pt_stride + (t0 >> 6)];
+      base = (int64_t)page * 64 + (t0 & 63);
+      bad = page < 0 || base + last >= c.num_rows;
     }
+    bf16x8 pf[9];
+    if (bad) {
+      s.bad = 1;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) pf[j] = bf16x8{};
+    } else {
+      const uint8_t* lat = c.latent + (u & 63) * 16;
+      const int r0 = u >> 6;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pf[j] = *reinterpret_cast<const bf16x8*>(lat + (base + min(r0 + 4 * j, last)) * c.latent_stride);
+      }
+      pf[8] = *reinterpret_cast<const bf16x8*>(c.rope + (base + min(u >> 3, last)) * c.rope_stride + (u & 7) * 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (r0 + 4 * j > last) pf[j] = bf16x8{};
+      }
+      if ((u >> 3) > last) pf[8] = bf16x8{};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sidx = u + 256 * j;
+      *reinterpret_cast<bf16x8*>(&s.c[buf][(sidx >> 6) * kCPitch + (sidx & 63) * 8]) = pf[j];
+    }
+    *reinterpret_cast<bf16x8*>(&s.k[buf][(u >> 3) * kKPitch + 128 + (u & 7) * 8]) = pf[8];
   };
   __syncthreads();  // the flag is cleared before any fetch can set it
   if (wave >= 4 && n_tiles > 0) fetch(0, 0);
