@@ -191,7 +191,7 @@ def time_back_to_back(fn, n: int, stream) -> float:
     return e0.elapsed_time(e1) / n
 
 
-def setup_attn_case(w, dev, copies: int):
+def setup_attn_case(w, dev, copies: int, lo: bool = True):
     """Seeded inputs of workload w on the GPU: q_lat from mla_absorb_q, the cache in the
     workload's layout (paged ones with NaN in every unused row), outputs and workspace."""
     import torch
@@ -227,12 +227,13 @@ def setup_attn_case(w, dev, copies: int):
             caches.append(ops.LatentCache.fp4(buf.clone(), w.Ckv, pl.capacity, page_table=pt))
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     q_lat = torch.empty(w.B, w.H, w.Q, w.Ckv, dtype=dt, device=dev)
-    ops.mla_absorb_q(inp.q_nope.to(dev), inp.wkv_b.to(dev), q_lat)
+    q_lo = torch.empty_like(q_lat) if (lo and w.dtype != "f32") else None
+    ops.mla_absorb_q(inp.q_nope.to(dev), inp.wkv_b.to(dev), q_lat, q_lat_lo=q_lo)
     code = ops.MLA_F32 if w.dtype == "f32" else ops.MLA_BF16
     ws = ops.mla_decode_workspace_size(w.B, w.H, w.Q, code, max_len)
     torch.cuda.synchronize()
     return {"lens": lens, "caches": caches, "seq_lens": seq_lens, "max_len": max_len,
-            "q_lat": q_lat, "q_pe": inp.q_pe.to(dev), "x": torch.empty_like(q_lat),
+            "q_lat": q_lat, "q_lat_lo": q_lo, "q_pe": inp.q_pe.to(dev), "x": torch.empty_like(q_lat),
             "lse": torch.empty(w.B, w.H, w.Q, dtype=torch.float32, device=dev),
             "workspace": torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)}
 
@@ -243,7 +244,7 @@ def setup_attn_case(w, dev, copies: int):
 OTHER_WORKLOADS = {"tiny_f32": 1, "ragged_paged_bf16": 1, "long_splitkv_bf16": 1, "mtp_fp4": 2}
 
 
-def measure_other_workloads(dev, stream, reps: int) -> dict:
+def measure_other_workloads(dev, stream, reps: int, lo: bool = True) -> dict:
     import torch
     import workloads as W
     from mla_latent_kv_08_amd import ops
@@ -251,12 +252,13 @@ def measure_other_workloads(dev, stream, reps: int) -> dict:
     for name, copies in OTHER_WORKLOADS.items():
         w = W.WORKLOADS[name]
         print(f"bench: workload {name}", file=sys.stderr, flush=True)
-        case = setup_attn_case(w, dev, copies)
+        case = setup_attn_case(w, dev, copies, lo)
 
         def call(i, case=case, w=w):
             ops.mla_decode_attn(case["q_lat"], case["q_pe"], case["caches"][i % len(case["caches"])],
                                 case["seq_lens"], case["max_len"], w.softmax_scale, case["x"],
-                                case["lse"], workspace=case["workspace"], stream=stream)
+                                case["lse"], workspace=case["workspace"], q_lat_lo=case["q_lat_lo"],
+                                stream=stream)
 
         ms = time_back_to_back(call, reps, stream)
         if not torch.isfinite(case["x"].float()).all():
@@ -266,6 +268,7 @@ def measure_other_workloads(dev, stream, reps: int) -> dict:
         t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         rec = {"attn_avg_ms": ms, "B": w.B, "H": w.H, "Q": w.Q, "tokens": sum(case["lens"]),
+               "q_lat_lo": case["q_lat_lo"] is not None,
                "cache": ("paged 64-token pages" if w.paged else "contiguous") + f", {w.dtype} latent",
                "cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops,
                "kv_GBps": cache_b / t / 1e9, "mfma_TFLOPs": flops / t / 1e12}
@@ -432,6 +435,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (>= 3 defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workgroups", type=int, default=0)
+    ap.add_argument("--no-lo", action="store_true",
+                    help="scores against q_lat alone (rounded to bf16), without its low part q_lat_lo")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step (and the timed attention calls) from captured HIP "
                          "graphs instead of launching the calls one by one")
@@ -489,6 +494,7 @@ def main():
     c_new = inp.latent[last].reshape(B, 1, w.Ckv).contiguous().to(dev)
     r_new = inp.rope[last].reshape(B, 1, w.Dr).contiguous().to(dev)
     q_lat = torch.empty(B, H, Q, w.Ckv, dtype=torch.bfloat16, device=dev)
+    q_lo = None if args.no_lo else torch.empty_like(q_lat)
     x = torch.empty_like(q_lat)
     lse = torch.empty(B, H, Q, dtype=torch.float32, device=dev)
     out = torch.empty(B, H, Q, w.Vd, dtype=torch.bfloat16, device=dev)
@@ -506,21 +512,21 @@ def main():
 
     def attend(c, st):
         ops.mla_decode_attn(q_lat, q_pe, caches[c], seq_lens, max_len, w.softmax_scale, x, lse,
-                            workspace=workspace, workgroups=args.workgroups, stream=st)
+                            workspace=workspace, workgroups=args.workgroups, q_lat_lo=q_lo, stream=st)
 
     def append_absorb(c, st):
         if args.separate_append:
             ops.mla_cache_append(c_new, r_new, caches[c], seq_lens, stream=st)
-            ops.mla_absorb_q(q_nope, wkv_b, q_lat, stream=st)
+            ops.mla_absorb_q(q_nope, wkv_b, q_lat, q_lat_lo=q_lo, stream=st)
         else:
-            ops.mla_append_absorb(c_new, r_new, caches[c], seq_lens, q_nope, wkv_b, q_lat, stream=st)
+            ops.mla_append_absorb(c_new, r_new, caches[c], seq_lens, q_nope, wkv_b, q_lat, q_lat_lo=q_lo, stream=st)
 
     def up_proj(c, st):
         ops.mla_up_proj_v(x, wkv_b, out, stream=st)
 
     def attend_up(c, st):
         ops.mla_decode_attn_up(q_lat, q_pe, caches[c], seq_lens, max_len, w.softmax_scale, x, lse, wkv_b, out,
-                               workspace=workspace, workgroups=args.workgroups, stream=st)
+                               workspace=workspace, workgroups=args.workgroups, q_lat_lo=q_lo, stream=st)
 
     if args.separate_up:
         parts = (("append_absorb", append_absorb), ("attn", attend), ("up_proj", up_proj))
@@ -646,7 +652,8 @@ def main():
     # The projections against their own weight-bandwidth roofline (bf16 weights
     # read once, activations in and out once).
     wt = H * w.Dn * w.Ckv * 2
-    proj_bytes = {"append_absorb": wt + B * H * Q * (w.Dn + w.Ckv) * 2 + 2 * B * Q * (w.Ckv + w.Dr) * 2,
+    proj_bytes = {"append_absorb": wt + B * H * Q * (w.Dn + (1 if args.no_lo else 2) * w.Ckv) * 2
+                  + 2 * B * Q * (w.Ckv + w.Dr) * 2,
                   "up_proj": H * w.Vd * w.Ckv * 2 + B * H * Q * (w.Ckv + w.Vd) * 2}
     attn_s = attn_avg_ms / 1e3
     achieved_gbps = bytes_alg / attn_s / 1e9
@@ -662,7 +669,7 @@ def main():
             calls[k].update({"alg_bytes": proj_bytes[k], "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS})
     others, context = None, None
     if not args.headline_only:
-        others = measure_other_workloads(dev, stream, max(10, args.steps))
+        others = measure_other_workloads(dev, stream, max(10, args.steps), lo=not args.no_lo)
         others["v4_form_bf16"] = measure_v4_form(dev, stream, max(10, args.steps))
         others["prefill_bf16"] = measure_prefill(dev, stream, 20)
         context = gpu_context(dev)
@@ -689,7 +696,10 @@ def main():
                              + (", append and absorption as two calls" if args.separate_append
                                 else ", append fused into the absorption launch")
                              + (", attention and up-projection as two calls" if args.separate_up
-                                else ", split merge fused with the up-projection")},
+                                else ", split merge fused with the up-projection"),
+                   "scores": ("q_lat (bf16) only" if args.no_lo
+                              else "q_lat + q_lat_lo (bf16 high and low parts of the fp32 absorption)"),
+                   "inputs_sha256": inp.sha256()},
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},

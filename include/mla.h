@@ -161,13 +161,19 @@ typedef struct mla_decode_opts {
  * mla_absorb_q -- q_lat[b,h,q,:] = sum_d q_nope[b,h,q,d] * W_UK[h,d,:].
  * Absorbs W_UK into the query so scores are taken against the latent
  * directly (deep-dive page, forward_inference comment; exercise page step 1).
- *   dtype   MLA_F32 (all fp32) or MLA_BF16 (bf16 in/out, fp32 accumulation)
- *   q_nope  [B, H, Q, Dn]
- *   wkv_b   [H, Dn+Vd, Ckv]
- *   q_lat   [B, H, Q, Ckv] output
+ *   dtype     MLA_F32 (all fp32) or MLA_BF16 (bf16 in/out, fp32 accumulation)
+ *   q_nope    [B, H, Q, Dn]
+ *   wkv_b     [H, Dn+Vd, Ckv]
+ *   q_lat     [B, H, Q, Ckv] output: the fp32 sum rounded to the dtype
+ *   q_lat_lo  MLA_BF16 only, or NULL: [B, H, Q, Ckv] bf16 output, the
+ *             residual (fp32 sum - q_lat) rounded to bf16. q_lat + q_lat_lo
+ *             carries about 16 significant bits of the sum instead of 8;
+ *             passed to mla_decode_attn it keeps the score's rounding error
+ *             small where the latent rows are large. Non-NULL with MLA_F32:
+ *             MLA_ERR_UNSUPPORTED.
  */
 MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope,
-                         const void* wkv_b, void* q_lat, void* stream);
+                         const void* wkv_b, void* q_lat, void* q_lat_lo, void* stream);
 
 /*
  * Bytes of workspace mla_decode_attn needs for these arguments on the
@@ -191,13 +197,18 @@ MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32
  *                rope bf16; products on bf16 matrix cores, fp32 accumulation,
  *                probabilities rounded to bf16 before the weighted sum.
  *   q_lat        [B, H, Q, Ckv];  q_pe [B, H, Q, Dr]
+ *   q_lat_lo     MLA_BF16 only, or NULL: [B, H, Q, Ckv] bf16 low part of the
+ *                query (as mla_absorb_q writes it). The latent score stream
+ *                is then q_lat.c + q_lat_lo.c, both on the matrix cores with
+ *                one fp32 accumulation (twice the latent matrix work of the
+ *                score). Non-NULL with MLA_F32: MLA_ERR_UNSUPPORTED.
  *   seq_lens     device int32 [B]
  *   max_seq_len  host upper bound of seq_lens (sizes the token split)
  *   x_lat        [B, H, Q, Ckv] output;  lse: float [B, H, Q] output or NULL
  *   workspace    device scratch of mla_decode_workspace_size() bytes (its
  *                contents need no initialisation and are not preserved)
  */
-MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat,
+MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
                             const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
                             int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
                             void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
@@ -212,11 +223,11 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
  * reading x back; with MLA_F32 the two calls' kernels run one after the
  * other. Nothing is enqueued unless both argument sets pass their checks.
  */
-MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
-                               const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                               float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
-                               void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
-                               void* stream);
+MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
+                               const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
+                               int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
+                               const void* wkv_b, void* out, void* workspace, size_t workspace_bytes,
+                               const mla_decode_opts* opts, void* stream);
 
 /*
  * mla_prefill_attn -- attention for many new tokens per sequence in the
@@ -369,13 +380,18 @@ MLA_API int mla_grouped_out_proj(const mla_dims* dims, int32_t dtype, int32_t gr
 MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                               const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
                               int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
-                              void* stream);
+                              void* q_lat_lo, void* stream);
 
 /*
  * mla_dequant_rows -- inspection aid: the latent of `n` physical cache rows
- * (device int32 rows[n]) as fp32 [n, Ckv], decoded by the same device code
- * the attention kernel uses (FP4: E2M1 value times E4M3 scale; bf16/fp32:
- * widened). Lets a caller check the stored cache bit for bit.
+ * (device int32 rows[n]) as fp32 [n, Ckv]. An FP4 row is decoded by the
+ * device functions the attention kernel decodes its tiles with (the hardware
+ * E2M1 conversion at scale 1, one fp32 multiply by the E4M3 scale, the
+ * product kept as bf16, which holds it exactly; a NaN scale gives NaN); bf16
+ * and fp32 rows are widened. A row index outside [0, num_rows) gives NaN.
+ * Lets a caller check the stored cache bit for bit (DeepSeek-V4.1-Flash
+ * course page, block 4A, profiling checklist: check the FP4 dequant and the
+ * scale's channel order).
  */
 MLA_API int mla_dequant_rows(const mla_kv_cache* cache, int32_t d_latent, const int32_t* rows,
                              int32_t n, float* out, void* stream);

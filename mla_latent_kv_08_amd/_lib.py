@@ -85,17 +85,17 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     I32 = ctypes.c_int32
-    lib.mla_absorb_q.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P]
+    lib.mla_absorb_q.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P, P]
     lib.mla_absorb_q.restype = ctypes.c_int
     lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(MlaDims), I32, I32,
                                               ctypes.POINTER(MlaDecodeOpts),
                                               ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_decode_workspace_size.restype = ctypes.c_int
-    lib.mla_decode_attn.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
+    lib.mla_decode_attn.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, ctypes.POINTER(MlaKvCache), P,
                                     I32, ctypes.c_float, P, P, P, ctypes.c_size_t,
                                     ctypes.POINTER(MlaDecodeOpts), P]
     lib.mla_decode_attn.restype = ctypes.c_int
-    lib.mla_decode_attn_up.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
+    lib.mla_decode_attn_up.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, ctypes.POINTER(MlaKvCache), P,
                                        I32, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t,
                                        ctypes.POINTER(MlaDecodeOpts), P]
     lib.mla_decode_attn_up.restype = ctypes.c_int
@@ -114,7 +114,7 @@ def load() -> ctypes.CDLL:
                                      ctypes.c_float, P, P, P]
     lib.mla_prefill_attn.restype = ctypes.c_int
     lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
-                                      I32, P, P, P, P]
+                                      I32, P, P, P, P, P]
     lib.mla_append_absorb.restype = ctypes.c_int
     lib.mla_dequant_rows.argtypes = [ctypes.POINTER(MlaKvCache), I32, P, I32, P, P]
     lib.mla_dequant_rows.restype = ctypes.c_int

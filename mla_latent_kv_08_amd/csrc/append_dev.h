@@ -233,7 +233,7 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
     // (A NaN element, from a position outside the RoPE table, gives the
     // group the E4M3 NaN scale, so the group decodes as NaN.)
     const uint32_t sc = nan ? 0x7fu : e4m3_encode_rne(__fdiv_rn(amax, 6.0f));  // correctly rounded fp32 division
-    const float s = e4m3_to_f32(sc);
+    const float s = e4m3_value(sc);
     uint32_t word = 0;
     if (!nan && s > 0.0f) {
 #pragma unroll

@@ -13,26 +13,26 @@
 // Both contractions run on bf16 matrix ops with fp32 accumulation. The eight
 // waves of a workgroup are two per SIMD, one of each role on every SIMD, so
 // the matrix work and the softmax arithmetic are spread evenly:
-//   score waves 0..3   row block rb = wave / 2 (32 rows), token half
-//                      th = wave % 2 of the tile (16 tokens): query fragments
-//                      in registers, S^T by v_mfma_f32_16x16x32_bf16, the
-//                      softmax of those 32 rows x 16 tokens.
+//   score waves 0..3   query rows 16w .. 16w+15 of the group over the whole
+//                      tile (32 tokens): query fragments in registers, S^T by
+//                      v_mfma_f32_16x16x32_bf16, the softmax of those rows.
+//                      With the query's low part (q_lat_lo: q_lat = hi + lo,
+//                      both bf16) each K fragment also meets the low part,
+//                      so the latent score carries about 16 bits of q_lat.
 //   P.V waves 4..7     latent channels 128*cq .. +127 of all 64 rows (O^T in
 //                      registers, v_mfma_f32_32x32x16_bf16); each transposed
-//                      V fragment feeds both row blocks. They also start the
-//                      tile copies into LDS.
+//                      V fragment feeds both 32-row blocks. They also start
+//                      the tile copies into LDS.
 // One barrier starts step k. Score waves form S^T for tile k and write its
-// bf16 probabilities, their half's reference max and row sum; P.V waves
-// start the copy of tile k+2 and apply both halves of tile k-1. The two
-// halves of a row block need not wait for each other: each takes its
-// probabilities against its own reference max, which follows the partner's
-// from the step before and moves by itself only on a jump of more than 2^8,
-// and the P.V waves keep O at the largest reference applied so far.
+// bf16 probabilities, each row's reference max and row sum; P.V waves start
+// the copy of tile k+2 and apply tile k-1. A row's reference max moves only
+// on a jump of more than 2^8, and the P.V waves move O to it when it does.
 //
 // Tiles of 32 tokens (half a cache page) live in a ring of four LDS buffers:
 // the P.V tile, the score tile and two tiles in flight. bf16 rows are copied
-// straight into LDS by buffer loads with an LDS destination; an FP4 tile is
-// loaded into registers one step ahead and decoded to bf16 as it is written.
+// straight into LDS by buffer loads with an LDS destination; a raw FP4 tile
+// is copied into LDS three tiles ahead and decoded to bf16 in LDS one step
+// before the score waves need it.
 // Latent row t holds its 16-byte chunk c at slot c ^ swz(t), which keeps the
 // score reads (16 tokens, one chunk) and the transposed P.V reads (4 tokens,
 // 4 chunks) free of bank conflicts; the RoPE keys of 8 tokens form one
@@ -42,8 +42,8 @@
 // sequences, end to end, are dealt in equal contiguous runs to the W
 // workgroups of each row block. A run that covers a whole sequence writes x
 // and lse directly; a piece of a sequence is written as a partial (x_s
-// normalised, in bf16 like x itself; lse_s in fp32) and merged by the
-// combine kernel in fp32:
+// normalised and lse_s, both fp32, so that x is rounded to bf16 only once)
+// and merged by the combine kernel in fp32:
 //   lse = log sum_s exp(lse_s),  x = sum_s exp(lse_s - lse) x_s.
 #include "internal.h"
 
@@ -64,11 +64,11 @@ constexpr int kRawCodeBytes = kTile * 256;
 constexpr int kRawScaleBase = kRawCodeBytes;
 constexpr int kRawRopeBase = kRawScaleBase + kTile * 32;
 constexpr int kRawBytes = kRawRopeBase + kTile * 128;  // 13312
-// Per tile and token half th (log2 domain): the reference max the half's
-// probabilities were taken against, and the half's running sum relative to it.
+// Per tile (log2 domain): each row's reference max, which its probabilities
+// were taken against, and its running sum relative to that reference.
 struct Meta {
-  float m[2][kRowsPerGroup];
-  float l[2][kRowsPerGroup];
+  float m[kRowsPerGroup];
+  float l[kRowsPerGroup];
 };
 constexpr int kDmaPerWave = kTile / 4 + 1;             // bf16 loads per P.V wave and tile
 constexpr int kFp4DmaPerWave = 4;                      // FP4 loads per P.V wave and tile
@@ -311,30 +311,6 @@ __device__ __forceinline__ void fp4_copy_pieces(const Fp4Copy& f, const uint8_t*
   }
 }
 
-// Two codes (byte e of w) times scale s as two bf16. The hardware conversion
-// takes only the exponent of its scale, so it runs at scale 1 (exact E2M1
-// values, straight to fp32) and the E4M3 scale is applied in fp32; every
-// product of an E2M1 value and an E4M3 scale fits in bf16, so taking the high
-// halves is exact.
-template <int e>
-__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
-  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, e);
-  const float lo = r[0] * s;
-  const float hi = r[1] * s;
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// Value of an E4M3 ("FN") scale byte, without branches (lanes hold different
-// scales): subnormal m * 2^-9, normal (1 + m/8) * 2^(e-7), NaN for e=15, m=7.
-__device__ __forceinline__ float e4m3_value(uint32_t byte) {
-  const uint32_t e = (byte >> 3) & 0xfu, m = byte & 7u;
-  const float sub = (float)m * 0.001953125f;
-  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  float v = e == 0u ? sub : nrm;
-  v = (e == 15u && m == 7u) ? __uint_as_float(0x7fc00000u) : v;
-  return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
-}
-
 // Decode part h (tokens 8d + 4h .. +3) of P.V wave d's 8 tokens of a raw
 // tile into the bf16 tile (latent rows with the chunk swizzle, RoPE groups).
 // Lane i: code chunk u = i + 64h (token u / 16, 32 channels at 32 * (u % 16));
@@ -386,7 +362,7 @@ __device__ __forceinline__ float xor16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool kFp4>
+template <bool kFp4, bool kLo>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   using L = Lds<kFp4>;
   constexpr int kRing = L::kRing;
@@ -461,61 +437,71 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 
   if (is_score) {
     // ================= score waves: S^T, softmax, probabilities =================
+    // Score wave w owns query rows 16w .. 16w+15 of the group over the whole
+    // tile, so each row's max and sum stay inside one wave. Its rows are in
+    // P.V row block rb = w / 2, at rows 16 * (w % 2) + 0..15 of that block.
     const int rb = wave >> 1;
-    const int th = wave & 1;
     // 16x16 operand layouts: lane -> index l16 (token for K, row for Q) and
     // k group g4 (channels 8*g4 .. +7 of each 32-channel k-step).
     const int l16 = lane & 15, g4 = lane >> 4;
-    const bool rows_on = g * kRowsPerGroup + rb * 32 < p.HQ;  // uniform
-    // Rows of the two 16-row halves rh: rb*32 + 16*rh + l16. Rows past HQ
-    // compute on row 0's query and are never stored.
-    int row_c[2], qi[2];
+    const int rl = 16 * wave + l16;                                  // row in the group
+    const bool rows_on = g * kRowsPerGroup + 16 * wave < p.HQ;       // uniform
+    // Rows past HQ compute on row 0's query and are never stored.
+    const int row_c = g * kRowsPerGroup + rl < p.HQ ? g * kRowsPerGroup + rl : 0;
+    const int qi = row_c % p.Q;
+    // K reads (A operand) of token half th: token tq = 16*th + l16, chunk
+    // 4*ks + g4 of the latent row for ks < 16 (at k_off[th][ks % 4] +
+    // 256 * (ks / 4)), RoPE chunk 4*(ks-16) + g4 for ks = 16, 17 (at
+    // rope_off[th] + 512 * (ks - 16)).
+    int k_off[2][4], rope_off[2];
 #pragma unroll
-    for (int rh = 0; rh < 2; ++rh) {
-      const int row = g * kRowsPerGroup + rb * 32 + 16 * rh + l16;
-      row_c[rh] = row < p.HQ ? row : 0;
-      qi[rh] = row_c[rh] % p.Q;
+    for (int th = 0; th < 2; ++th) {
+      const int tq = kHalf * th + l16;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) k_off[th][b4] = tq * kLatRowBytes + (((4 * b4 + g4) ^ swz(tq)) << 4);
+      rope_off[th] = kRopeBase + (tq >> 3) * kRopeGroupBytes + g4 * 128 + (tq & 7) * 16;
     }
-    // K reads (A operand): token tq, chunk 4*ks + g4 of the latent row for
-    // ks < 16 (at k_off[ks % 4] + 256 * (ks / 4)), RoPE chunk 4*(ks-16) + g4
-    // for ks = 16, 17 (at rope_off + 512 * (ks - 16)).
-    const int tq = kHalf * th + l16;
-    int k_off[4];
-#pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) k_off[b4] = tq * kLatRowBytes + (((4 * b4 + g4) ^ swz(tq)) << 4);
-    const int rope_off = kRopeBase + (tq >> 3) * kRopeGroupBytes + g4 * 128 + (tq & 7) * 16;
 
     Cursor sc = cur;
-    // Query fragments (B operand): row half rh, channels 32*ks + 8*g4 .. +7 of
-    // [q_lat | q_pe]; from the staged rows at the run start, from global
-    // memory at a later sequence of the run.
-    bf16x8 qf[2][18];
-    auto load_q = [&](int b) {
+    // Query fragments (B operand): channels 32*ks + 8*g4 .. +7 of [q_lat | q_pe]
+    // (qh) and of the low part q_lat_lo (ql); from the staged rows at the run
+    // start (ql straight from global memory), from global memory at a later
+    // sequence of the run.
+    bf16x8 qh[18];
+    bf16x8 ql[kLo ? 16 : 1];
+    auto load_lo = [&](int b) {
+      if constexpr (kLo) {
+        const bf16x8* q = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat_lo) +
+                                                          ((int64_t)b * p.HQ + row_c) * 512 + 8 * g4);
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const int64_t grow = (int64_t)b * p.HQ + row_c[rh];
-        const bf16x8* ql = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
-                                                           grow * 512 + 8 * g4);
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
-                                                           grow * 64 + 8 * g4);
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qf[rh][ks] = ql[4 * ks];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qf[rh][16 + ks] = qp[4 * ks];
+        for (int ks = 0; ks < 16; ++ks) ql[ks] = q[4 * ks];
       }
     };
+    auto load_q = [&](int b) {
+      const int64_t grow = (int64_t)b * p.HQ + row_c;
+      const bf16x8* qa = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_lat) +
+                                                         grow * 512 + 8 * g4);
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(p.q_pe) +
+                                                         grow * 64 + 8 * g4);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qh[ks] = qa[4 * ks];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) qh[16 + ks] = qp[4 * ks];
+      load_lo(b);
+    };
+    if (rows_on) load_lo(cur.b);
     {
       // Score wave w copies latent rows 16w .. 16w+15 and RoPE chunks 2w,
       // 2w+1 of the group's query rows; rows past HQ read as zero.
       const int64_t grow0 = (int64_t)cur.b * p.HQ + g * kRowsPerGroup;
       const int nrows = min(kRowsPerGroup, p.HQ - g * kRowsPerGroup);
-      const int32x4_t ql =
+      const int32x4_t qa =
           buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_lat) + grow0 * kLatRowBytes, nrows * kLatRowBytes);
       const int32x4_t qp = buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_pe) + grow0 * 128, nrows * 128);
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const int r = 16 * wave + n;
-        lds_copy16(ql, lds_addr(smem + L::kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
+        lds_copy16(qa, lds_addr(smem + L::kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
       }
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
@@ -527,146 +513,120 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     lds_barrier();  // query rows staged
     if (rows_on) {
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const int r = rb * 32 + 16 * rh + l16;
+      for (int ks = 0; ks < 16; ++ks) {
+        qh[ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQBase + rl * kLatRowBytes +
+                                                  (((4 * ks + g4) ^ (rl & 15)) << 4));
+      }
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          qf[rh][ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQBase + r * kLatRowBytes +
-                                                         (((4 * ks + g4) ^ (r & 15)) << 4));
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          qf[rh][16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + r * 16);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        qh[16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + rl * 16);
       }
     }
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+    float m = -INFINITY, l = 0.0f;
     for (int k = 0; k <= count; ++k) {
       lds_barrier();  // step k
-      const bool active = rows_on && k < count;
-      floatx4 s[2];
-      float mx[2], esp[2][4];
-      float sc_c = 1.0f;
-      if (active) {
+      if (rows_on && k < count) {
         if (k == 0 || sc.tile == 0) {
           // New segment (sequence sc.b).
           if (k > 0) load_q(sc.b);
-          m[0] = m[1] = -INFINITY;
-          l[0] = l[1] = 0.0f;
+          m = -INFINITY;
+          l = 0.0f;
         }
         const uint8_t* tb = smem + (k % kRing) * kTileBytes;
 
-        // ---- S^T: this wave's 16 tokens x 32 rows (two 16x16 blocks) ----
+        // ---- S^T: 32 tokens (two 16-token halves) x this wave's 16 rows ----
         // The score chain (S, then the softmax) bounds the step; while its
         // matrix ops run, this wave issues ahead of the P.V wave sharing the
         // SIMD, whose matrix ops then fill the softmax phase.
+        floatx4 s[2];
         __builtin_amdgcn_s_setprio(2);
-        // Each K fragment feeds both row halves; even and odd k-steps
-        // accumulate separately so no matrix op waits on the one before.
         {
-          auto kaddr = [&](int ks) {
-            return ks < 16 ? tb + k_off[ks & 3] + 256 * (ks >> 2) : tb + rope_off + 512 * (ks - 16);
+          // Fragment f = 2*ks + th. Each K fragment feeds the high part of the
+          // query and, with the low part, a second matrix op; the four
+          // accumulators (th, part) take turns so no matrix op waits on the
+          // one before (without the low part, part = ks % 2).
+          auto kaddr = [&](int f) {
+            const int ks = f >> 1, th = f & 1;
+            return ks < 16 ? tb + k_off[th][ks & 3] + 256 * (ks >> 2) : tb + rope_off[th] + 512 * (ks - 16);
           };
-          constexpr int kAhead = 6;
+          constexpr int kF = 36;
+          constexpr int kAhead = 8;
           bf16x8 ka[kAhead];
 #pragma unroll
           for (int u = 0; u < kAhead; ++u) ka[u] = *reinterpret_cast<const bf16x8*>(kaddr(u));
           floatx4 acc[2][2];
 #pragma unroll
-          for (int rh = 0; rh < 2; ++rh) acc[rh][0] = acc[rh][1] = floatx4{};
+          for (int th = 0; th < 2; ++th) acc[th][0] = acc[th][1] = floatx4{};
 #pragma unroll
-          for (int ks = 0; ks < 18; ++ks) {
-            const bf16x8 a = ka[ks % kAhead];
-            acc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], acc[0][ks & 1], 0, 0, 0);
-            acc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], acc[1][ks & 1], 0, 0, 0);
-            if (ks + kAhead < 18) ka[ks % kAhead] = *reinterpret_cast<const bf16x8*>(kaddr(ks + kAhead));
+          for (int f = 0; f < kF; ++f) {
+            const int ks = f >> 1, th = f & 1;
+            const bf16x8 a = ka[f % kAhead];
+            if constexpr (kLo) {
+              acc[th][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], acc[th][0], 0, 0, 0);
+              if (ks < 16) acc[th][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], acc[th][1], 0, 0, 0);
+            } else {
+              acc[th][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], acc[th][ks & 1], 0, 0, 0);
+            }
+            if (f + kAhead < kF) ka[f % kAhead] = *reinterpret_cast<const bf16x8*>(kaddr(f + kAhead));
           }
           s[0] = acc[0][0] + acc[0][1];
           s[1] = acc[1][0] + acc[1][1];
-          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-          for (int ks = 0; ks < 18 - kAhead; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
         }
-
         __builtin_amdgcn_s_setprio(0);
 
-        // ---- scale, causal limit, row max over this half ----
-        // Lane holds rows rb*32 + 16*rh + l16, tokens tok0 + i (i < 4). Raw
-        // scores; with a positive scale and no masking the scale enters
-        // through the max and one fused multiply-add per exponent.
+        // ---- scale, causal limit, row max over the tile ----
+        // Lane holds row rl, tokens tok0 + 16*th + i (i < 4). Raw scores; with
+        // a positive scale and no masking the scale enters through the max
+        // and one fused multiply-add per exponent.
         const float c = p.scale_log2;
-        const int tok0 = sc.tile * kTile + kHalf * th + 4 * g4;
+        const int tok0 = sc.tile * kTile + 4 * g4;
         const bool whole_tile = c > 0.0f && (sc.tile + 1) * kTile <= sc.L - p.Q + 1;
-        sc_c = whole_tile ? c : 1.0f;
+        const float sc_c = whole_tile ? c : 1.0f;
+        if (!whole_tile) {
+          const int vis = sc.L - p.Q + qi + 1;  // the row sees tokens t < vis
 #pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          if (!whole_tile) {
-            const int vis = sc.L - p.Q + qi[rh] + 1;  // the row sees tokens t < vis
+          for (int th = 0; th < 2; ++th) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[rh][i] = tok0 + i < vis ? s[rh][i] * c : -INFINITY;
+            for (int i = 0; i < 4; ++i) s[th][i] = tok0 + kHalf * th + i < vis ? s[th][i] * c : -INFINITY;
           }
-          float v = fmaxf(fmaxf(s[rh][0], s[rh][1]), fmaxf(s[rh][2], s[rh][3]));
-          v = xor32_max(xor16_max(v));
-          mx[rh] = whole_tile ? v * c : v;
         }
-      }
-      if (active) {
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = xor32_max(xor16_max(mx));
+        if (whole_tile) mx *= c;
+
         // ---- online softmax in the log2 domain ----
-        // Each token half keeps its own reference max per row and takes its
-        // probabilities against it. The reference moves when the partner half
-        // had a larger one at the previous step (read here, with no wait: it
-        // was written before this step's barrier) or when this half's tile
-        // max exceeds it by more than kRescaleLog2, so p stays <= 2^kRescaleLog2
-        // and the references of the two halves part only for the step after
-        // one of them jumps. O keeps its own scale (see the P.V waves).
-        const bool seg_first = k == 0 || sc.tile == 0;
-        const Meta* prev = metas + ((k + 1) & 1);  // step k - 1
-        float alpha[2];
+        // The reference max moves only when the tile max exceeds it by more
+        // than kRescaleLog2, so p stays <= 2^kRescaleLog2 and O (kept by the
+        // P.V waves at the reference it was last moved to) is rarely rescaled.
+        const float m_new = mx > m + kRescaleLog2 ? mx : m;
+        const float alpha = m_new == m ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        float rs = 0.0f;
         bf16x4 pk[2];
 #pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          const int rl = rb * 32 + 16 * rh + l16;
-          const float pm = seg_first ? -INFINITY : prev->m[th ^ 1][rl];
-          const float ref = fmaxf(m[rh], pm);
-          const float m_new = mx[rh] > ref + kRescaleLog2 ? mx[rh] : ref;
-          alpha[rh] = m_new == m[rh] ? 1.0f : __builtin_amdgcn_exp2f(m[rh] - m_new);
-          m[rh] = m_new;
-          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) esp[rh][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][i], sc_c, -m_use));
-        }
-#pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          float rs = 0.0f;
+        for (int th = 0; th < 2; ++th) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = esp[rh][i];
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[th][i], sc_c, -m_use));
             rs += e;
-            pk[rh][i] = (__bf16)e;
+            pk[th][i] = (__bf16)e;
           }
-          l[rh] = l[rh] * alpha[rh] + xor32_sum(xor16_sum(rs));
         }
+        l = l * alpha + xor32_sum(xor16_sum(rs));
         // Probabilities in the P.V B-operand layout [rb][kk][lane]: k-step
-        // kk = th covers this half's tokens; lane L holds row L % 32, tokens
-        // 8 * (L / 32) .. +7, so this lane's 4 tokens go to lane
-        // 16*rh + l16 + 32*(g4 / 2) at element 4 * (g4 % 2).
-        uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048 + th * 1024 + 8 * (g4 & 1);
+        // kk = th covers that half's tokens; lane L holds row L % 32 of the
+        // block, tokens 8 * (L / 32) .. +7, so this lane's 4 tokens go to lane
+        // 16*(w % 2) + l16 + 32*(g4 / 2) at element 4 * (g4 % 2).
+        uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048 + 8 * (g4 & 1) +
+                      (16 * (wave & 1) + l16 + 32 * (g4 >> 1)) * 16;
 #pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          *reinterpret_cast<bf16x4*>(ps + (16 * rh + l16 + 32 * (g4 >> 1)) * 16) = pk[rh];
-        }
-        Meta* mt = metas + (k & 1);
+        for (int th = 0; th < 2; ++th) *reinterpret_cast<bf16x4*>(ps + th * 1024) = pk[th];
         if (g4 == 0) {
-#pragma unroll
-          for (int rh = 0; rh < 2; ++rh) {
-            const int rl = rb * 32 + 16 * rh + l16;
-            mt->m[th][rl] = m[rh];
-            mt->l[th][rl] = l[rh];
-          }
+          Meta* mt = metas + (k & 1);
+          mt->m[rl] = m;
+          mt->l[rl] = l;
         }
       }
       if constexpr (kFp4) {
@@ -749,44 +709,33 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = floatx16{};
     // Scale of O (log2 domain) for rows lane % 32 of each row block: the
-    // largest reference of the halves applied so far in the segment.
+    // reference it was last moved to in the segment.
     float oref[2] = {-INFINITY, -INFINITY};
     // P.V of 16 tokens (k-step kk) of tile kt. All V fragments of the half
     // are requested before its first matrix op, so the reads overlap each
-    // other instead of one LDS round trip per channel block.
-    // Before a half: O moves to the larger of its scale and the half's
-    // reference; a half whose reference is below O's scale (its partner
-    // jumped in this tile) has its probabilities scaled down to O's in
-    // registers (factor < 2^-kRescaleLog2; rare).
+    // other instead of one LDS round trip per channel block. Before the
+    // first half, O moves up to the tile's reference of each row (r0, r1:
+    // row blocks 0 and 1); within a segment the reference never falls.
     auto pv_half = [&](int kt, int kk, float r0, float r1) {
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
       bf16x8 a[4];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
-      bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
-      bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
-      const float t0 = fmaxf(oref[0], r0), t1 = fmaxf(oref[1], r1);
-      const bool up0 = t0 != oref[0], up1 = t1 != oref[1];
-      if (__any(up0 || up1)) {
-        const float a0 = up0 ? __builtin_amdgcn_exp2f(oref[0] - t0) : 1.0f;
-        const float a1 = up1 ? __builtin_amdgcn_exp2f(oref[1] - t1) : 1.0f;
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+      if (kk == 0) {
+        const bool up0 = r0 > oref[0], up1 = r1 > oref[1];
+        if (__any(up0 || up1)) {
+          const float a0 = up0 ? __builtin_amdgcn_exp2f(oref[0] - r0) : 1.0f;
+          const float a1 = up1 ? __builtin_amdgcn_exp2f(oref[1] - r1) : 1.0f;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          o[cb] *= a0;
-          o[4 + cb] *= a1;
-        }
-        oref[0] = t0;
-        oref[1] = t1;
-      }
-      const bool lo0 = r0 != -INFINITY && r0 < t0, lo1 = r1 != -INFINITY && r1 < t1;
-      if (__any(lo0 || lo1)) {
-        const float f0 = lo0 ? __builtin_amdgcn_exp2f(r0 - t0) : 1.0f;
-        const float f1 = lo1 ? __builtin_amdgcn_exp2f(r1 - t1) : 1.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p0[e] = (__bf16)((float)p0[e] * f0);
-          p1[e] = (__bf16)((float)p1[e] * f1);
+          for (int cb = 0; cb < 4; ++cb) {
+            o[cb] *= a0;
+            o[4 + cb] *= a1;
+          }
+          oref[0] = up0 ? r0 : oref[0];
+          oref[1] = up1 ? r1 : oref[1];
         }
       }
 #pragma unroll
@@ -822,16 +771,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       stored = false;
       lds_barrier();  // step k
-      // References of both halves of tile k-1, read before the copies are
-      // issued so that their latency is covered.
-      float ref[2][2];
+      // References of tile k-1's rows, read before the copies are issued so
+      // that their latency is covered.
+      float ref[2];
       if (k > 0) {
         const Meta* mt = metas + ((k + 1) & 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          ref[kk][0] = mt->m[kk][lane & 31];
-          ref[kk][1] = mt->m[kk][32 + (lane & 31)];
-        }
+        ref[0] = mt->m[lane & 31];
+        ref[1] = mt->m[32 + (lane & 31)];
       }
       if constexpr (kFp4) {
         // Raw tile k+3 goes to the slot tile k left (decoded in step k-1);
@@ -862,8 +808,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       // ahead of the score wave sharing the SIMD (FP4, whose score chain
       // sets the step, keeps them behind it).
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(2);
-      pv_half(kt, 0, ref[0][0], ref[0][1]);
-      pv_half(kt, 1, ref[1][0], ref[1][1]);
+      pv_half(kt, 0, ref[0], ref[1]);
+      pv_half(kt, 1, ref[0], ref[1]);
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(0);
 
       const int nt = tiles_of(pc.L);
@@ -884,16 +830,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         for (int rb = 0; rb < 2; ++rb) {
           const int row_local = rb * 32 + (lane & 31);
           const bool row_ok = g * kRowsPerGroup + row_local < p.HQ;
-          // Each half's sum, moved to O's scale (factors <= 1).
+          // The row's sum is relative to the tile's reference, which O was
+          // moved to before this tile.
           const float m = oref[rb];
-          float l = 0.0f;
-#pragma unroll
-          for (int th = 0; th < 2; ++th) {
-            const float mh = mt->m[th][row_local];
-            if (mh != -INFINITY) l += mt->l[th][row_local] * __builtin_amdgcn_exp2f(mh - m);
-          }
-          const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-          float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+          const float l = mt->l[row_local];
+          // l = 0: no visible token (x = 0, lse = -inf); a NaN sum stays NaN.
+          const float inv_l = l > 0.0f ? 1.0f / l : (l == 0.0f ? 0.0f : nanv);
+          float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : (l == 0.0f ? -INFINITY : nanv);
           if (seg_bad) lse_v = nanv;
           if (row_ok && cq == 0 && hi == 0) {
             if (whole) {
@@ -917,10 +860,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                 *reinterpret_cast<float4*>(stage + (lane & 31) * kStageRow + 32 * cb + 8 * i4 + 4 * hi) = v;
               }
             }
-            // 16 lanes per row, 8 channels (16 B of bf16) each, to the x row or
-            // the partial row.
-            uint16_t* const dst0 = whole ? reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32) * 512
-                                         : p.part_x + (prow0 + rb * 32) * 512;
+            // 16 lanes per row, 8 channels each, to the x row (bf16) or the
+            // partial row (fp32).
+            uint16_t* const dst0 = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32) * 512;
+            float* const dstp = p.part_x + (prow0 + rb * 32) * 512;
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
               const int r = 4 * it + (lane >> 4);
@@ -928,9 +871,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
               const float4 a = *reinterpret_cast<const float4*>(src);
               const float4 b = *reinterpret_cast<const float4*>(src + 4);
               if (g * kRowsPerGroup + rb * 32 + r < p.HQ) {
-                *reinterpret_cast<uint4*>(dst0 + r * 512 + 128 * cq + 8 * (lane & 15)) =
-                    make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                               pack_bf16x2(b.z, b.w));
+                const int c = r * 512 + 128 * cq + 8 * (lane & 15);
+                if (whole) {
+                  *reinterpret_cast<uint4*>(dst0 + c) =
+                      make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                                 pack_bf16x2(b.z, b.w));
+                } else {
+                  *reinterpret_cast<float4*>(dstp + c) = a;
+                  *reinterpret_cast<float4*>(dstp + c + 4) = b;
+                }
               }
             }
           } else if (row_ok) {
@@ -943,9 +892,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = nan_x ? nanv : o[rb * 4 + cb][4 * i4 + e] * inv_l;
-                uint16_t* const xo = whole ? reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512
-                                           : p.part_x + (prow0 + row_local) * 512;
-                *reinterpret_cast<uint2*>(xo + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                if (whole) {
+                  uint16_t* const xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512;
+                  *reinterpret_cast<uint2*>(xo + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                } else {
+                  *reinterpret_cast<float4*>(p.part_x + (prow0 + row_local) * 512 + c) =
+                      make_float4(v[0], v[1], v[2], v[3]);
+                }
               }
             }
           }
@@ -1018,16 +971,19 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, i
   bool any_nan = false;
   for (int i0 = i_first; i0 <= i_last; i0 += kBatch) {
     float ls[kBatch];
-    uint4 xv[kBatch][kC];
+    float4 xv[kBatch][2 * kC];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool in = i0 + u <= i_last;
       const int64_t prow = prow_of(in ? i0 + u : i_first);
       ls[u] = p.part_lse[prow];
       if (!in) ls[u] = -INFINITY;
-      const uint4* src = reinterpret_cast<const uint4*>(p.part_x + prow * 512 + c0);
+      const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
 #pragma unroll
-      for (int k = 0; k < kC; ++k) xv[u][k] = src[L * k];
+      for (int k = 0; k < kC; ++k) {
+        xv[u][2 * k] = src[2 * L * k];
+        xv[u][2 * k + 1] = src[2 * L * k + 1];
+      }
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -1046,13 +1002,11 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, i
       const float w = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
       S += w;
 #pragma unroll
-      for (int k = 0; k < kC; ++k) {
-        const uint32_t wd[4] = {xv[u][k].x, xv[u][k].y, xv[u][k].z, xv[u][k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[8 * k + 2 * e] += w * __uint_as_float(wd[e] << 16);
-          acc[8 * k + 2 * e + 1] += w * __uint_as_float(wd[e] & 0xffff0000u);
-        }
+      for (int k = 0; k < 2 * kC; ++k) {
+        acc[4 * k] += w * xv[u][k].x;
+        acc[4 * k + 1] += w * xv[u][k].y;
+        acc[4 * k + 2] += w * xv[u][k].z;
+        acc[4 * k + 3] += w * xv[u][k].w;
       }
     }
     M = Mn;
@@ -1149,10 +1103,17 @@ __global__ void __launch_bounds__(kMUThreads) merge_up_kernel(AttnParams p, Proj
 
 hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, const ProjParams* up, hipStream_t s) {
   const int blocks = ((p.workgroups + 7) / 8) * 8 * p.groups;
+  const bool lo = p.q_lat_lo != nullptr;
   if (fp4_latent) {
-    hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, p);
+    if (lo) {
+      hipLaunchKernelGGL((attn_mfma_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((attn_mfma_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+    }
+  } else if (lo) {
+    hipLaunchKernelGGL((attn_mfma_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

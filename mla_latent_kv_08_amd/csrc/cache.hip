@@ -20,28 +20,46 @@ __global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
   }
 }
 
-// grid (n); latent of physical row rows[i] as fp32.
+// grid (n); latent of physical row rows[i] as fp32. An FP4 row is decoded
+// by fp4_pair / e4m3_value, the functions the attention kernel decodes its
+// tiles with: thread t takes the 4-byte code word t (channels 8t .. 8t+7)
+// and its group's scale, exactly as one lane of the tile decode does.
 __global__ void __launch_bounds__(256) dequant_kernel(CacheView c, int latent_dtype, int Ckv,
                                                       const int32_t* rows, float* out) {
   const int i = blockIdx.x;
   const int64_t r = rows[i];
   const bool ok = r >= 0 && r < c.num_rows;
   const uint8_t* lat = c.latent + (ok ? r : 0) * c.latent_stride;
+  float* o = out + (int64_t)i * Ckv;
+  const float nanv = __uint_as_float(0x7fc00000u);
+  if (latent_dtype == MLA_FP4_E2M1_E4M3X16) {
+    for (int t = threadIdx.x; t < Ckv / 8; t += 256) {
+      if (!ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[8 * t + e] = nanv;
+        continue;
+      }
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(lat + 4 * t);
+      const float s = e4m3_value(c.scale[r * c.scale_stride + (t >> 1)]);
+      const uint32_t pr[4] = {fp4_pair<0>(w, s), fp4_pair<1>(w, s), fp4_pair<2>(w, s), fp4_pair<3>(w, s)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[8 * t + 2 * e] = __uint_as_float(pr[e] << 16);
+        o[8 * t + 2 * e + 1] = __uint_as_float(pr[e] & 0xffff0000u);
+      }
+    }
+    return;
+  }
   for (int ch = threadIdx.x; ch < Ckv; ch += 256) {
     float v;
     if (!ok) {
-      v = __uint_as_float(0x7fc00000u);
+      v = nanv;
     } else if (latent_dtype == MLA_F32) {
       v = reinterpret_cast<const float*>(lat)[ch];
-    } else if (latent_dtype == MLA_BF16) {
-      v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(lat)[ch]);
     } else {
-      const uint32_t byte = lat[ch >> 1];
-      const uint32_t code = (ch & 1) ? (byte >> 4) : (byte & 0xfu);
-      const float s = e4m3_to_f32(c.scale[(ok ? r : 0) * c.scale_stride + (ch >> 4)]);
-      v = __uint_as_float(e2m1_f32_bits(code)) * s;
+      v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(lat)[ch]);
     }
-    out[(int64_t)i * Ckv + ch] = v;
+    o[ch] = v;
   }
 }
 

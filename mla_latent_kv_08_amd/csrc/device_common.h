@@ -33,33 +33,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // FP4 latent codec: E2M1 codes with one E4M3 ("FN") scale per 16 channels.
 // ---------------------------------------------------------------------------
 
-// fp32 bit pattern of an E2M1 code: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ uint32_t e2m1_f32_bits(uint32_t code) {
-  const uint32_t k = code & 7u;
-  uint32_t mag;
-  if (k < 2u) {
-    mag = k ? 0x3f000000u : 0u;  // 0.5 or 0
-  } else {
-    mag = (((k >> 1) + 126u) << 23) | ((k & 1u) << 22);
-  }
-  return mag | ((code & 8u) << 28);
-}
-
-// Value of an E4M3 ("FN") byte.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-  const uint32_t e = (byte >> 3) & 0xfu;
-  const uint32_t m = byte & 7u;
-  float v;
-  if (e == 0u) {
-    v = (float)m * 0.001953125f;  // m * 2^-9
-  } else if (e == 15u && m == 7u) {
-    v = __uint_as_float(0x7fc00000u);
-  } else {
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  }
-  return (byte & 0x80u) ? -v : v;
-}
-
 // E4M3 code nearest to r >= 0 (fp32), ties to the even code, saturating to 448.
 __device__ __forceinline__ uint32_t e4m3_encode_rne(float r) {
   if (!(r < 448.0f)) return 0x7eu;  // also catches +inf
@@ -101,6 +74,30 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x, float s) {
   }
   if (k == 0u) return 0u;
   return k | ((x < 0.0f) ? 8u : 0u);
+}
+
+// Two codes (byte e of w) times scale s as two bf16. The hardware conversion
+// takes only the exponent of its scale, so it runs at scale 1 (exact E2M1
+// values, straight to fp32) and the E4M3 scale is applied in fp32; every
+// product of an E2M1 value and an E4M3 scale fits in bf16, so taking the high
+// halves is exact.
+template <int e>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, e);
+  const float lo = r[0] * s;
+  const float hi = r[1] * s;
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Value of an E4M3 ("FN") scale byte, without branches (lanes hold different
+// scales): subnormal m * 2^-9, normal (1 + m/8) * 2^(e-7), NaN for e=15, m=7.
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 0xfu, m = byte & 7u;
+  const float sub = (float)m * 0.001953125f;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  float v = e == 0u ? sub : nrm;
+  v = (e == 15u && m == 7u) ? __uint_as_float(0x7fc00000u) : v;
+  return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
 }
 
 // ---------------------------------------------------------------------------

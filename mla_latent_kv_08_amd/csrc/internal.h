@@ -22,12 +22,13 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 struct AttnParams {
   const void* q_lat;  // [B, HQ, Ckv]
+  const void* q_lat_lo;  // [B, HQ, Ckv] bf16 low part of q_lat, or null
   const void* q_pe;   // [B, HQ, Dr]
   CacheView cache;
   const int32_t* seq_lens;
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
-  uint16_t* part_x;  // [G, 2W, kRowsPerGroup, Ckv] bf16 partial results
+  float* part_x;     // [G, 2W, kRowsPerGroup, Ckv] fp32 partial results
   float* part_lse;  // [G, 2W, kRowsPerGroup] (fp32 path: [B, HQ, S] in the log2 domain)
   float* part_xf;   // fp32 path with S > 1 token splits: [B, HQ, S, Ckv] partial results
   int split_tokens;  // fp32 path: tokens per split
@@ -43,6 +44,7 @@ struct ProjParams {
   const void* w;    // wkv_b [H, Dn+Vd, Ckv]
   void* out;        // absorb: q_lat [B,H,Q,Ckv]; up: out [B,H,Q,Vd]
   int B, H, Q, Dn, Vd, Ckv;
+  void* out_lo;     // absorb (bf16): low part of q_lat [B,H,Q,Ckv], or null
 };
 
 // Attention kernel, then either the merge (up == null) or the merge and the

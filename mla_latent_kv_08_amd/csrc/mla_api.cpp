@@ -170,8 +170,8 @@ size_t attn_workspace_bytes(const mla_dims* d, int32_t dtype, int w) {
   const int64_t hq = (int64_t)d->heads * d->q_len;
   const int64_t groups = (hq + kRowsPerGroup - 1) / kRowsPerGroup;
   const int64_t rows = groups * 2 * w * kRowsPerGroup;
-  // partial x [rows, Ckv] bf16, partial lse [rows] fp32, run plan [B + 1] int32
-  return (size_t)(rows * d->d_latent * 2 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
+  // partial x [rows, Ckv] fp32, partial lse [rows] fp32, run plan [B + 1] int32
+  return (size_t)(rows * d->d_latent * 4 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
 }
 
 }  // namespace
@@ -193,28 +193,32 @@ namespace {
 
 // Checks of mla_absorb_q; fills p.
 int prepare_absorb(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
-                   mla::ProjParams* p) {
+                   void* q_lat_lo, mla::ProjParams* p) {
   int st = check_dims(dims);
   if (st) return st;
   if (q_nope == nullptr || wkv_b == nullptr || q_lat == nullptr) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_lat) || !aligned16(q_lat_lo)) {
+    return MLA_ERR_INVALID_ARG;
+  }
   if (dtype == MLA_BF16) {
     if (!deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
   } else if (dtype != MLA_F32) {
     return MLA_ERR_UNSUPPORTED;
+  } else if (q_lat_lo != nullptr) {
+    return MLA_ERR_UNSUPPORTED;  // fp32 q_lat has no low part
   }
   if ((int64_t)dims->batch * dims->heads * dims->q_len > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
   *p = mla::ProjParams{q_nope, wkv_b, q_lat, dims->batch, dims->heads, dims->q_len,
-                       dims->d_nope, dims->d_v, dims->d_latent};
+                       dims->d_nope, dims->d_v, dims->d_latent, q_lat_lo};
   return MLA_OK;
 }
 
 }  // namespace
 
 MLA_API int mla_absorb_q(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* wkv_b,
-                         void* q_lat, void* stream) {
+                         void* q_lat, void* q_lat_lo, void* stream) {
   mla::ProjParams p{};
-  const int st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, &p);
+  const int st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, q_lat_lo, &p);
   if (st) return st;
   if (dims->batch == 0) return MLA_OK;
   return hip_status(mla::launch_absorb(p, dtype == MLA_BF16, static_cast<hipStream_t>(stream)));
@@ -253,7 +257,7 @@ MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32
 namespace {
 
 // Checks of mla_decode_attn; fills p (a batch of 0 leaves p.B = 0).
-int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
+int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo, const void* q_pe,
                    const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
                    void* x_lat, float* lse, void* workspace, size_t workspace_bytes,
                    const mla_decode_opts* opts, mla::AttnParams* out) {
@@ -264,13 +268,17 @@ int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const
   if (q_lat == nullptr || q_pe == nullptr || seq_lens == nullptr || x_lat == nullptr) {
     return MLA_ERR_INVALID_ARG;
   }
-  if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(x_lat)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(x_lat) || !aligned16(q_lat_lo)) {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (q_lat_lo != nullptr && dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;  // fp32 q_lat has no low part
   if (!(softmax_scale == softmax_scale)) return MLA_ERR_INVALID_ARG;
   *out = mla::AttnParams{};
   if (dims->batch == 0) return MLA_OK;
 
   mla::AttnParams p{};
   p.q_lat = q_lat;
+  p.q_lat_lo = q_lat_lo;
   p.q_pe = q_pe;
   p.cache = view_of(cache);
   p.seq_lens = seq_lens;
@@ -309,8 +317,8 @@ int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const
   p.groups = (p.HQ + kRowsPerGroup - 1) / kRowsPerGroup;
   p.workgroups = w;
   const int64_t part_rows = (int64_t)p.groups * 2 * w * kRowsPerGroup;
-  p.part_x = static_cast<uint16_t*>(workspace);
-  p.part_lse = reinterpret_cast<float*>(p.part_x + part_rows * p.Ckv);
+  p.part_x = static_cast<float*>(workspace);
+  p.part_lse = p.part_x + part_rows * p.Ckv;
   p.plan = reinterpret_cast<int*>(p.part_lse + part_rows);
   *out = p;
   return MLA_OK;
@@ -336,30 +344,30 @@ int prepare_up(const mla_dims* dims, int32_t dtype, const void* x_lat, const voi
 
 }  // namespace
 
-MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
-                            const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                            float softmax_scale, void* x_lat, float* lse, void* workspace,
+MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
+                            const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
+                            int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse, void* workspace,
                             size_t workspace_bytes, const mla_decode_opts* opts, void* stream) {
   mla::AttnParams p{};
-  const int st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat,
-                                lse, workspace, workspace_bytes, opts, &p);
+  const int st = prepare_decode(dims, dtype, q_lat, q_lat_lo, q_pe, cache, seq_lens, max_seq_len, softmax_scale,
+                                x_lat, lse, workspace, workspace_bytes, opts, &p);
   if (st || p.B == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MLA_F32) return hip_status(mla::launch_attn_f32(p, s));
   return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, nullptr, s));
 }
 
-MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_pe,
-                               const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                               float softmax_scale, void* x_lat, float* lse, const void* wkv_b, void* out,
-                               void* workspace, size_t workspace_bytes, const mla_decode_opts* opts,
-                               void* stream) {
+MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
+                               const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
+                               int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
+                               const void* wkv_b, void* out, void* workspace, size_t workspace_bytes,
+                               const mla_decode_opts* opts, void* stream) {
   // The up-projection's arguments first: they need no device query.
   mla::ProjParams u{};
   int st = prepare_up(dims, dtype, x_lat, wkv_b, out, &u);
   if (st) return st;
   mla::AttnParams p{};
-  st = prepare_decode(dims, dtype, q_lat, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat, lse,
+  st = prepare_decode(dims, dtype, q_lat, q_lat_lo, q_pe, cache, seq_lens, max_seq_len, softmax_scale, x_lat, lse,
                       workspace, workspace_bytes, opts, &p);
   if (st || p.B == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -536,12 +544,12 @@ MLA_API int mla_grouped_out_proj(const mla_dims* dims, int32_t dtype, int32_t gr
 MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                               const void* k_pe_new, const mla_kv_cache* cache, const int32_t* seq_lens,
                               int32_t dtype, const void* q_nope, const void* wkv_b, void* q_lat,
-                              void* stream) {
+                              void* q_lat_lo, void* stream) {
   mla::AppendParams a{};
   int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &a);
   if (st) return st;
   mla::ProjParams p{};
-  st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, &p);
+  st = prepare_absorb(dims, dtype, q_nope, wkv_b, q_lat, q_lat_lo, &p);
   if (st) return st;
   if (dims->batch == 0) return MLA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -74,6 +74,7 @@ struct AbsorbLds {
   uint16_t w[128 * kWPad];
   uint16_t q[32 * kQPad];
   uint16_t o[32 * kQPad];
+  uint16_t o_lo[32 * kQPad];
 };
 
 // Head h, latent channels c0 .. c0+127, by one 256-thread block.
@@ -132,19 +133,35 @@ __device__ __forceinline__ void absorb_bf16_block(const ProjParams& p, int h, in
       }
     }
     // D^T[c][m]: lane holds row m = lane%32, channels 8*(i/4) + 4*hi + i%4 of the wave's 32.
+    // With a low-part output, q_lat = hi + lo: hi = bf16(acc), and the
+    // residual acc - hi (exact in fp32) rounded to bf16.
     {
-      uint16_t* o = s_o + (lane & 31) * kQPad + 32 * wave + 4 * hi;
+      const int off = (lane & 31) * kQPad + 32 * wave + 4 * hi;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        *reinterpret_cast<uint2*>(o + 8 * i4) =
-            make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+        const uint32_t h01 = pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]);
+        const uint32_t h23 = pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]);
+        *reinterpret_cast<uint2*>(s_o + off + 8 * i4) = make_uint2(h01, h23);
+        if (p.out_lo != nullptr) {
+          const float r0 = acc[4 * i4] - __uint_as_float(h01 << 16);
+          const float r1 = acc[4 * i4 + 1] - __uint_as_float(h01 & 0xffff0000u);
+          const float r2 = acc[4 * i4 + 2] - __uint_as_float(h23 << 16);
+          const float r3 = acc[4 * i4 + 3] - __uint_as_float(h23 & 0xffff0000u);
+          *reinterpret_cast<uint2*>(lds.o_lo + off + 8 * i4) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+        }
       }
     }
     __syncthreads();
     if (m0 + sr < M) {
-      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + q_row(m0 + sr) * p.Ckv + c0 + sc;
+      const int64_t orow = q_row(m0 + sr) * p.Ckv + c0 + sc;
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + orow;
       *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc);
       *reinterpret_cast<uint4*>(o + 8) = *reinterpret_cast<const uint4*>(s_o + sr * kQPad + sc + 8);
+      if (p.out_lo != nullptr) {
+        uint16_t* ol = reinterpret_cast<uint16_t*>(p.out_lo) + orow;
+        *reinterpret_cast<uint4*>(ol) = *reinterpret_cast<const uint4*>(lds.o_lo + sr * kQPad + sc);
+        *reinterpret_cast<uint4*>(ol + 8) = *reinterpret_cast<const uint4*>(lds.o_lo + sr * kQPad + sc + 8);
+      }
     }
   }
 }

@@ -131,14 +131,16 @@ class LatentCache:
         return d_latent // 2 + d_latent // 16 + 2 * d_rope
 
 
-def mla_absorb_q(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_lat: torch.Tensor, stream=None) -> None:
-    """q_lat[b,h,q,:] = W_UK[h]^T q_nope[b,h,q,:]; q_nope [B,H,Q,Dn], wkv_b [H,Dn+Vd,Ckv]."""
+def mla_absorb_q(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_lat: torch.Tensor,
+                 q_lat_lo: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q_lat[b,h,q,:] = W_UK[h]^T q_nope[b,h,q,:]; q_nope [B,H,Q,Dn], wkv_b [H,Dn+Vd,Ckv]. With q_lat_lo
+    (bf16 only) the residual of q_lat's rounding is written there too."""
     B, H, Q, Dn = q_nope.shape
     Vd = wkv_b.shape[1] - Dn
     Ckv = wkv_b.shape[2]
     d = _dims(B, H, Q, Dn, 64, Vd, Ckv)
     _lib.check(_lib.load().mla_absorb_q(ctypes.byref(d), _code(q_nope), _ptr(q_nope), _ptr(wkv_b),
-                                        _ptr(q_lat), _stream(stream)), "mla_absorb_q")
+                                        _ptr(q_lat), _ptr(q_lat_lo), _stream(stream)), "mla_absorb_q")
 
 
 def mla_decode_workspace_size(batch: int, heads: int, q_len: int, dtype: int, max_seq_len: int,
@@ -157,7 +159,8 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
                     seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
                     x_lat: torch.Tensor, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, workgroups: int = 0,
-                    d_nope: int = 128, d_v: int = 128, stream=None) -> None:
+                    d_nope: int = 128, d_v: int = 128, q_lat_lo: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
     """Absorbed attention over the latent cache; see mla_decode_attn in include/mla.h."""
     B, H, Q, Ckv = q_lat.shape
     Dr = q_pe.shape[-1]
@@ -173,7 +176,7 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q_lat.device)
     desc = cache.desc()
     _lib.check(_lib.load().mla_decode_attn(
-        ctypes.byref(d), code, _ptr(q_lat), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
+        ctypes.byref(d), code, _ptr(q_lat), _ptr(q_lat_lo), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
         int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
         "mla_decode_attn")
@@ -202,7 +205,8 @@ def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCach
 def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
                        seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
                        x_lat: torch.Tensor, lse: Optional[torch.Tensor], wkv_b: torch.Tensor, out: torch.Tensor,
-                       workspace: Optional[torch.Tensor] = None, workgroups: int = 0, stream=None) -> None:
+                       workspace: Optional[torch.Tensor] = None, workgroups: int = 0,
+                       q_lat_lo: Optional[torch.Tensor] = None, stream=None) -> None:
     """mla_decode_attn then mla_up_proj_v on its x; see mla_decode_attn_up in include/mla.h."""
     B, H, Q, Ckv = q_lat.shape
     Dr = q_pe.shape[-1]
@@ -220,7 +224,7 @@ def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCac
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q_lat.device)
     desc = cache.desc()
     _lib.check(_lib.load().mla_decode_attn_up(
-        ctypes.byref(d), code, _ptr(q_lat), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
+        ctypes.byref(d), code, _ptr(q_lat), _ptr(q_lat_lo), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
         int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(wkv_b), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
         "mla_decode_attn_up")
@@ -303,7 +307,7 @@ def mla_sink_inverse_rope(x_lat: torch.Tensor, lse: Optional[torch.Tensor], seq_
 
 def mla_append_absorb(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache,
                       seq_lens: torch.Tensor, q_nope: torch.Tensor, wkv_b: torch.Tensor, q_lat: torch.Tensor,
-                      stream=None) -> None:
+                      q_lat_lo: Optional[torch.Tensor] = None, stream=None) -> None:
     """mla_cache_append(c_kv_new, k_pe_new, cache, seq_lens) then mla_absorb_q(q_nope, wkv_b, q_lat),
     in one launch for bf16. The new tokens are the queries: [B, Q, ...] and [B, H, Q, ...]."""
     B, Qn, Ckv = c_kv_new.shape
@@ -318,7 +322,8 @@ def mla_append_absorb(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: Lat
     desc = cache.desc()
     _lib.check(_lib.load().mla_append_absorb(ctypes.byref(d), _code(c_kv_new), _ptr(c_kv_new), _ptr(k_pe_new),
                                              ctypes.byref(desc), _ptr(seq_lens), _code(q_nope), _ptr(q_nope),
-                                             _ptr(wkv_b), _ptr(q_lat), _stream(stream)), "mla_append_absorb")
+                                             _ptr(wkv_b), _ptr(q_lat), _ptr(q_lat_lo), _stream(stream)),
+               "mla_append_absorb")
 
 
 def mla_dequant_rows(cache: LatentCache, rows: torch.Tensor, out: torch.Tensor, d_latent: int = 512,

@@ -15,6 +15,9 @@ import workloads as W
 from oracle import fp4_ref, mla_ref
 
 TOL = {"f32": 1e-4, "bf16": 1e-2, "fp4": 1e-2}
+# q_lat + q_lat_lo against the fp64 absorption: the two bf16 parts hold the
+# fp32 sum to about 2^-17 of each element, plus the fp32 accumulation error.
+Q_SPLIT_TOL = 1e-4
 
 
 def ops():
@@ -73,21 +76,27 @@ class GpuCase:
                 r[b, n - L:] = inp.seq_rope(b)
         o.mla_cache_append(c.cuda(), r.cuda(), self.cache, self.seq_lens)
 
-    def run(self, workgroups: int = 0):
+    def run(self, workgroups: int = 0, lo: bool = True):
+        """One decode step through the C ABI. bf16 / FP4: with `lo` the query's low
+        part (q_lat_lo) is formed by mla_absorb_q and used by the scores."""
         o = ops()
         w = self.w
         dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
         B, H, Q = w.B, w.H, w.Q
         q_lat = torch.empty(B, H, Q, w.Ckv, dtype=dt, device="cuda")
+        q_lo = torch.empty_like(q_lat) if (lo and w.dtype != "f32") else None
         x = torch.empty(B, H, Q, w.Ckv, dtype=dt, device="cuda")
         lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
         out = torch.empty(B, H, Q, w.Vd, dtype=dt, device="cuda")
-        o.mla_absorb_q(self.q_nope, self.wkv_b, q_lat)
+        o.mla_absorb_q(self.q_nope, self.wkv_b, q_lat, q_lat_lo=q_lo)
         o.mla_decode_attn(q_lat, self.q_pe, self.cache, self.seq_lens, self.max_len, w.softmax_scale,
-                          x, lse, workgroups=workgroups)
+                          x, lse, workgroups=workgroups, q_lat_lo=q_lo)
         o.mla_up_proj_v(x, self.wkv_b, out)
         torch.cuda.synchronize()
-        return {"q_lat": q_lat, "x": x, "lse": lse, "out": out}
+        res = {"q_lat": q_lat, "x": x, "lse": lse, "out": out}
+        if q_lo is not None:
+            res["q_lat_lo"] = q_lo
+        return res
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -141,11 +150,16 @@ def assert_lse_close(gpu: np.ndarray, ref: np.ndarray, tol: float, name: str = "
         assert err <= lim
 
 
-def compare(gpu: dict, ref: dict, w: W.Workload, heads=None, batch=None):
-    tol = TOL[w.dtype]
+def compare(gpu: dict, ref: dict, w: W.Workload, heads=None, batch=None, tol=None):
+    """x, out (and q_lat) within tol * max|ref| (default: the dtype's bar); lse within tol * (1 + max|lse|)."""
+    tol = TOL[w.dtype] if tol is None else tol
     sel = lambda t: t if batch is None else t[list(batch)]  # noqa: E731
     hsel = lambda t: t if heads is None else t[:, list(heads)]  # noqa: E731
     assert_close(to64(hsel(sel(gpu["q_lat"]))), ref["q_lat"], tol, "q_lat")
+    if "q_lat_lo" in gpu:
+        # hi + lo keeps about 16 significant bits of the fp32 sum.
+        both = to64(hsel(sel(gpu["q_lat"]))) + to64(hsel(sel(gpu["q_lat_lo"])))
+        assert_close(both, ref["q_lat"], Q_SPLIT_TOL, "q_lat + q_lat_lo")
     assert_close(to64(hsel(sel(gpu["x"]))), ref["x"], tol, "x")
     assert_lse_close(to64(hsel(sel(gpu["lse"]))), ref["lse"], tol)
     assert_close(to64(hsel(sel(gpu["out"]))), ref["out"], tol, "out")

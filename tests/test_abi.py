@@ -65,29 +65,38 @@ P = 0x20000  # a 16-byte aligned fake device address; never dereferenced on thes
 
 def test_absorb_validation(lib):
     byref = ctypes.byref
-    assert lib.mla_absorb_q(None, 1, P, P, P, None) == _lib.MLA_ERR_INVALID_ARG
-    assert lib.mla_absorb_q(byref(_dims()), 1, None, P, P, None) == _lib.MLA_ERR_INVALID_ARG
-    assert lib.mla_absorb_q(byref(_dims()), 1, P + 2, P, P, None) == _lib.MLA_ERR_INVALID_ARG
-    assert lib.mla_absorb_q(byref(_dims(heads=0)), 1, P, P, P, None) == _lib.MLA_ERR_INVALID_ARG
-    assert lib.mla_absorb_q(byref(_dims(d_nope=64)), 1, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
-    assert lib.mla_absorb_q(byref(_dims()), 7, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(None, 1, P, P, P, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims()), 1, None, P, P, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims()), 1, P + 2, P, P, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims()), 1, P, P, P, P + 2, None) == _lib.MLA_ERR_INVALID_ARG
+    # fp32 q_lat has no low part.
+    assert lib.mla_absorb_q(byref(_dims()), 0, P, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(byref(_dims(heads=0)), 1, P, P, P, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(byref(_dims(d_nope=64)), 1, P, P, P, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(byref(_dims()), 7, P, P, P, None, None) == _lib.MLA_ERR_UNSUPPORTED
     # An empty batch is a valid no-op.
-    assert lib.mla_absorb_q(byref(_dims(batch=0)), 1, P, P, P, None) == _lib.MLA_OK
+    assert lib.mla_absorb_q(byref(_dims(batch=0)), 1, P, P, P, None, None) == _lib.MLA_OK
+    assert lib.mla_absorb_q(byref(_dims(batch=0)), 1, P, P, P, P, None) == _lib.MLA_OK
     assert lib.mla_up_proj_v(byref(_dims(d_v=64)), 1, P, P, P, None) == _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_up_proj_v(byref(_dims()), 1, P, None, P, None) == _lib.MLA_ERR_INVALID_ARG
 
 
 def _attn(lib, dims=None, dtype=1, cache=None, seq=P, max_len=4096, ws=P, ws_bytes=1 << 30, opts=None,
-          q=P):
+          q=P, q_lo=None):
     dims = dims or _dims()
     cache = cache or _cache()
-    return lib.mla_decode_attn(ctypes.byref(dims), dtype, q, P, ctypes.byref(cache), seq, max_len,
+    return lib.mla_decode_attn(ctypes.byref(dims), dtype, q, q_lo, P, ctypes.byref(cache), seq, max_len,
                                0.072, P, P, ws, ws_bytes, ctypes.byref(opts) if opts else None, None)
 
 
 def test_attn_validation(lib):
     E = _lib
     assert _attn(lib, q=None) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, q_lo=P + 8) == E.MLA_ERR_INVALID_ARG
+    assert _attn(lib, q_lo=P, dtype=E.MLA_F32, cache=_cache(latent_dtype=E.MLA_F32, rope_dtype=E.MLA_F32,
+                                                             latent_stride=2304, rope_stride=2304)) \
+        == E.MLA_ERR_UNSUPPORTED  # fp32 q_lat has no low part
+    assert _attn(lib, q_lo=P, dims=_dims(batch=0)) == E.MLA_OK
     assert _attn(lib, seq=None) == E.MLA_ERR_INVALID_ARG
     assert _attn(lib, max_len=-1) == E.MLA_ERR_INVALID_ARG
     assert _attn(lib, dims=_dims(q_len=17)) == E.MLA_ERR_UNSUPPORTED
@@ -178,15 +187,17 @@ def test_attn_up_and_append_absorb_validation(lib):
     d = _dims()
 
     def up(wkv=P, out=P, dims=None):
-        return lib.mla_decode_attn_up(byref(dims or d), E.MLA_BF16, P, P, byref(c), P, 4096, 0.072, P, P, wkv, out,
-                                      P, 1 << 30, None, None)
+        return lib.mla_decode_attn_up(byref(dims or d), E.MLA_BF16, P, None, P, byref(c), P, 4096, 0.072, P, P,
+                                      wkv, out, P, 1 << 30, None, None)
     assert up(wkv=None) == E.MLA_ERR_INVALID_ARG
     assert up(out=None) == E.MLA_ERR_INVALID_ARG
     assert up(dims=_dims(d_v=64)) == E.MLA_ERR_UNSUPPORTED
     assert up(dims=_dims(batch=0)) == E.MLA_OK
-    assert lib.mla_append_absorb(byref(d), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, None, P, P,
+    assert lib.mla_append_absorb(byref(d), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, None, P, P, None,
                                  None) == E.MLA_ERR_INVALID_ARG
-    assert lib.mla_append_absorb(byref(_dims(batch=0)), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, P, P, P,
+    assert lib.mla_append_absorb(byref(d), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, P, P, P, P + 4,
+                                 None) == E.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb(byref(_dims(batch=0)), E.MLA_BF16, P, P, byref(c), P, E.MLA_BF16, P, P, P, P,
                                  None) == E.MLA_OK
 
 

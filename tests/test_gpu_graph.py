@@ -22,6 +22,7 @@ def test_graph_replays_match_eager():
     c_new = inp.latent[last].reshape(B, 1, w.Ckv).contiguous().cuda()
     r_new = inp.rope[last].reshape(B, 1, w.Dr).contiguous().cuda()
     q_lat = torch.empty(B, H, Q, w.Ckv, dtype=bf16, device="cuda")
+    q_lo = torch.empty_like(q_lat)
     x = torch.empty_like(q_lat)
     lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
     out = torch.empty(B, H, Q, w.Vd, dtype=bf16, device="cuda")
@@ -30,13 +31,14 @@ def test_graph_replays_match_eager():
 
     def step(stream):
         o.mla_cache_append(c_new, r_new, g.cache, g.seq_lens, stream=stream)
-        o.mla_absorb_q(g.q_nope, g.wkv_b, q_lat, stream=stream)
+        o.mla_absorb_q(g.q_nope, g.wkv_b, q_lat, q_lat_lo=q_lo, stream=stream)
         o.mla_decode_attn(q_lat, g.q_pe, g.cache, g.seq_lens, g.max_len, w.softmax_scale, x, lse,
-                          workspace=ws, stream=stream)
+                          workspace=ws, q_lat_lo=q_lo, stream=stream)
         o.mla_up_proj_v(x, g.wkv_b, out, stream=stream)
 
     def snapshot():
-        return {"q_lat": q_lat.view(torch.int16).clone(), "x": x.view(torch.int16).clone(),
+        return {"q_lat": q_lat.view(torch.int16).clone(), "q_lat_lo": q_lo.view(torch.int16).clone(),
+                "x": x.view(torch.int16).clone(),
                 "lse": lse.clone(), "out": out.view(torch.int16).clone()}
 
     side = torch.cuda.Stream()
@@ -58,6 +60,7 @@ def test_graph_replays_match_eager():
         out.zero_()
         lse.fill_(1.0)
         q_lat.zero_()
+        q_lo.zero_()
         if rep == 2:
             step(torch.cuda.current_stream())
             torch.cuda.synchronize()
