@@ -215,6 +215,26 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
                             void* stream);
 
 /*
+ * mla_decode_attn_noalloc -- mla_decode_attn without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation. Arguments,
+ * results and errors are those of mla_decode_attn.
+ *   Its scratch (split partials, their lse, the run plan) is one device
+ *   array of MLA_NOALLOC_SCRATCH_BYTES per GPU, inside the library, held
+ *   until the process ends; no call allocates or frees memory. A call whose
+ *   workspace (mla_decode_workspace_size) would exceed that size returns
+ *   MLA_ERR_WORKSPACE and enqueues nothing.
+ *   Every call on a GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams, or different host threads without ordering)
+ *   race and must not be issued; calls ordered on one stream are safe.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+MLA_API int mla_decode_attn_noalloc(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
+                                    const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
+                                    int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,
+                                    const mla_decode_opts* opts, void* stream);
+
+/*
  * mla_decode_attn_up -- mla_decode_attn followed by mla_up_proj_v on its x
  * (same arguments as the two calls; x_lat and lse are still written). The
  * results are those of the two calls in sequence. With dtype MLA_BF16 the

@@ -18,12 +18,14 @@ MLA_FP4_E2M1_E4M3X16 = 2
 MLA_ROPE_INTERLEAVED = 0
 MLA_ROPE_HALVES = 1
 MLA_ROPE_LATENT_TAIL = 2
+MLA_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 EXPORTS = (
     "mla_absorb_q",
     "mla_decode_workspace_size",
     "mla_decode_attn",
     "mla_decode_attn_up",
+    "mla_decode_attn_noalloc",
     "mla_up_proj_v",
     "mla_cache_append",
     "mla_rope_append",
@@ -99,6 +101,9 @@ def load() -> ctypes.CDLL:
                                        I32, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t,
                                        ctypes.POINTER(MlaDecodeOpts), P]
     lib.mla_decode_attn_up.restype = ctypes.c_int
+    lib.mla_decode_attn_noalloc.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, ctypes.POINTER(MlaKvCache), P,
+                                            I32, ctypes.c_float, P, P, ctypes.POINTER(MlaDecodeOpts), P]
+    lib.mla_decode_attn_noalloc.restype = ctypes.c_int
     lib.mla_up_proj_v.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, P, P]
     lib.mla_up_proj_v.restype = ctypes.c_int
     lib.mla_cache_append.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P, P]

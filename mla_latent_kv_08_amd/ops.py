@@ -21,6 +21,7 @@ __all__ = [
     "MLA_ROPE_LATENT_TAIL", "MLAError", "LatentCache", "mla_rope_append", "mla_sink_inverse_rope",
     "mla_grouped_out_proj", "mla_prefill_attn",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn", "mla_decode_attn_up", "mla_up_proj_v",
+    "mla_decode_attn_noalloc",
     "mla_cache_append", "mla_append_absorb", "mla_dequant_rows",
 ]
 
@@ -180,6 +181,28 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
         int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(stream)),
         "mla_decode_attn")
+
+
+def mla_decode_attn_noalloc(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
+                            seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                            x_lat: torch.Tensor, lse: Optional[torch.Tensor] = None, workgroups: int = 0,
+                            d_nope: int = 128, d_v: int = 128, q_lat_lo: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """mla_decode_attn with the library's own scratch instead of a workspace; see
+    mla_decode_attn_noalloc in include/mla.h."""
+    B, H, Q, Ckv = q_lat.shape
+    Dr = q_pe.shape[-1]
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    d = _dims(B, H, Q, d_nope, Dr, d_v, Ckv)
+    opts = MlaDecodeOpts(int(workgroups))
+    desc = cache.desc()
+    _lib.check(_lib.load().mla_decode_attn_noalloc(
+        ctypes.byref(d), _code(q_lat), _ptr(q_lat), _ptr(q_lat_lo), _ptr(q_pe), ctypes.byref(desc),
+        _ptr(seq_lens), int(max_seq_len), float(softmax_scale), _ptr(x_lat), _ptr(lse), ctypes.byref(opts),
+        _stream(stream)), "mla_decode_attn_noalloc")
 
 
 def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache, seq_lens: torch.Tensor,

@@ -218,3 +218,22 @@ def test_prefill_attn_validation(lib):
     assert call(sl=None) == E.MLA_ERR_INVALID_ARG
     assert call(cache=_cache(num_rows=100)) == E.MLA_ERR_INVALID_ARG  # 2 x 4096 rows do not fit
     assert call(dims=_dims(q_len=256, batch=0)) == E.MLA_OK
+
+
+def test_attn_noalloc_validation(lib):
+    """Host-side rejections of mla_decode_attn_noalloc (before any device query)."""
+    E = _lib
+    byref = ctypes.byref
+    c = _cache()
+
+    def call(dims=None, dtype=E.MLA_BF16, opts=None):
+        return lib.mla_decode_attn_noalloc(byref(dims or _dims()), dtype, P, None, P, byref(c), P, 4096, 0.072, P,
+                                           P, byref(opts) if opts else None, None)
+    assert lib.mla_decode_attn_noalloc(None, E.MLA_BF16, P, None, P, byref(c), P, 4096, 0.072, P, P, None,
+                                       None) == E.MLA_ERR_INVALID_ARG
+    assert call(dims=_dims(q_len=17)) == E.MLA_ERR_UNSUPPORTED
+    assert call(dtype=7) == E.MLA_ERR_UNSUPPORTED
+    assert call(opts=_lib.MlaDecodeOpts(-1)) == E.MLA_ERR_INVALID_ARG
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.MLA_NOALLOC_SCRATCH_BYTES
