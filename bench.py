@@ -232,7 +232,7 @@ def setup_attn_case(w, dev, copies: int, lo: bool = True):
     code = ops.MLA_F32 if w.dtype == "f32" else ops.MLA_BF16
     ws = ops.mla_decode_workspace_size(w.B, w.H, w.Q, code, max_len)
     torch.cuda.synchronize()
-    return {"lens": lens, "caches": caches, "seq_lens": seq_lens, "max_len": max_len,
+    return {"lens": lens, "caches": caches, "seq_lens": seq_lens, "max_len": max_len, "inputs_sha256": inp.sha256(),
             "q_lat": q_lat, "q_lat_lo": q_lo, "q_pe": inp.q_pe.to(dev), "x": torch.empty_like(q_lat),
             "lse": torch.empty(w.B, w.H, w.Q, dtype=torch.float32, device=dev),
             "workspace": torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)}
@@ -244,15 +244,18 @@ def setup_attn_case(w, dev, copies: int, lo: bool = True):
 OTHER_WORKLOADS = {"tiny_f32": 1, "ragged_paged_bf16": 1, "long_splitkv_bf16": 1, "mtp_fp4": 2}
 
 
-def measure_other_workloads(dev, stream, reps: int, lo: bool = True) -> dict:
+def measure_other_workloads(dev, stream, reps: int, lo: bool = True, names=None) -> dict:
     import torch
     import workloads as W
     from mla_latent_kv_08_amd import ops
     out = {}
     for name, copies in OTHER_WORKLOADS.items():
+        if names is not None and name not in names:
+            continue
         w = W.WORKLOADS[name]
         print(f"bench: workload {name}", file=sys.stderr, flush=True)
         case = setup_attn_case(w, dev, copies, lo)
+        inputs_sha = case["inputs_sha256"]
 
         def call(i, case=case, w=w):
             ops.mla_decode_attn(case["q_lat"], case["q_pe"], case["caches"][i % len(case["caches"])],
@@ -268,7 +271,7 @@ def measure_other_workloads(dev, stream, reps: int, lo: bool = True) -> dict:
         t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         rec = {"attn_avg_ms": ms, "B": w.B, "H": w.H, "Q": w.Q, "tokens": sum(case["lens"]),
-               "q_lat_lo": case["q_lat_lo"] is not None,
+               "q_lat_lo": case["q_lat_lo"] is not None, "inputs_sha256": inputs_sha,
                "cache": ("paged 64-token pages" if w.paged else "contiguous") + f", {w.dtype} latent",
                "cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops,
                "kv_GBps": cache_b / t / 1e9, "mfma_TFLOPs": flops / t / 1e12}
@@ -449,6 +452,9 @@ def main():
                          "and the context figures (copy rate, clocks)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time mla_prefill_attn (chunked and full prefill) and print that record")
+    ap.add_argument("--workload", choices=sorted(OTHER_WORKLOADS),
+                    help="only time the attention call of this workload (--steps back-to-back calls) and "
+                         "print its record: for profiling runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one device-to-device copy of COPY_BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -467,10 +473,16 @@ def main():
     import workloads as W
     from mla_latent_kv_08_amd import ops
 
+    dev = torch.device("cuda", 0)
+    if args.workload:
+        torch.cuda.set_device(dev)
+        rec = measure_other_workloads(dev, torch.cuda.current_stream(dev), max(1, args.steps), lo=not args.no_lo,
+                                      names=(args.workload,))
+        print(json.dumps({"workload": args.workload, **rec[args.workload]}))
+        return
     w = W.WORKLOADS[WORKLOAD]
     inp = W.generate(w)
     pl = W.place(inp)
-    dev = torch.device("cuda", 0)
     if args.prefill_only:
         print(json.dumps({"prefill_bf16": measure_prefill(dev, torch.cuda.current_stream(dev), 20)}))
         return

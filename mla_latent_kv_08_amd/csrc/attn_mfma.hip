@@ -34,9 +34,9 @@
 // is copied into LDS three tiles ahead and decoded to bf16 in LDS one step
 // before the score waves need it.
 // Latent row t holds its 16-byte chunk c at slot c ^ swz(t), which keeps the
-// score reads (16 tokens, one chunk) and the transposed P.V reads (4 tokens,
-// 4 chunks) free of bank conflicts; the RoPE keys of 8 tokens form one
-// chunk-major group after the latent rows.
+// score reads (16 tokens, one chunk each) and the transposed P.V reads (4
+// tokens, 4 chunks) free of bank conflicts (see swz); the RoPE keys of 8
+// tokens form one chunk-major group after the latent rows.
 //
 // Tokens are split across workgroups (flash-decoding): the tiles of all
 // sequences, end to end, are dealt in equal contiguous runs to the W
@@ -118,14 +118,11 @@ typedef int int32x4_t __attribute__((ext_vector_type(4)));
 // such a load writes, would otherwise wait for all of them still in flight
 // before every later LDS read of the issuing wave, draining the copies meant
 // to overlap the next steps. The copying waves wait for their own copies
-// (vmcnt) before the barrier that hands a tile to the other waves. M0 (the
-// LDS address) is set inside the block; nothing else in these kernels keeps a
-// value in M0.
+// (vmcnt) before the barrier that hands a tile to the other waves. The LDS
+// address goes in M0 as an input operand, so the compiler sets M0 itself and
+// knows the block reads it.
 __device__ __forceinline__ void lds_copy16(int32x4_t rsrc, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voff), "s"(rsrc)
-               : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -142,9 +139,17 @@ __device__ __forceinline__ bf16x8 join(shortx4 a, shortx4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Slot permutation of the 16-byte chunks of latent row t (an involution on
-// the low four bits of the chunk index).
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+// XOR mask on the low four bits of the chunk index of latent row t: a linear
+// map of t's low four bits (bit 0 -> 5, bit 1 -> 12, bit 2 -> 3, bit 3 -> 2).
+// It was chosen by measurement: rocprofv3's bank-conflict counter reads zero
+// for both of the kernel's LDS read patterns with it (the score waves' K
+// fragments, 16 bytes a lane, 16 tokens x one chunk; the P.V waves'
+// transposed fragments, 8 bytes a lane, 4 tokens x 4 chunks), where the
+// bit-transposing mask left every K read 2-way conflicted and t itself every
+// transposed read 4-way conflicted.
+__device__ __forceinline__ int swz(int t) {
+  return (-(t & 1) & 5) ^ (-((t >> 1) & 1) & 12) ^ (-((t >> 2) & 1) & 3) ^ (-((t >> 3) & 1) & 2);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (lgkm and exp counters left alone).
@@ -571,6 +576,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           }
           s[0] = acc[0][0] + acc[0][1];
           s[1] = acc[1][0] + acc[1][1];
+          // Keep the reads kAhead fragments ahead of the matrix ops (the
+          // scheduler would otherwise pull each read down to its first use):
+          // kAhead reads, then per fragment its matrix ops and the next read.
+          constexpr int kMf = kLo ? 2 : 1;  // matrix ops per latent fragment
+          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+          for (int f = 0; f < 32; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+            if (f + kAhead < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int f = 32; f < kF; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (f + kAhead < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         }
         __builtin_amdgcn_s_setprio(0);
 

@@ -82,6 +82,9 @@ int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t
   } else if (c->page_size == kPageTokens) {
     if (c->page_table == nullptr || c->page_table_stride <= 0) return MLA_ERR_INVALID_ARG;
     if ((int64_t)c->page_table_stride * kPageTokens < c->capacity) return MLA_ERR_INVALID_ARG;
+    // A paged pool holds whole pages, so "page p exists" is p*64 + 63 < num_rows
+    // for every kernel, whichever rows of the page it reads.
+    if (c->num_rows % kPageTokens) return MLA_ERR_INVALID_ARG;
   } else {
     return MLA_ERR_UNSUPPORTED;
   }

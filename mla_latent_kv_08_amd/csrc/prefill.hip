@@ -29,6 +29,7 @@ namespace {
 constexpr int kPfThreads = 512;
 constexpr int kPfQ = 64;        // queries per block
 constexpr int kPfT = 32;        // tokens per tile
+static_assert(kPageTokens % kPfT == 0, "a tile never crosses a page");
 constexpr int kCPitch = 520;    // latent row pitch in LDS (bf16)
 constexpr int kKPitch = 200;    // key row pitch: 128 decompressed + 64 RoPE + pad
 constexpr int kVPitch = 40;     // transposed value row pitch: 32 tokens + pad
@@ -107,9 +108,12 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
     if (c.page_size == 0) {
       base = (int64_t)b * c.capacity + t0;
     } else {
-      const int page = c.page_table[(int64_t)b * c.pt_stride + (t0 >> 6)];
-      base = (int64_t)page * 64 + (t0 & 63);
-      bad = page < 0 || base + last >= c.num_rows;
+      // The same rule as the decode kernel: the whole page must exist (a
+      // paged pool's num_rows is a multiple of the page size).
+      const int page = c.page_table[(int64_t)b * c.pt_stride + t0 / kPageTokens];
+      const int64_t p0 = (int64_t)page * kPageTokens;
+      base = p0 + t0 % kPageTokens;
+      bad = page < 0 || p0 + kPageTokens > c.num_rows;
     }
     bf16x8 pf[9];
     if (bad) {

@@ -107,6 +107,9 @@ def test_attn_validation(lib):
     assert _attn(lib, cache=_cache(num_rows=100)) == E.MLA_ERR_INVALID_ARG  # B*capacity rows missing
     assert _attn(lib, cache=_cache(page_size=32)) == E.MLA_ERR_UNSUPPORTED
     assert _attn(lib, cache=_cache(page_size=64)) == E.MLA_ERR_INVALID_ARG  # no page table
+    # A paged pool holds whole 64-row pages.
+    assert _attn(lib, cache=_cache(page_size=64, page_table=P, page_table_stride=64, num_rows=4096 + 32)) \
+        == E.MLA_ERR_INVALID_ARG
     assert _attn(lib, cache=_cache(latent_dtype=E.MLA_F32)) == E.MLA_ERR_UNSUPPORTED  # bf16 q, f32 cache
     assert _attn(lib, cache=_cache(latent_dtype=E.MLA_FP4_E2M1_E4M3X16)) == E.MLA_ERR_INVALID_ARG
     assert _attn(lib, dtype=E.MLA_F32) == E.MLA_ERR_UNSUPPORTED  # fp32 q, bf16 cache
