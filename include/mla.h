@@ -228,7 +228,7 @@ MLA_API int mla_decode_attn(const mla_dims* dims, int32_t dtype, const void* q_l
  *   GPU (different streams, or different host threads without ordering)
  *   race and must not be issued; calls ordered on one stream are safe.
  */
-#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
 MLA_API int mla_decode_attn_noalloc(const mla_dims* dims, int32_t dtype, const void* q_lat, const void* q_lat_lo,
                                     const void* q_pe, const mla_kv_cache* cache, const int32_t* seq_lens,
                                     int32_t max_seq_len, float softmax_scale, void* x_lat, float* lse,

@@ -18,7 +18,7 @@ MLA_FP4_E2M1_E4M3X16 = 2
 MLA_ROPE_INTERLEAVED = 0
 MLA_ROPE_HALVES = 1
 MLA_ROPE_LATENT_TAIL = 2
-MLA_NOALLOC_SCRATCH_BYTES = 72 << 20
+MLA_NOALLOC_SCRATCH_BYTES = 40 << 20
 
 EXPORTS = (
     "mla_absorb_q",

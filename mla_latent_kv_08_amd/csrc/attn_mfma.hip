@@ -42,7 +42,8 @@
 // sequences, end to end, are dealt in equal contiguous runs to the W
 // workgroups of each row block. A run that covers a whole sequence writes x
 // and lse directly; a piece of a sequence is written as a partial (x_s
-// normalised and lse_s, both fp32, so that x is rounded to bf16 only once)
+// normalised, as fp16 times a power of two per 128-channel quarter, 11
+// significant bits, so that the rounding that matters is x's own; lse_s fp32)
 // and merged by the combine kernel in fp32:
 //   lse = log sum_s exp(lse_s),  x = sum_s exp(lse_s - lse) x_s.
 #include "internal.h"
@@ -855,7 +856,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           const float m = oref[rb];
           const float l = mt->l[row_local];
           // l = 0: no visible token (x = 0, lse = -inf); a NaN sum stays NaN.
-          const float inv_l = l > 0.0f ? 1.0f / l : (l == 0.0f ? 0.0f : nanv);
+          float inv_l = l > 0.0f ? 1.0f / l : (l == 0.0f ? 0.0f : nanv);
           float lse_v = l > 0.0f ? (m + __log2f(l)) * kLn2 : (l == 0.0f ? -INFINITY : nanv);
           if (seg_bad) lse_v = nanv;
           if (row_ok && cq == 0 && hi == 0) {
@@ -866,6 +867,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
             }
           }
           const bool nan_x = whole && seg_bad;
+          if (!whole) {
+            // A partial row leaves as fp16 times a power of two per 128-channel
+            // quarter, chosen from the quarter's largest |x_s| (lanes l and
+            // l ^ 32 hold the row's quarter) so that it lands in [2^14, 2^15);
+            // the merge multiplies by the inverse, which is exact.
+            float amax = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[rb * 4 + cb][e]));
+            }
+            amax = xor32_max(amax * fabsf(inv_l));
+            const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+            const int fe = (amax == 0.0f || ex == 255) ? 127 : min(253, max(1, 268 - ex));
+            inv_l *= __uint_as_float((uint32_t)fe << 23);
+            if (row_ok && hi == 0) p.part_scale[(prow0 + row_local) * 4 + cq] = __uint_as_float((uint32_t)(254 - fe) << 23);
+          }
           if (staged) {
             // Lane holds row `row_local`, channels 32*cb + 8*i4 + 4*hi + {0..3}.
 #pragma unroll
@@ -881,9 +899,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
               }
             }
             // 16 lanes per row, 8 channels each, to the x row (bf16) or the
-            // partial row (fp32).
+            // partial row (scaled fp16).
             uint16_t* const dst0 = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + rb * 32) * 512;
-            float* const dstp = p.part_x + (prow0 + rb * 32) * 512;
+            uint16_t* const dstp = p.part_x + (prow0 + rb * 32) * 512;
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
               const int r = 4 * it + (lane >> 4);
@@ -897,8 +915,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                       make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
                                  pack_bf16x2(b.z, b.w));
                 } else {
-                  *reinterpret_cast<float4*>(dstp + c) = a;
-                  *reinterpret_cast<float4*>(dstp + c + 4) = b;
+                  *reinterpret_cast<uint4*>(dstp + c) =
+                      make_uint4(pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y),
+                                 pack_f16x2(b.z, b.w));
                 }
               }
             }
@@ -916,8 +935,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                   uint16_t* const xo = reinterpret_cast<uint16_t*>(p.x_lat) + (xrow0 + row_local) * 512;
                   *reinterpret_cast<uint2*>(xo + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 } else {
-                  *reinterpret_cast<float4*>(p.part_x + (prow0 + row_local) * 512 + c) =
-                      make_float4(v[0], v[1], v[2], v[3]);
+                  *reinterpret_cast<uint2*>(p.part_x + (prow0 + row_local) * 512 + c) =
+                      make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
                 }
               }
             }
@@ -990,19 +1009,19 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, i
   float M = -INFINITY, S = 0.0f;
   bool any_nan = false;
   for (int i0 = i_first; i0 <= i_last; i0 += kBatch) {
-    float ls[kBatch];
-    float4 xv[kBatch][2 * kC];
+    float ls[kBatch], qs[kBatch][kC];
+    uint4 xv[kBatch][kC];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool in = i0 + u <= i_last;
       const int64_t prow = prow_of(in ? i0 + u : i_first);
       ls[u] = p.part_lse[prow];
       if (!in) ls[u] = -INFINITY;
-      const float4* src = reinterpret_cast<const float4*>(p.part_x + prow * 512 + c0);
+      const uint4* src = reinterpret_cast<const uint4*>(p.part_x + prow * 512 + c0);
 #pragma unroll
       for (int k = 0; k < kC; ++k) {
-        xv[u][2 * k] = src[2 * L * k];
-        xv[u][2 * k + 1] = src[2 * L * k + 1];
+        xv[u][k] = src[L * k];
+        qs[u][k] = p.part_scale[prow * 4 + ((c0 + 8 * L * k) >> 7)];
       }
     }
     float bm = -INFINITY;
@@ -1022,11 +1041,14 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, i
       const float w = ls[u] == -INFINITY ? 0.0f : __expf(ls[u] - Mn);
       S += w;
 #pragma unroll
-      for (int k = 0; k < 2 * kC; ++k) {
-        acc[4 * k] += w * xv[u][k].x;
-        acc[4 * k + 1] += w * xv[u][k].y;
-        acc[4 * k + 2] += w * xv[u][k].z;
-        acc[4 * k + 3] += w * xv[u][k].w;
+      for (int k = 0; k < kC; ++k) {
+        const float ws = w * qs[u][k];
+        const uint32_t wd[4] = {xv[u][k].x, xv[u][k].y, xv[u][k].z, xv[u][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[8 * k + 2 * e] += ws * f16_lo(wd[e]);
+          acc[8 * k + 2 * e + 1] += ws * f16_hi(wd[e]);
+        }
       }
     }
     M = Mn;

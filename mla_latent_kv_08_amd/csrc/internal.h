@@ -28,7 +28,8 @@ struct AttnParams {
   const int32_t* seq_lens;
   void* x_lat;   // [B, HQ, Ckv]
   float* lse;    // [B, HQ] or null
-  float* part_x;     // [G, 2W, kRowsPerGroup, Ckv] fp32 partial results
+  uint16_t* part_x;   // [G, 2W, kRowsPerGroup, Ckv] partial results: fp16 bits, scaled per quarter
+  float* part_scale;  // [G, 2W, kRowsPerGroup, 4]: the power of two each quarter of part_x is multiplied by
   float* part_lse;  // [G, 2W, kRowsPerGroup] (fp32 path: [B, HQ, S] in the log2 domain)
   float* part_xf;   // fp32 path with S > 1 token splits: [B, HQ, S, Ckv] partial results
   int split_tokens;  // fp32 path: tokens per split

@@ -173,8 +173,9 @@ size_t attn_workspace_bytes(const mla_dims* d, int32_t dtype, int w) {
   const int64_t hq = (int64_t)d->heads * d->q_len;
   const int64_t groups = (hq + kRowsPerGroup - 1) / kRowsPerGroup;
   const int64_t rows = groups * 2 * w * kRowsPerGroup;
-  // partial x [rows, Ckv] fp32, partial lse [rows] fp32, run plan [B + 1] int32
-  return (size_t)(rows * d->d_latent * 4 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
+  // partial x [rows, Ckv] fp16, its scales [rows, 4] fp32, partial lse [rows] fp32,
+  // run plan [B + 1] int32
+  return (size_t)(rows * d->d_latent * 2 + rows * 16 + rows * 4 + ((int64_t)d->batch + 1) * 4 + 256);
 }
 
 }  // namespace
@@ -320,8 +321,9 @@ int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const
   p.groups = (p.HQ + kRowsPerGroup - 1) / kRowsPerGroup;
   p.workgroups = w;
   const int64_t part_rows = (int64_t)p.groups * 2 * w * kRowsPerGroup;
-  p.part_x = static_cast<float*>(workspace);
-  p.part_lse = p.part_x + part_rows * p.Ckv;
+  p.part_x = static_cast<uint16_t*>(workspace);
+  p.part_scale = reinterpret_cast<float*>(p.part_x + part_rows * p.Ckv);
+  p.part_lse = p.part_scale + part_rows * 4;
   p.plan = reinterpret_cast<int*>(p.part_lse + part_rows);
   *out = p;
   return MLA_OK;

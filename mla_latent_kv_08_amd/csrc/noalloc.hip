@@ -12,8 +12,8 @@ namespace {
 
 // Largest scratch the entry point serves (MLA_NOALLOC_SCRATCH_BYTES): the
 // workspace mla_decode_attn needs at its default split on a 256-compute-unit
-// GPU (about 64 MiB of fp32 partials for one workgroup per compute unit)
-// with room to spare.
+// GPU (about 33 MiB of partials for one workgroup per compute unit) with
+// room to spare.
 constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
 
 // One copy per GPU, held until the process ends. In host code this name is a

@@ -117,8 +117,9 @@ def replay(B, H, Q, lens, fp4=False, paged=False, page_table=None, num_rows=None
     xo = Alloc("x", 5 << 40, B * HQ * 1024)
     lse = Alloc("lse", 6 << 40, B * HQ * 4)
     part_rows = G * 2 * W_ * ROWS
-    part_x = Alloc("partial x", 7 << 40, part_rows * 512 * 4)
-    part_lse = Alloc("partial lse", part_x.hi, part_rows * 4)
+    part_x = Alloc("partial x", 7 << 40, part_rows * 512 * 2)
+    part_scale = Alloc("partial scales", part_x.hi, part_rows * 16)
+    part_lse = Alloc("partial lse", part_scale.hi, part_rows * 4)
     plan = Alloc("run plan", part_lse.hi, (B + 1) * 4)
     if paged:
         assert num_rows % PAGE == 0
@@ -220,7 +221,8 @@ def replay(B, H, Q, lens, fp4=False, paged=False, page_table=None, num_rows=None
                     xo.check(xo.lo + (xrow0 + r) * 1024, 1024, "x row")
                     lse.check(lse.lo + (xrow0 + r) * 4, 4, "lse")
                 else:
-                    part_x.check(part_x.lo + (prow0 + r) * 2048, 2048, "partial row")
+                    part_x.check(part_x.lo + (prow0 + r) * 1024, 1024, "partial row")
+                    part_scale.check(part_scale.lo + (prow0 + r) * 16, 16, "partial scales")
                     part_lse.check(part_lse.lo + (prow0 + r) * 4, 4, "partial lse")
                 first = False
                 seg_lo = 0
@@ -237,7 +239,8 @@ def replay(B, H, Q, lens, fp4=False, paged=False, page_table=None, num_rows=None
         for i in range(i_first, i_last + 1):
             slot = 2 * i + (1 if (i == i_first and cum[b] != i_first * per) else 0)
             prow = (g * 2 * W_ + slot) * ROWS + rl
-            part_x.check(part_x.lo + prow * 2048, 2048, "merge partial read")
+            part_x.check(part_x.lo + prow * 1024, 1024, "merge partial read")
+            part_scale.check(part_scale.lo + prow * 16, 16, "merge scale read")
             part_lse.check(part_lse.lo + prow * 4, 4, "merge lse read")
     assert cache.touched > 0
     return cache.touched
