@@ -5,6 +5,8 @@
 // page: steps 1 and 5 of mla_decode_step.) Both stream each head's weight
 // slice once; the bf16 forms run on v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation, the fp32 forms on the vector ALU.
+#include <algorithm>
+
 #include "append_dev.h"
 #include "internal.h"
 
@@ -171,13 +173,12 @@ __global__ void __launch_bounds__(kThreads) absorb_bf16_kernel(ProjParams p) {
   absorb_bf16_block(p, blockIdx.x, blockIdx.y * 128, lds);
 }
 
-// Cache append and query absorption of one decode step in one launch: the
-// first ceil(B*Qn/4) blocks store four new tokens each, one per wave; the
-// blocks after them absorb as above (head = i / (Ckv/128) for absorb block i).
-// The append blocks come first so that they are dispatched with the absorb
-// blocks rather than after them: two absorb blocks fill a compute unit's
-// LDS, so blocks placed after all H*Ckv/128 absorb blocks wait for one of
-// those to finish.
+// Cache append and query absorption of one decode step in one launch. Block
+// i < ceil(B*Qn/4) first stores new tokens 4i .. 4i+3, one per wave; block
+// i < H*Ckv/128 then absorbs (head = i / (Ckv/128)). The grid is the larger of
+// the two counts, so the append adds no blocks to the H*Ckv/128 absorb blocks:
+// two absorb blocks fill a compute unit's LDS, and blocks beyond what the
+// compute units hold at once would wait for a whole absorb block to finish.
 __global__ void __launch_bounds__(kThreads) append_absorb_bf16_kernel(ProjParams p, AppendParams a) {
   __shared__ __attribute__((aligned(16))) AbsorbLds lds;
   const int nc = p.Ckv / 128;
@@ -187,10 +188,8 @@ __global__ void __launch_bounds__(kThreads) append_absorb_bf16_kernel(ProjParams
   if (bid < n_append) {
     const int token = bid * (kThreads / 64) + (int)(threadIdx.x >> 6);
     if (token < tokens) append_token(a, token, threadIdx.x & 63);
-  } else {
-    const int i = bid - n_append;
-    absorb_bf16_block(p, i / nc, (i % nc) * 128, lds);
   }
+  if (bid < p.H * nc) absorb_bf16_block(p, bid / nc, (bid % nc) * 128, lds);
 }
 
 // Up-projection, transposed: out^T[v][m] = sum_c W_UV[v][c] x^T[c][m] for one
@@ -302,7 +301,7 @@ hipError_t launch_absorb(const ProjParams& p, bool bf16, hipStream_t s) {
 
 hipError_t launch_append_absorb_bf16(const ProjParams& p, const AppendParams& a, hipStream_t s) {
   const int64_t tokens = (int64_t)a.B * a.Qn;
-  const int64_t blocks = (int64_t)p.H * (p.Ckv / 128) + (tokens + kThreads / 64 - 1) / (kThreads / 64);
+  const int64_t blocks = std::max<int64_t>((int64_t)p.H * (p.Ckv / 128), (tokens + kThreads / 64 - 1) / (kThreads / 64));
   hipLaunchKernelGGL(append_absorb_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, a);
   return hipGetLastError();
 }
