@@ -104,8 +104,9 @@ def summarize_counters(fetch_dir: str, write_dir: str):
     copy_kib = COPY_BYTES / 1024.0
     f_factor = copy_kib / max(values(fetch, "copyBuffer"))
     w_factor = copy_kib / max(values(write, "copyBuffer"))
-    attn_f = pick(fetch, "attn_mfma_kernel<false>") * 1024.0 * f_factor
-    attn_w = pick(write, "attn_mfma_kernel<false>") * 1024.0 * w_factor
+    # bf16 latent (first template argument false), with or without the low part of q_lat
+    attn_f = pick(fetch, "attn_mfma_kernel<false") * 1024.0 * f_factor
+    attn_w = pick(write, "attn_mfma_kernel<false") * 1024.0 * w_factor
     comb_f = pick(fetch, "attn_combine_kernel") * 1024.0 * f_factor
     comb_w = pick(write, "attn_combine_kernel") * 1024.0 * w_factor
     rec = {
@@ -452,7 +453,7 @@ def main():
                          "and the context figures (copy rate, clocks)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time mla_prefill_attn (chunked and full prefill) and print that record")
-    ap.add_argument("--workload", choices=sorted(OTHER_WORKLOADS),
+    ap.add_argument("--workload", choices=sorted(OTHER_WORKLOADS) + ["v4_form_bf16"],
                     help="only time the attention call of this workload (--steps back-to-back calls) and "
                          "print its record: for profiling runs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -474,6 +475,11 @@ def main():
     from mla_latent_kv_08_amd import ops
 
     dev = torch.device("cuda", 0)
+    if args.workload == "v4_form_bf16":
+        torch.cuda.set_device(dev)
+        rec = measure_v4_form(dev, torch.cuda.current_stream(dev), max(1, args.steps))
+        print(json.dumps({"workload": args.workload, **rec}))
+        return
     if args.workload:
         torch.cuda.set_device(dev)
         rec = measure_other_workloads(dev, torch.cuda.current_stream(dev), max(1, args.steps), lo=not args.no_lo,

@@ -320,32 +320,58 @@ __device__ __forceinline__ void fp4_copy_pieces(const Fp4Copy& f, const uint8_t*
 // Decode part h (tokens 8d + 4h .. +3) of P.V wave d's 8 tokens of a raw
 // tile into the bf16 tile (latent rows with the chunk swizzle, RoPE groups).
 // Lane i: code chunk u = i + 64h (token u / 16, 32 channels at 32 * (u % 16));
-// lanes 0..31 also move RoPE chunk 32h + i.
-__device__ __forceinline__ void fp4_decode_part(const uint8_t* raw, uint8_t* dst, int d, int lane, int h) {
-  {
-    const int u = lane + 64 * h;
-    const int t = 8 * d + (u >> 4);
-    const int j = u & 15;
-    const uint4 cw = *reinterpret_cast<const uint4*>(raw + 8 * d * 256 + u * 16);
-    const uint32_t sc = *reinterpret_cast<const uint16_t*>(raw + kRawScaleBase + 8 * d * 32 + 2 * u);
-    const float s0 = e4m3_value(sc & 0xffu);
-    const float s1 = e4m3_value(sc >> 8);
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+// lanes 0..31 also move RoPE chunk 32h + i. The raw bytes are read into
+// registers first (fp4_load_part) and decoded and written later
+// (fp4_store_part), so that the reads' LDS latency is covered by other work:
+// the compiler, unable to tell the raw slot from the bf16 buffer, would keep
+// each read behind the previous write.
+struct Fp4Part {
+  uint32_t w[4];  // code words, in the order the chunks are written
+  uint32_t sc;    // the chunk's two E4M3 scale bytes
+  uint4 rope;
+};
+
+__device__ __forceinline__ Fp4Part fp4_load_part(const uint8_t* raw, int d, int lane, int h) {
+  Fp4Part f;
+  const int u = lane + 64 * h;
+  const int j = u & 15;
+  const uint8_t* cw = raw + 8 * d * 256 + u * 16;
+  // Lane j writes its four 16-byte chunks 4j .. 4j+3 starting at 4j + j/4,
+  // so in every write the 16 lanes of a token hit 16 different bank groups
+  // (in order, chunk slot mod 16 would take 4 values: 4-way conflicts); the
+  // code words are read in that order.
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const float sv = qd < 2 ? s0 : s1;
-      const int slot = (4 * j + qd) ^ swz(t);
-      *reinterpret_cast<uint4*>(dst + t * kLatRowBytes + slot * 16) =
-          make_uint4(fp4_pair<0>(words[qd], sv), fp4_pair<1>(words[qd], sv), fp4_pair<2>(words[qd], sv),
-                     fp4_pair<3>(words[qd], sv));
-    }
+  for (int r = 0; r < 4; ++r) f.w[r] = *reinterpret_cast<const uint32_t*>(cw + 4 * ((r + (j >> 2)) & 3));
+  f.sc = *reinterpret_cast<const uint16_t*>(raw + kRawScaleBase + 8 * d * 32 + 2 * u);
+  f.rope = *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + ((lane & 31) + 32 * h) * 16);
+  return f;
+}
+
+__device__ __forceinline__ void fp4_store_part(const Fp4Part& f, uint8_t* dst, int d, int lane, int h) {
+  const int u = lane + 64 * h;
+  const int t = 8 * d + (u >> 4);
+  const int j = u & 15;
+  const float2 sv = e4m3_pair(f.sc);
+  uint8_t* row = dst + t * kLatRowBytes;
+  const int fz = swz(t);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qd = (r + (j >> 2)) & 3;
+    const float s = (qd & 2) ? sv.y : sv.x;
+    const uint32_t wd = f.w[r];
+    *reinterpret_cast<uint4*>(row + (((4 * j + qd) ^ fz) << 4)) =
+        make_uint4(fp4_pair<0>(wd, s), fp4_pair<1>(wd, s), fp4_pair<2>(wd, s), fp4_pair<3>(wd, s));
   }
   if (lane < 32) {
     const int c = lane + 32 * h;
-    const int t = 8 * d + (c >> 3), ch = c & 7;
-    *reinterpret_cast<uint4*>(dst + kRopeBase + (t >> 3) * kRopeGroupBytes + ch * 128 + (t & 7) * 16) =
-        *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + c * 16);
+    const int tr = 8 * d + (c >> 3), ch = c & 7;
+    *reinterpret_cast<uint4*>(dst + kRopeBase + (tr >> 3) * kRopeGroupBytes + ch * 128 + (tr & 7) * 16) = f.rope;
   }
+}
+
+__device__ __forceinline__ void fp4_decode_part(const uint8_t* raw, uint8_t* dst, int d, int lane, int h) {
+  const Fp4Part f = fp4_load_part(raw, d, lane, h);
+  fp4_store_part(f, dst, d, lane, h);
 }
 
 // Lane-wise combination across lane groups: lanes l and l ^ 32 (or l ^ 16)
@@ -531,6 +557,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     float m = -INFINITY, l = 0.0f;
     for (int k = 0; k <= count; ++k) {
       lds_barrier();  // step k
+      // FP4: this wave decodes the second half of P.V wave `wave`'s tokens of
+      // tile k+1 (its raw bytes landed before this step's barrier); the raw
+      // bytes are read after S, decoded at the end of the step.
+      const bool dec = kFp4 && k + 1 < count;
+      constexpr int kSlots = kFp4 ? L::kRawSlots : 1;
+      const uint8_t* const dec_raw = smem + L::kRawBase + ((k + 1) % kSlots) * kRawBytes;
+      Fp4Part dp{};
       if (rows_on && k < count) {
         if (k == 0 || sc.tile == 0) {
           // New segment (sequence sc.b).
@@ -594,6 +627,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           }
         }
         __builtin_amdgcn_s_setprio(0);
+        if (dec) dp = fp4_load_part(dec_raw, wave, lane, 1);
 
         // ---- scale, causal limit, row max over the tile ----
         // Lane holds row rl, tokens tok0 + 16*th + i (i < 4). Raw scores; with
@@ -649,15 +683,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           mt->m[rl] = m;
           mt->l[rl] = l;
         }
+      } else if (dec) {
+        dp = fp4_load_part(dec_raw, wave, lane, 1);
       }
-      if constexpr (kFp4) {
-        // Second half of P.V wave `wave`'s tokens of tile k+1 (its raw bytes
-        // landed before this step's barrier).
-        if (k + 1 < count) {
-          fp4_decode_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
-                          smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
-        }
-      }
+      if (dec) fp4_store_part(dp, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
       if (k < count) sc.next(p);
     }
   } else {
@@ -792,6 +821,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       stored = false;
       lds_barrier();  // step k
+      // FP4: the raw bytes of the first half of this wave's tokens of tile k+1
+      // are read first, so that their latency is covered by the reads and
+      // copies below.
+      Fp4Part dp{};
+      if (kFp4 && k + 1 < count) {
+        dp = fp4_load_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes, cq, lane, 0);
+      }
       // References of tile k-1's rows, read before the copies are issued so
       // that their latency is covered.
       float ref[2];
@@ -810,8 +846,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           // The decode bounds the FP4 step, so it issues ahead of the score
           // wave on the same SIMD.
           __builtin_amdgcn_s_setprio(3);
-          fp4_decode_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes,
-                          smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
+          fp4_store_part(dp, smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
           __builtin_amdgcn_s_setprio(0);
         }
       } else if (issued < count) {

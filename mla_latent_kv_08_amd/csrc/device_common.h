@@ -101,16 +101,15 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// Value of an E4M3 ("FN") scale byte, without branches (lanes hold different
-// scales): subnormal m * 2^-9, normal (1 + m/8) * 2^(e-7), NaN for e=15, m=7.
-__device__ __forceinline__ float e4m3_value(uint32_t byte) {
-  const uint32_t e = (byte >> 3) & 0xfu, m = byte & 7u;
-  const float sub = (float)m * 0.001953125f;
-  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  float v = e == 0u ? sub : nrm;
-  v = (e == 15u && m == 7u) ? __uint_as_float(0x7fc00000u) : v;
-  return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
+// Values of E4M3 ("FN") scale bytes: subnormal m * 2^-9, normal
+// (1 + m/8) * 2^(e-7), NaN for e=15, m=7. The hardware FP8 conversion at
+// scale 1 (whose scale only adds to the exponent) gives them exactly: one
+// instruction for the two bytes of the low half of w.
+__device__ __forceinline__ float2 e4m3_pair(uint32_t w) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  return make_float2(r[0], r[1]);
 }
+__device__ __forceinline__ float e4m3_value(uint32_t byte) { return e4m3_pair(byte).x; }
 
 // ---------------------------------------------------------------------------
 // Cache addressing
