@@ -290,15 +290,19 @@ def measure_other_workloads(dev, stream, reps: int, lo: bool = True, names=None)
 
 
 def measure_prefill(dev, stream, reps: int) -> dict:
-    """mla_prefill_attn (non-absorbed, K and V formed per 32-token chunk in LDS) at DeepSeek-V3 dimensions
-    (H=128, Dn=Vd=128, Dr=64, Ckv=512, bf16): chunked prefill, 64 new tokens on a 4096-token cache, B=8;
-    and a full prefill of 4096 tokens, B=1. alg_flops counts each head's K and V made once per token plus
-    the causal score and value products; exec_flops what the kernel issues (the chunks are decompressed
-    again for every 64-query tile)."""
+    """mla_prefill_attn (non-absorbed) at DeepSeek-V3 dimensions (H=128, Dn=Vd=128, Dr=64, Ckv=512, bf16):
+    chunked prefill, 64 new tokens on a 4096-token cache, B=8 (fused path: every chunk's K and V formed once,
+    in LDS); and a full prefill of 4096 tokens, B=1, on the two-kernel path (K and V formed once into a
+    workspace, then flash attention), with the fused path timed beside it. alg_flops counts each head's K and
+    V made once per token plus the causal score and value products; exec_flops what the path issues (the
+    fused path forms the chunks again for every 64-query tile; the two-kernel path forms them once and its
+    attention runs whole 32-token tiles, masked)."""
     import torch
     from mla_latent_kv_08_amd import ops
     out = {}
-    for name, B, Q, L, n in (("chunked_q64_lk4096_b8", 8, 64, 4096, reps), ("full_q4096_b1", 1, 4096, 4096, 3)):
+    for name, B, Q, L, n, two in (("chunked_q64_lk4096_b8", 8, 64, 4096, reps, False),
+                                  ("full_q4096_b1", 1, 4096, 4096, 10, True),
+                                  ("full_q4096_b1_fused", 1, 4096, 4096, 3, False)):
         print(f"bench: prefill {name}", file=sys.stderr, flush=True)
         H, C, R, D = 128, 512, 64, 128
         g = torch.Generator().manual_seed(11)
@@ -311,22 +315,30 @@ def measure_prefill(dev, stream, reps: int) -> dict:
         o = torch.empty(B, H, Q, D, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(B, H, Q, dtype=torch.float32, device=dev)
         scale = 1.0 / math.sqrt(D + R)
-        ms = time_back_to_back(lambda i: ops.mla_prefill_attn(qn, qp, cache, sl, wkv, scale, o, lse, stream=stream),
-                               n, stream)
+        ws_bytes = ops.mla_prefill_workspace_size(B, H, Q, L) if two else 0
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if two else None
+        ms = time_back_to_back(lambda i: ops.mla_prefill_attn(qn, qp, cache, sl, wkv, scale, o, lse, workspace=ws,
+                                                              stream=stream), n, stream)
         if not torch.isfinite(o.float()).all():
             raise SystemExit(f"prefill {name}: non-finite output")
         pairs = sum(L - Q + q + 1 for q in range(Q))
         alg = B * H * (L * 2 * D * C * 2 + pairs * (D + R + D) * 2)
+        qt = 128 if two else 64
         tiles = 0
-        for q0 in range(0, Q, 64):
-            last = L - Q + min(q0 + 63, Q - 1)
+        for q0 in range(0, Q, qt):
+            last = L - Q + min(q0 + qt - 1, Q - 1)
             tiles += last // 32 + 1
-        execf = B * H * tiles * (32 * 2 * D * C * 2 + 64 * 32 * (D + R + D) * 2)
+        attn = B * H * tiles * qt * 32 * (D + R + D) * 2
+        execf = attn + (B * H * ((L + 31) // 32) * 32 * 2 * D * C * 2 if two else B * H * tiles * 32 * 2 * D * C * 2)
         t = ms / 1e3
-        out[name] = {"B": B, "H": H, "Q": Q, "Lk": L, "ms": ms, "alg_flops": alg, "exec_flops": execf,
+        out[name] = {"B": B, "H": H, "Q": Q, "Lk": L, "ms": ms,
+                     "path": "two kernels (K, V formed once into a workspace; flash attention)" if two
+                     else "fused (K, V formed per 64-query tile in LDS)",
+                     "workspace_bytes": ws_bytes, "alg_flops": alg, "exec_flops": execf,
                      "alg_TFLOPs": alg / t / 1e12, "exec_TFLOPs": execf / t / 1e12,
+                     "mfma_frac_alg": alg / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac_exec": execf / t / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-        del buf, cache, qn, qp, wkv, o, lse
+        del buf, cache, qn, qp, wkv, o, lse, ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return out

@@ -31,7 +31,8 @@
  *   mla_grouped_out_proj   V4.1-Flash grouped W_O (one matrix per group of
  *                      heads, outputs joined into the hidden dimension)
  *
- * Helpers: mla_decode_workspace_size, mla_dequant_rows, mla_status_string.
+ * Helpers: mla_decode_workspace_size, mla_prefill_workspace_size,
+ *   mla_dequant_rows, mla_status_string.
  *
  * Sources of the operations: the "MLA decode step" exercise page (6547.cn):
  * the prose on the two score streams, scaling, masking and the low-rank
@@ -251,11 +252,10 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
 
 /*
  * mla_prefill_attn -- attention for many new tokens per sequence in the
- * non-absorbed form: per chunk of 32 cached tokens the per-head keys
- * K = C W_UK^T and values V = C W_UV^T are formed from the latent rows on
- * chip and never written to memory (CANN fused-operator page, section 2: the
- * chunk loop that up-projects K into local memory; exercise page: scores,
- * scaling, causal mask, softmax, values).
+ * non-absorbed form: the per-head keys K = C W_UK^T and values V = C W_UV^T
+ * are formed from the latent rows chunk by chunk (CANN fused-operator page,
+ * section 2: the chunk loop that up-projects K into local memory; exercise
+ * page: scores, scaling, causal mask, softmax, values).
  *   For query row (b, h, q) with L = seq_lens[b] (the Q new tokens included),
  *   the visible positions are t = 0 .. L-Q+q and
  *     s_t  = softmax_scale * (q_nope[b,h,q,:] . K[t] + q_pe[b,h,q,:] . k_pe_t)
@@ -263,20 +263,42 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
  *     lse  = log sum_t exp(s_t) (natural log)   -> lse[b,h,q] (may be NULL)
  *   with K[t] = W_UK[h] c_t and V[t] = W_UV[h] c_t. A row with no visible
  *   position gets out = 0 and lse = -inf. The result equals mla_absorb_q +
- *   mla_decode_attn + mla_up_proj_v up to rounding; this form pays off when
- *   Q is large (each decompressed chunk serves 64 queries of a head).
+ *   mla_decode_attn + mla_up_proj_v up to rounding.
+ *   Two ways to run it, with the same roundings (K, V and probabilities in
+ *   bf16, fp32 accumulation):
+ *    - fused (workspace NULL, or Q below 256): each block of 64 queries of a
+ *      head forms K and V of every 32-token chunk it needs in on-chip memory
+ *      and never writes them out; at Q = 64 every chunk is formed once.
+ *    - two kernels (Q >= 256 and a workspace of mla_prefill_workspace_size
+ *      bytes): K and V are formed once per (token, head) into the workspace,
+ *      then a flash-attention kernel reads them for every query tile. This is
+ *      the form for long prefills, where the fused form would form every
+ *      chunk Q / 64 times.
  *   dtype    MLA_BF16 only, DeepSeek dimensions (Dn = Vd = 128, Dr = 64,
  *            Ckv = 512); fp32 accumulation, bf16 K, V and probabilities
  *   q_nope   [B, H, Q, Dn];  q_pe [B, H, Q, Dr] (already rotated)
  *   cache    bf16 latent and bf16 rope (contiguous or paged); any Q
  *   wkv_b    [H, Dn+Vd, Ckv] bf16;  out [B, H, Q, Vd] bf16
+ *   workspace  NULL (fused path) or device memory of at least
+ *            mla_prefill_workspace_size bytes, 16-byte aligned; a smaller
+ *            non-NULL workspace returns MLA_ERR_WORKSPACE when the two-kernel
+ *            path applies. Its contents are scratch, owned by the caller.
  *   A page index outside the cache turns the outputs of the blocks that read
  *   it into NaN. Returns MLA_ERR_UNSUPPORTED for other dtypes or dimensions.
  *   Device pointers; nothing is allocated; stream-ordered.
  */
 MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* q_pe,
                              const mla_kv_cache* cache, const int32_t* seq_lens, const void* wkv_b,
-                             float softmax_scale, void* out, float* lse, void* stream);
+                             float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * mla_prefill_workspace_size -- bytes of the two-kernel prefill's workspace
+ * for these dims and a cache of `capacity` tokens per sequence:
+ * B * H * ceil(capacity / 32) * 16 KiB (K and V of every token and head,
+ * bf16), or 0 when Q < 256 (the fused path runs). Host-only.
+ */
+MLA_API int mla_prefill_workspace_size(const mla_dims* dims, int32_t capacity, size_t* bytes);
 
 /*
  * mla_up_proj_v -- out[b,h,q,v] = sum_c W_UV[h,v,c] * x_lat[b,h,q,c]

@@ -32,6 +32,7 @@ EXPORTS = (
     "mla_sink_inverse_rope",
     "mla_grouped_out_proj",
     "mla_prefill_attn",
+    "mla_prefill_workspace_size",
     "mla_append_absorb",
     "mla_dequant_rows",
     "mla_status_string",
@@ -116,7 +117,9 @@ def load() -> ctypes.CDLL:
     lib.mla_grouped_out_proj.argtypes = [ctypes.POINTER(MlaDims), I32, I32, I32, P, P, P, P]
     lib.mla_grouped_out_proj.restype = ctypes.c_int
     lib.mla_prefill_attn.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P, P,
-                                     ctypes.c_float, P, P, P]
+                                     ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(MlaDims), I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_workspace_size.restype = ctypes.c_int
     lib.mla_prefill_attn.restype = ctypes.c_int
     lib.mla_append_absorb.argtypes = [ctypes.POINTER(MlaDims), I32, P, P, ctypes.POINTER(MlaKvCache), P,
                                       I32, P, P, P, P, P]

@@ -384,9 +384,20 @@ MLA_API int mla_decode_attn_up(const mla_dims* dims, int32_t dtype, const void* 
   return hip_status(mla::launch_attn_bf16(p, cache->latent_dtype == MLA_FP4_E2M1_E4M3X16, &u, s));
 }
 
+MLA_API int mla_prefill_workspace_size(const mla_dims* dims, int32_t capacity, size_t* bytes) {
+  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+  *bytes = 0;
+  const int st = check_dims(dims);
+  if (st) return st;
+  if (capacity < 0) return MLA_ERR_INVALID_ARG;
+  *bytes = (size_t)mla::prefill_workspace_bytes(dims->batch, dims->heads, dims->q_len, capacity);
+  return MLA_OK;
+}
+
 MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_nope, const void* q_pe,
                              const mla_kv_cache* cache, const int32_t* seq_lens, const void* wkv_b,
-                             float softmax_scale, void* out, float* lse, void* stream) {
+                             float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (dtype != MLA_BF16 || !deepseek_dims(dims)) return MLA_ERR_UNSUPPORTED;
@@ -403,6 +414,11 @@ MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_
       dims->batch > 65535) {
     return MLA_ERR_UNSUPPORTED;
   }
+  // The two-kernel path runs when it applies (Q large enough) and a
+  // workspace is given; it must then be large enough.
+  const int64_t need = mla::prefill_workspace_bytes(dims->batch, dims->heads, dims->q_len, cache->capacity);
+  const bool two = need > 0 && workspace != nullptr;
+  if (two && ((size_t)need > workspace_bytes || !aligned16(workspace))) return MLA_ERR_WORKSPACE;
   if (dims->batch == 0) return MLA_OK;
   mla::PrefillParams p{};
   p.q_nope = q_nope;
@@ -416,6 +432,8 @@ MLA_API int mla_prefill_attn(const mla_dims* dims, int32_t dtype, const void* q_
   p.H = dims->heads;
   p.Q = dims->q_len;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.kv_ws = two ? workspace : nullptr;
+  p.Lt = (cache->capacity + 31) / 32;
   return hip_status(mla::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -18,7 +18,15 @@ struct PrefillParams {
   float* lse;
   int B, H, Q;
   float scale_log2;  // softmax_scale * log2(e)
+  // Two-kernel path (decompress once, then flash attention) when non-null:
+  // Lt tiles of 32 tokens per (b, h), as sized by prefill_workspace_bytes.
+  void* kv_ws;
+  int Lt;
 };
+// Queries per sequence from which the two-kernel path is used.
+constexpr int kPrefillTwoKernelMinQ = 256;
+// Workspace bytes of the two-kernel path (0 when Q is below the threshold).
+int64_t prefill_workspace_bytes(int B, int H, int Q, int capacity);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 
 }  // namespace mla

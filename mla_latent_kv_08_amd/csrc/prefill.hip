@@ -259,12 +259,314 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Long prefill in two kernels: the per-head keys and values are decompressed
+// once per (token, head) into a workspace, then a flash-attention kernel
+// streams them for every query tile. (CANN page, section 2: each chunk of
+// the latent is decompressed once; the fused kernel above repeats that for
+// every 64-query tile, which at Q = Lk is Q / 64 times the work.)
+//
+// Workspace: per (b, h) Lt = ceil(capacity / 32) tiles of 16 KiB each, tile
+// j holding K[32 tokens][128] (token-major) then V^T[128][32] (value-major),
+// bf16, tokens 32j .. 32j+31; rows past the sequence's length are zero.
+// ---------------------------------------------------------------------------
+constexpr int kKvTilesPerBlock = 8;  // tiles (of 32 tokens) per block of the decompression
+constexpr int kWsTileBytes = 2 * kPfT * 128 * 2;
+constexpr int kKsPitch = 136;        // K staging row pitch (bf16): 128 + 8
+
+struct KvLds {
+  uint16_t c[kPfT * kCPitch];
+  uint16_t k[kPfT * kKsPitch];
+  uint16_t vt[128 * kVPitch];
+};
+
+// First physical row of tile `t0 / 32` of sequence b, or -1 for a page index
+// outside the cache (the same whole-page rule as the fused kernel).
+__device__ __forceinline__ int64_t pf_tile_base(const CacheView& c, int b, int t0) {
+  if (c.page_size == 0) return (int64_t)b * c.capacity + t0;
+  const int page = c.page_table[(int64_t)b * c.pt_stride + t0 / kPageTokens];
+  const int64_t p0 = (int64_t)page * kPageTokens;
+  if (page < 0 || p0 + kPageTokens > c.num_rows) return -1;
+  return p0 + t0 % kPageTokens;
+}
+
+// Block (chunk of kKvTilesPerBlock tiles, head h, sequence b), 512 threads:
+// wave w holds weight rows as in the fused kernel and forms its 32 x 32
+// slice of K or V per tile; the tile leaves through LDS as whole rows.
+__global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) KvLds s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const CacheView& c = p.cache;
+  const int len = clamp_len(p.seq_lens[b], c.capacity);
+  const int n_tiles = (len + kPfT - 1) / kPfT;
+  const int tile0 = blockIdx.x * kKvTilesPerBlock;
+  if (tile0 >= n_tiles) return;
+  const int tile1 = min(n_tiles, tile0 + kKvTilesPerBlock);
+  const uint16_t* wkv = reinterpret_cast<const uint16_t*>(p.wkv_b) + (int64_t)h * 256 * 512;
+  bf16x8 wf[32];
+  {
+    const uint16_t* wr = wkv + (int64_t)((wave >= 4 ? 128 : 0) + 32 * (wave & 3) + (lane & 31)) * 512 + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) wf[ks] = *reinterpret_cast<const bf16x8*>(wr + 16 * ks);
+  }
+  uint8_t* ws = reinterpret_cast<uint8_t*>(p.kv_ws) + ((int64_t)b * p.H + h) * p.Lt * kWsTileBytes;
+  // Thread tid moves 16-byte chunk tid % 64 of latent rows tid / 64 + 8j.
+  const int cc = tid & 63, r0 = tid >> 6;
+  auto load = [&](int tile, bf16x8* v) {
+    const int t0 = tile * kPfT;
+    const int last = min(kPfT - 1, len - 1 - t0);
+    const int64_t base = pf_tile_base(c, b, t0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + 8 * j;
+      v[j] = bf16x8{};
+      if (base >= 0 && r <= last) {
+        v[j] = *reinterpret_cast<const bf16x8*>(c.latent + (base + r) * c.latent_stride + cc * 16);
+      }
+    }
+  };
+  bf16x8 v[4];
+  load(tile0, v);
+  for (int tile = tile0; tile < tile1; ++tile) {
+    __syncthreads();  // the previous tile's readers and copies are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(&s.c[(r0 + 8 * j) * kCPitch + cc * 8]) = v[j];
+    if (tile + 1 < tile1) load(tile + 1, v);
+    __syncthreads();
+    floatx16 acc = floatx16{};
+    const uint16_t* a = &s.c[(lane & 31) * kCPitch + 8 * hi];
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0, 0,
+                                                    0);
+      if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    // D lane l: column n = 32(w%4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
+    const int n = 32 * (wave & 3) + (lane & 31);
+    if (wave < 4) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s.k[(8 * (i >> 2) + 4 * hi + (i & 3)) * kKsPitch + n] = to_bf16(acc[i]);
+    } else {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 8 * i4 + 4 * hi]) =
+            make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+      }
+    }
+    __syncthreads();
+    uint8_t* wt = ws + (int64_t)tile * kWsTileBytes;
+    *reinterpret_cast<uint4*>(wt + (tid >> 4) * 256 + (tid & 15) * 16) =
+        *reinterpret_cast<const uint4*>(&s.k[(tid >> 4) * kKsPitch + (tid & 15) * 8]);
+    *reinterpret_cast<uint4*>(wt + kPfT * 256 + (tid >> 2) * 64 + (tid & 3) * 16) =
+        *reinterpret_cast<const uint4*>(&s.vt[(tid >> 2) * kVPitch + (tid & 3) * 8]);
+  }
+}
+
+// Row reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15), on the
+// VALU: swap within pairs, within quads, mirror within half-rows, mirror
+// within the row; every lane ends with the row's result.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x + dpp_f<0x140>(x);
+}
+
+constexpr int kFaQ = 128;  // queries per flash-attention block (16 per wave)
+
+struct FaLds {
+  uint16_t k[2][kPfT * kKPitch];   // [token][128 decompressed | 64 RoPE | pad]
+  uint16_t vt[2][128 * kVPitch];   // [value dim][token]
+  uint16_t p[8][16 * kPPitch];
+  int bad;
+};
+
+// Block of 128 queries of one (b, h), 512 threads; every wave takes 16
+// queries: S = [q_nope | q_pe] . [K | k_pe]^T (16x16x32 matrix ops, query
+// fragments in registers), scale, causal limit, online softmax, O += P V.
+// All threads move the next tile into the other LDS buffer (prefetched into
+// registers one tile ahead), so one barrier per tile suffices. Blocks are
+// dealt so that the query tiles of a (b, h) run on one XCD and share its L2,
+// heaviest (last) query tiles first.
+__global__ void __launch_bounds__(kPfThreads) prefill_fa_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) FaLds s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nqt = (p.Q + kFaQ - 1) / kFaQ;
+  const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
+  const int unit = xcd + 8 * (r / nqt);
+  if (unit >= p.B * p.H) return;
+  const int qt = nqt - 1 - r % nqt;
+  const int b = unit / p.H, h = unit % p.H;
+  const int H = p.H, Q = p.Q;
+  const CacheView& c = p.cache;
+  const int len = clamp_len(p.seq_lens[b], c.capacity);
+  const int q0 = qt * kFaQ;
+  const int pos_max = len - Q + min(q0 + kFaQ - 1, Q - 1);
+  const int n_tiles = pos_max < 0 ? 0 : min(pos_max / kPfT + 1, (len + kPfT - 1) / kPfT);
+  const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.kv_ws) + ((int64_t)b * H + h) * p.Lt * kWsTileBytes;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // Query fragments (A operand): query q0 + 16w + l%16, dims 32ks + 8(l/16) .. +7.
+  bf16x8 qa[6];
+  {
+    const int qi = min(q0 + 16 * wave + l16, Q - 1);
+    const int64_t row = ((int64_t)b * H + h) * Q + qi;
+    const uint16_t* qn = reinterpret_cast<const uint16_t*>(p.q_nope) + row * 128 + 8 * g4;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_pe) + row * 64 + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = *reinterpret_cast<const bf16x8*>(qn + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qa[4 + ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+  }
+  if (tid == 0) s.bad = 0;
+
+  // Tile moves: thread tid carries K row tid / 16 chunk tid % 16, V^T row
+  // tid / 4 chunk tid % 4 and, for tid < 256, RoPE row tid / 8 chunk tid % 8.
+  struct Tile {
+    uint4 k, v, r;
+    int bad;
+  };
+  auto load = [&](int tile) {
+    Tile t;
+    const uint8_t* wt = ws + (int64_t)tile * kWsTileBytes;
+    t.k = *reinterpret_cast<const uint4*>(wt + (tid >> 4) * 256 + (tid & 15) * 16);
+    t.v = *reinterpret_cast<const uint4*>(wt + kPfT * 256 + (tid >> 2) * 64 + (tid & 3) * 16);
+    const int t0 = tile * kPfT;
+    const int64_t base = pf_tile_base(c, b, t0);
+    t.bad = base < 0 ? 1 : 0;
+    const int rr = (tid >> 3) & 31;
+    t.r = make_uint4(0, 0, 0, 0);
+    if (tid < 256 && base >= 0 && t0 + rr < len) {
+      t.r = *reinterpret_cast<const uint4*>(c.rope + (base + rr) * c.rope_stride + (tid & 7) * 16);
+    }
+    return t;
+  };
+  auto store = [&](const Tile& t, int buf) {
+    *reinterpret_cast<uint4*>(&s.k[buf][(tid >> 4) * kKPitch + (tid & 15) * 8]) = t.k;
+    *reinterpret_cast<uint4*>(&s.vt[buf][(tid >> 2) * kVPitch + (tid & 3) * 8]) = t.v;
+    if (tid < 256) *reinterpret_cast<uint4*>(&s.k[buf][(tid >> 3) * kKPitch + 128 + (tid & 7) * 8]) = t.r;
+    if (t.bad) s.bad = 1;
+  };
+
+  float m[4], l[4];
+  floatx4 o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+  }
+#pragma unroll
+  for (int vb = 0; vb < 8; ++vb) o[vb] = floatx4{};
+  Tile nx{};
+  __syncthreads();  // the flag is cleared before any store can set it
+  if (n_tiles > 0) store(load(0), 0);
+  if (n_tiles > 1) nx = load(1);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int t0 = tile * kPfT;
+    const int buf = tile & 1;
+    // Tile+1 goes to the buffer tile-1 left (its readers passed the last
+    // barrier); tile+2 is requested.
+    if (tile + 1 < n_tiles) store(nx, buf ^ 1);
+    if (tile + 2 < n_tiles) nx = load(tile + 2);
+    floatx4 sc[2] = {floatx4{}, floatx4{}};
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const uint16_t* kr = &s.k[buf][(16 * tb + l16) * kKPitch + 8 * g4];
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) {
+        sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(kr + 32 * ks),
+                                                         sc[tb], 0, 0, 0);
+      }
+    }
+    // S lane l: token t0 + 16tb + l%16, queries q0 + 16w + 4(l/16) + i.
+    float pr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qg = q0 + 16 * wave + 4 * g4 + i;
+      const int pos = len - Q + qg;
+      float x[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int t = t0 + 16 * tb + l16;
+        x[tb] = (qg < Q && t <= pos && t < len) ? sc[tb][i] * p.scale_log2 : -INFINITY;
+      }
+      const float mx = row16_max(fmaxf(x[0], x[1]));
+      const float m_new = fmaxf(m[i], mx);
+      const float alpha = m_new == m[i] ? 1.0f : __builtin_amdgcn_exp2f(m[i] - m_new);
+      const float mu = m_new == -INFINITY ? 0.0f : m_new;
+      pr[0][i] = __builtin_amdgcn_exp2f(x[0] - mu);
+      pr[1][i] = __builtin_amdgcn_exp2f(x[1] - mu);
+      l[i] = l[i] * alpha + row16_sum(pr[0][i] + pr[1][i]);
+      m[i] = m_new;
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) o[vb][i] *= alpha;
+    }
+    // P to this wave's LDS rows [query 4(l/16)+i][token 16tb + l%16], read
+    // back as the A operand (query l%16, tokens 8(l/16) .. +7).
+    uint16_t* pw = s.p[wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) pw[(4 * g4 + i) * kPPitch + 16 * tb + l16] = to_bf16(pr[tb][i]);
+    }
+    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pw[l16 * kPPitch + 8 * g4]);
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      const bf16x8 vbk = *reinterpret_cast<const bf16x8*>(&s.vt[buf][(16 * vb + l16) * kVPitch + 8 * g4]);
+      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbk, o[vb], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  const bool bad = s.bad != 0;
+  const float nanv = __uint_as_float(0x7fc00000u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qg = q0 + 16 * wave + 4 * g4 + i;
+    if (qg >= Q) continue;
+    const int64_t row = ((int64_t)b * H + h) * Q + qg;
+    const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + row * 128;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) orow[16 * vb + l16] = to_bf16(bad ? nanv : o[vb][i] * inv);
+    if (p.lse != nullptr && l16 == 0) {
+      p.lse[row] = bad ? nanv : (l[i] > 0.0f ? (m[i] + __log2f(l[i])) * kLn2 : -INFINITY);
+    }
+  }
+}
+
 }  // namespace
+
+int64_t prefill_workspace_bytes(int B, int H, int Q, int capacity) {
+  if (Q < kPrefillTwoKernelMinQ || B <= 0 || H <= 0) return 0;
+  return (int64_t)B * H * ((capacity + kPfT - 1) / kPfT) * kWsTileBytes;
+}
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
   if (p.B == 0 || p.Q == 0) return hipSuccess;
-  const int qt = (p.Q + kPfQ - 1) / kPfQ;
   if (p.H > 65535 || p.B > 65535) return hipErrorInvalidConfiguration;
+  if (p.kv_ws != nullptr) {
+    const int chunks = (p.Lt + kKvTilesPerBlock - 1) / kKvTilesPerBlock;
+    if (chunks > 0) hipLaunchKernelGGL(prefill_kv_kernel, dim3(chunks, p.H, p.B), dim3(kPfThreads), 0, s, p);
+    const int64_t units = ((int64_t)p.B * p.H + 7) / 8 * 8;
+    const int64_t blocks = units * ((p.Q + kFaQ - 1) / kFaQ);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(prefill_fa_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, s, p);
+    return hipGetLastError();
+  }
+  const int qt = (p.Q + kPfQ - 1) / kPfQ;
   hipLaunchKernelGGL(prefill_kernel, dim3(qt, p.H, p.B), dim3(kPfThreads), 0, s, p);
   return hipGetLastError();
 }

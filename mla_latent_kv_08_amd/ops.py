@@ -205,11 +205,22 @@ def mla_decode_attn_noalloc(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: Late
         _stream(stream)), "mla_decode_attn_noalloc")
 
 
+def mla_prefill_workspace_size(B: int, H: int, Q: int, capacity: int, Dn: int = 128, Dr: int = 64, Vd: int = 128,
+                               Ckv: int = 512) -> int:
+    """Bytes of the two-kernel prefill's workspace (0 when Q < 256); see include/mla.h."""
+    d = _dims(B, H, Q, Dn, Dr, Vd, Ckv)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().mla_prefill_workspace_size(ctypes.byref(d), int(capacity), ctypes.byref(n)),
+               "mla_prefill_workspace_size")
+    return int(n.value)
+
+
 def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache, seq_lens: torch.Tensor,
                      wkv_b: torch.Tensor, softmax_scale: float, out: torch.Tensor,
-                     lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Non-absorbed attention with K and V formed from the latent on chip; see mla_prefill_attn in
-    include/mla.h."""
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Non-absorbed attention with K and V formed from the latent: fused on chip without a workspace, in two
+    kernels (K and V formed once, then flash attention) with one; see mla_prefill_attn in include/mla.h."""
     B, H, Q, Dn = q_nope.shape
     Dr = q_pe.shape[-1]
     Vd = out.shape[-1]
@@ -220,9 +231,11 @@ def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCach
         raise TypeError("lse must be float32")
     d = _dims(B, H, Q, Dn, Dr, Vd, Ckv)
     desc = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(_lib.load().mla_prefill_attn(
         ctypes.byref(d), _code(q_nope), _ptr(q_nope), _ptr(q_pe), ctypes.byref(desc), _ptr(seq_lens),
-        _ptr(wkv_b), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)), "mla_prefill_attn")
+        _ptr(wkv_b), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
+        "mla_prefill_attn")
 
 
 def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,

@@ -208,10 +208,10 @@ def test_prefill_attn_validation(lib):
     E = _lib
     byref = ctypes.byref
 
-    def call(dims=None, dtype=E.MLA_BF16, cache=None, qn=P, qp=P, sl=P, wkv=P, out=P):
+    def call(dims=None, dtype=E.MLA_BF16, cache=None, qn=P, qp=P, sl=P, wkv=P, out=P, ws=None, ws_bytes=0):
         c = cache or _cache()
         return lib.mla_prefill_attn(byref(dims or _dims(q_len=256)), dtype, qn, qp, byref(c), sl, wkv, 0.1, out,
-                                    None, None)
+                                    None, ws, ws_bytes, None)
     assert call(dtype=E.MLA_F32) == E.MLA_ERR_UNSUPPORTED
     assert call(dims=_dims(q_len=256, d_v=64)) == E.MLA_ERR_UNSUPPORTED
     assert call(cache=_cache(latent_dtype=E.MLA_F32, latent_stride=2048)) == E.MLA_ERR_UNSUPPORTED
@@ -221,6 +221,23 @@ def test_prefill_attn_validation(lib):
     assert call(sl=None) == E.MLA_ERR_INVALID_ARG
     assert call(cache=_cache(num_rows=100)) == E.MLA_ERR_INVALID_ARG  # 2 x 4096 rows do not fit
     assert call(dims=_dims(q_len=256, batch=0)) == E.MLA_OK
+    # Two-kernel path (Q >= 256 with a workspace): too small or misaligned.
+    assert call(ws=P, ws_bytes=1 << 20) == E.MLA_ERR_WORKSPACE
+    assert call(ws=P + 8, ws_bytes=1 << 40) == E.MLA_ERR_WORKSPACE
+
+
+def test_prefill_workspace_size(lib):
+    """B * H * ceil(capacity / 32) tiles of 16 KiB (K [32][128] and V^T [128][32], bf16) from Q = 256 on;
+    0 below (the fused path needs none)."""
+    byref = ctypes.byref
+    n = ctypes.c_size_t(7)
+    for B, H, Q, cap in ((2, 128, 256, 4096), (1, 128, 4096, 4096), (3, 5, 300, 1000), (2, 128, 255, 4096),
+                         (8, 128, 64, 4096), (1, 1, 256, 0)):
+        assert lib.mla_prefill_workspace_size(byref(_dims(batch=B, heads=H, q_len=Q)), cap, byref(n)) == 0
+        want = 0 if Q < 256 else B * H * ((cap + 31) // 32) * 16384
+        assert n.value == want, (B, H, Q, cap, n.value)
+    assert lib.mla_prefill_workspace_size(byref(_dims()), -1, byref(n)) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_workspace_size(byref(_dims()), 64, None) == _lib.MLA_ERR_INVALID_ARG
 
 
 def test_attn_noalloc_validation(lib):
