@@ -345,12 +345,13 @@ def measure_prefill(dev, stream, reps: int) -> dict:
 
 
 def measure_v4_form(dev, stream, reps: int) -> dict:
-    """The DeepSeek-V4.1-Flash form at the headline's cache size: 64 query heads over one bf16 latent
-    whose last 64 dims carry the rotation, B=32, Lk=4096, Q=1, two rotated cache copies (302 MB, past the
-    MALL). Each call alone and the chain of the three, back to back: mla_rope_append in latent-tail mode
-    (the step's new token and its 64 query rows), mla_decode_attn with an all-zero q_pe,
-    mla_sink_inverse_rope (sink column, x's tail turned back), mla_grouped_out_proj (8 groups x 1024,
-    random bf16 W_O, 67 MB)."""
+    """The DeepSeek-V4.1-Flash form at the headline's cache size: 64 query heads over one latent whose last
+    64 dims carry the rotation, B=32, Lk=4096, Q=1, on the form's own rows (no RoPE section): bf16 1024-byte
+    rows (3 rotated copies, 403 MB) and FP4 288-byte rows of codes and scales (8 copies, 302 MB), both past
+    the MALL; and, for comparison, DeepSeek-V3 rows with a zero 64-dim RoPE slot (1152 B, 2 copies). Each
+    attention call alone, and the chain on the bf16 own rows, back to back: mla_rope_append in latent-tail
+    mode (the step's new token and its 64 query rows), mla_decode_attn, mla_sink_inverse_rope (sink
+    column, x's tail turned back), mla_grouped_out_proj (8 groups x 1024, random bf16 W_O, 67 MB)."""
     import torch
     import workloads as W
     from mla_latent_kv_08_amd import ops
@@ -360,12 +361,17 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
     hist = torch.randn(B, L, C, generator=g).to(torch.bfloat16).to(dev)
     sl = torch.full((B,), L, dtype=torch.int32, device=dev)
     table = W.rope_table(L, R).to(dev)
-    caches = []
-    for _ in range(2):
-        buf = torch.zeros(B * L, C + R, dtype=torch.bfloat16, device=dev)
-        cache = ops.LatentCache.combined(buf, C, L)
+
+    def fill(cache):
         ops.mla_rope_append(hist, None, cache, sl, table, latent_tail=True, stream=stream)
-        caches.append(cache)
+        return cache
+    own = [fill(ops.LatentCache.latent_only(torch.zeros(B * L, C, dtype=torch.bfloat16, device=dev), C, L))
+           for _ in range(3)]
+    fp4_row = ops.LatentCache.fp4_row_bytes(C, 0)
+    fp4 = [fill(ops.LatentCache.fp4(torch.zeros(B * L, fp4_row, dtype=torch.uint8, device=dev), C, L, rope=False))
+           for _ in range(8)]
+    v3rows = [fill(ops.LatentCache.combined(torch.zeros(B * L, C + R, dtype=torch.bfloat16, device=dev), C, L))
+              for _ in range(2)]
     new = hist[:, L - Q:].contiguous()
     del hist
     q = torch.randn(B, H, Q, C, generator=g).to(torch.bfloat16).to(dev)
@@ -377,10 +383,16 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
     scale = 1.0 / math.sqrt(C)
 
     def rope(i):
-        ops.mla_rope_append(new, None, caches[i % 2], sl, table, q_pe=q, latent_tail=True, stream=stream)
+        ops.mla_rope_append(new, None, own[i % len(own)], sl, table, q_pe=q, latent_tail=True, stream=stream)
 
     def attn(i):
-        ops.mla_decode_attn(q, zero_pe, caches[i % 2], sl, L, scale, x, lse, workspace=ws, stream=stream)
+        ops.mla_decode_attn(q, None, own[i % len(own)], sl, L, scale, x, lse, workspace=ws, stream=stream)
+
+    def attn_fp4(i):
+        ops.mla_decode_attn(q, None, fp4[i % len(fp4)], sl, L, scale, x, lse, workspace=ws, stream=stream)
+
+    def attn_v3rows(i):
+        ops.mla_decode_attn(q, zero_pe, v3rows[i % len(v3rows)], sl, L, scale, x, lse, workspace=ws, stream=stream)
 
     def sink(i):
         ops.mla_sink_inverse_rope(x, lse, sl, sinks, table, stream=stream)
@@ -398,23 +410,35 @@ def measure_v4_form(dev, stream, reps: int) -> dict:
         sink(i)
         out_proj(i)
 
-    rec = {"B": B, "H": H, "Q": Q, "Lk": L, "cache": "contiguous, bf16 latent (tail rotated), zero RoPE slot"}
-    for name, fn in (("rope_append_ms", rope), ("attn_ms", attn), ("sink_inverse_rope_ms", sink),
-                     ("grouped_out_proj_ms", out_proj), ("chain_ms", chain)):
+    rec = {"B": B, "H": H, "Q": Q, "Lk": L,
+           "cache": "contiguous, the form's own rows: bf16 latent (tail rotated), no RoPE section, 1024 B"}
+    for name, fn in (("attn_fp4_ms", attn_fp4), ("attn_v3_rows_ms", attn_v3rows), ("rope_append_ms", rope),
+                     ("attn_ms", attn), ("sink_inverse_rope_ms", sink), ("grouped_out_proj_ms", out_proj),
+                     ("chain_ms", chain)):
         rec[name] = time_back_to_back(fn, reps, stream)
     if not torch.isfinite(x.float()).all():
         raise SystemExit("v4_form_bf16: non-finite output")
-    cache_b = B * L * (C + R) * 2
-    io_b = B * H * Q * ((C + R) * 2 + C * 2 + 4)
-    flops = B * H * Q * L * 2 * (C + R + C)
-    t = rec["attn_ms"] / 1e3
-    t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
-    rec.update({"cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops, "kv_GBps": cache_b / t / 1e9,
-                "bound": "hbm", "t_roofline_us": t_hbm * 1e6, "roofline_frac": t_hbm / t,
+    io_b = B * H * Q * (C * 2 + C * 2 + 4)
+    flops = B * H * Q * L * 2 * (C + C)
+    mfma_t = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+
+    def roof(cache_b, ms):
+        t = ms / 1e3
+        t_hbm = (cache_b + io_b) / (HBM_PEAK_GBPS * 1e9)
+        bound = "hbm" if t_hbm >= mfma_t else "mfma"
+        return {"cache_bytes": cache_b, "io_bytes": io_b, "alg_flops": flops, "ms": ms,
+                "kv_GBps": cache_b / t / 1e9, "bound": bound, "t_roofline_us": max(t_hbm, mfma_t) * 1e6,
+                "roofline_frac": max(t_hbm, mfma_t) / t}
+    rec["own_rows_bf16"] = roof(B * L * C * 2, rec["attn_ms"])
+    rec["own_rows_fp4"] = roof(B * L * fp4_row, rec["attn_fp4_ms"])
+    # V3 rows: the zero RoPE slot is read but carries nothing, so the fraction counts the latent bytes only.
+    rec["v3_rows_zero_rope_slot"] = roof(B * L * C * 2, rec["attn_v3_rows_ms"])
+    rec.update({"bound": "hbm", "t_roofline_us": rec["own_rows_bf16"]["t_roofline_us"],
+                "roofline_frac": rec["own_rows_bf16"]["roofline_frac"],
                 "tokens_per_s": B * Q / (rec["chain_ms"] / 1e3),
                 "grouped_out_proj": {"groups": G, "group_out": N, "weight_bytes": G * N * (H // G) * C * 2,
                                      "GBps": G * N * (H // G) * C * 2 / (rec["grouped_out_proj_ms"] / 1e3) / 1e9}})
-    del caches, x, q, w_o, hidden
+    del own, fp4, v3rows, x, q, w_o, hidden
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec

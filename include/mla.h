@@ -129,6 +129,15 @@ typedef struct mla_dims {
  * FP4 latent rows: byte i of a row holds channel 2i in its low nibble and
  * channel 2i+1 in its high nibble (E2M1: sign, 2 exponent bits, 1 mantissa
  * bit); the scale row holds Ckv/16 E4M3 ("FN") bytes in channel-group order.
+ *
+ * Without a RoPE section (rope NULL and rope_stride 0): the DeepSeek-V4.1-Flash
+ * layout of the course page (block 4A, section 1 and the figure of section
+ * 2: one 512-wide latent whose last 64 dims carry the rotation; 1024 B per
+ * bf16 row, 288 B per FP4 row of codes and scales). Accepted by the bf16 /
+ * FP4 decode attention (scores over the latent alone, q_pe NULL), by
+ * mla_cache_append with k_pe_new NULL, by mla_rope_append in latent-tail
+ * mode and by mla_dequant_rows; every other call returns
+ * MLA_ERR_INVALID_ARG for it.
  */
 typedef struct mla_kv_cache {
   int32_t latent_dtype; /* MLA_F32, MLA_BF16 or MLA_FP4_E2M1_E4M3X16 */
@@ -197,7 +206,10 @@ MLA_API int mla_decode_workspace_size(const mla_dims* dims, int32_t dtype, int32
  *                MLA_BF16: q_lat/q_pe/x_lat bf16, cache latent bf16 or FP4,
  *                rope bf16; products on bf16 matrix cores, fp32 accumulation,
  *                probabilities rounded to bf16 before the weighted sum.
- *   q_lat        [B, H, Q, Ckv];  q_pe [B, H, Q, Dr]
+ *   q_lat        [B, H, Q, Ckv];  q_pe [B, H, Q, Dr], or NULL exactly when the
+ *                cache has no RoPE section (MLA_BF16 only): then
+ *                s_t = softmax_scale * q_lat[b,h,q,:] . c_t, over the Ckv
+ *                latent channels alone (the rotation is in c_t's tail).
  *   q_lat_lo     MLA_BF16 only, or NULL: [B, H, Q, Ckv] bf16 low part of the
  *                query (as mla_absorb_q writes it). The latent score stream
  *                is then q_lat.c + q_lat_lo.c, both on the matrix cores with
@@ -321,6 +333,7 @@ MLA_API int mla_up_proj_v(const mla_dims* dims, int32_t dtype, const void* x_lat
  *              channels, element = nearest E2M1 value of x/scale, ties to the
  *              even code, saturating; scale 0 -> all-zero codes).
  *   c_kv_new   [B, Q, Ckv];  k_pe_new [B, Q, Dr] in the cache's rope dtype
+ *              (NULL, and nothing stored, for a cache without a RoPE section)
  */
 MLA_API int mla_cache_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new,
                              const void* k_pe_new, const mla_kv_cache* cache,

@@ -159,9 +159,10 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
   const CacheView& c = p.cache;
   const bool rotate = p.cos_sin != nullptr;
   const bool tail = rotate && p.rope_tail;
+  const bool has_rope = c.rope != nullptr;  // no RoPE section: the rotation lives in the latent's tail
   // Words copied as they are: the RoPE key only when it is not rotated; the
   // latent, without its tail in latent-tail mode.
-  const int rope_words = rotate ? 0 : p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
+  const int rope_words = rotate || !has_rope ? 0 : p.Dr * (p.rope_dtype == MLA_F32 ? 4 : 2) / 4;
   const bool fp4 = p.latent_dtype == MLA_FP4_E2M1_E4M3X16;
   const int lat_words = fp4 ? 0 : (tail ? p.Ckv - p.Dr : p.Ckv) * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
   const int64_t lat_src_words = fp4 ? 0 : p.Ckv * (p.latent_dtype == MLA_F32 ? 4 : 2) / 4;
@@ -208,7 +209,7 @@ __device__ __forceinline__ void append_token(const AppendParams& p, int token, i
   }
   if (tail) {
     for (int u = lane; u < p.Dr; u += 64) {
-      store_dst(const_cast<uint8_t*>(c.rope) + r * c.rope_stride, u, p.rope_dtype, 0.0f);
+      if (has_rope) store_dst(const_cast<uint8_t*>(c.rope) + r * c.rope_stride, u, p.rope_dtype, 0.0f);
       if (!fp4) store_dst(lat, (p.Ckv - p.Dr) + u, p.latent_dtype, tail_value(p, src_row, u, pos));
     }
   }

@@ -301,13 +301,14 @@ __device__ __forceinline__ Fp4Copy fp4_copy(const CacheView& c, int64_t row0, in
   return f;
 }
 
+template <bool kRope>
 __device__ __forceinline__ void fp4_copy_pieces(const Fp4Copy& f, const uint8_t* raw, int d, int lane) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = 8 * d + 4 * h + (lane >> 4);
     lds_copy16(f.codes, lds_addr(raw + (8 * d + 4 * h) * 256), (int)(t * f.cs) + ((lane & 15) << 4));
   }
-  {
+  if constexpr (kRope) {
     const int t = 8 * d + (lane >> 3);
     lds_copy16(f.rope, lds_addr(raw + kRawRopeBase + 8 * d * 128), (int)(t * f.rs) + ((lane & 7) << 4));
   }
@@ -331,6 +332,7 @@ struct Fp4Part {
   uint4 rope;
 };
 
+template <bool kRope>
 __device__ __forceinline__ Fp4Part fp4_load_part(const uint8_t* raw, int d, int lane, int h) {
   Fp4Part f;
   const int u = lane + 64 * h;
@@ -343,10 +345,13 @@ __device__ __forceinline__ Fp4Part fp4_load_part(const uint8_t* raw, int d, int 
 #pragma unroll
   for (int r = 0; r < 4; ++r) f.w[r] = *reinterpret_cast<const uint32_t*>(cw + 4 * ((r + (j >> 2)) & 3));
   f.sc = *reinterpret_cast<const uint16_t*>(raw + kRawScaleBase + 8 * d * 32 + 2 * u);
-  f.rope = *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + ((lane & 31) + 32 * h) * 16);
+  if constexpr (kRope) {
+    f.rope = *reinterpret_cast<const uint4*>(raw + kRawRopeBase + 8 * d * 128 + ((lane & 31) + 32 * h) * 16);
+  }
   return f;
 }
 
+template <bool kRope>
 __device__ __forceinline__ void fp4_store_part(const Fp4Part& f, uint8_t* dst, int d, int lane, int h) {
   const int u = lane + 64 * h;
   const int t = 8 * d + (u >> 4);
@@ -362,16 +367,17 @@ __device__ __forceinline__ void fp4_store_part(const Fp4Part& f, uint8_t* dst, i
     *reinterpret_cast<uint4*>(row + (((4 * j + qd) ^ fz) << 4)) =
         make_uint4(fp4_pair<0>(wd, s), fp4_pair<1>(wd, s), fp4_pair<2>(wd, s), fp4_pair<3>(wd, s));
   }
-  if (lane < 32) {
+  if (kRope && lane < 32) {
     const int c = lane + 32 * h;
     const int tr = 8 * d + (c >> 3), ch = c & 7;
     *reinterpret_cast<uint4*>(dst + kRopeBase + (tr >> 3) * kRopeGroupBytes + ch * 128 + (tr & 7) * 16) = f.rope;
   }
 }
 
+template <bool kRope>
 __device__ __forceinline__ void fp4_decode_part(const uint8_t* raw, uint8_t* dst, int d, int lane, int h) {
-  const Fp4Part f = fp4_load_part(raw, d, lane, h);
-  fp4_store_part(f, dst, d, lane, h);
+  const Fp4Part f = fp4_load_part<kRope>(raw, d, lane, h);
+  fp4_store_part<kRope>(f, dst, d, lane, h);
 }
 
 // Lane-wise combination across lane groups: lanes l and l ^ 32 (or l ^ 16)
@@ -394,9 +400,14 @@ __device__ __forceinline__ float xor16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool kFp4, bool kLo>
+template <bool kFp4, bool kLo, bool kRope>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   using L = Lds<kFp4>;
+  // Without separate RoPE keys (a cache with no RoPE section: the rotation
+  // lives in the latent's tail), the scores run over the 512 latent channels
+  // and the tile copies skip the RoPE piece.
+  constexpr int kDma = kRope ? kDmaPerWave : kDmaPerWave - 1;
+  constexpr int kFp4Dma = kRope ? kFp4DmaPerWave : kFp4DmaPerWave - 1;
   constexpr int kRing = L::kRing;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
   __shared__ int s_tmp[kThreads / 64];
@@ -517,8 +528,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                                                          grow * 64 + 8 * g4);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qh[ks] = qa[4 * ks];
+      if constexpr (kRope) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) qh[16 + ks] = qp[4 * ks];
+        for (int ks = 0; ks < 2; ++ks) qh[16 + ks] = qp[4 * ks];
+      }
       load_lo(b);
     };
     if (rows_on) load_lo(cur.b);
@@ -529,16 +542,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       const int nrows = min(kRowsPerGroup, p.HQ - g * kRowsPerGroup);
       const int32x4_t qa =
           buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_lat) + grow0 * kLatRowBytes, nrows * kLatRowBytes);
-      const int32x4_t qp = buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_pe) + grow0 * 128, nrows * 128);
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const int r = 16 * wave + n;
         lds_copy16(qa, lds_addr(smem + L::kQBase + r * kLatRowBytes), r * kLatRowBytes + ((lane ^ (r & 15)) << 4));
       }
+      if constexpr (kRope) {
+        const int32x4_t qp = buffer_rsrc(reinterpret_cast<const uint8_t*>(p.q_pe) + grow0 * 128, nrows * 128);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int c = 2 * wave + n;
-        lds_copy16(qp, lds_addr(smem + L::kQRopeBase + c * 1024), lane * 128 + c * 16);
+        for (int n = 0; n < 2; ++n) {
+          const int c = 2 * wave + n;
+          lds_copy16(qp, lds_addr(smem + L::kQRopeBase + c * 1024), lane * 128 + c * 16);
+        }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -549,9 +564,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         qh[ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQBase + rl * kLatRowBytes +
                                                   (((4 * ks + g4) ^ (rl & 15)) << 4));
       }
+      if constexpr (kRope) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        qh[16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + rl * 16);
+        for (int ks = 0; ks < 2; ++ks) {
+          qh[16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + rl * 16);
+        }
       }
     }
     float m = -INFINITY, l = 0.0f;
@@ -588,7 +605,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
             const int ks = f >> 1, th = f & 1;
             return ks < 16 ? tb + k_off[th][ks & 3] + 256 * (ks >> 2) : tb + rope_off[th] + 512 * (ks - 16);
           };
-          constexpr int kF = 36;
+          constexpr int kF = kRope ? 36 : 32;
           constexpr int kAhead = 8;
           bf16x8 ka[kAhead];
 #pragma unroll
@@ -627,7 +644,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (dec) dp = fp4_load_part(dec_raw, wave, lane, 1);
+        if (dec) dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
 
         // ---- scale, causal limit, row max over the tile ----
         // Lane holds row rl, tokens tok0 + 16*th + i (i < 4). Raw scores; with
@@ -684,9 +701,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           mt->l[rl] = l;
         }
       } else if (dec) {
-        dp = fp4_load_part(dec_raw, wave, lane, 1);
+        dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
       }
-      if (dec) fp4_store_part(dp, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
+      if (dec) fp4_store_part<kRope>(dp, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
       if (k < count) sc.next(p);
     }
   } else {
@@ -722,11 +739,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       const int valid = bad ? 1 : min(kTile, ic.L - ic.tile * kTile);
       if constexpr (kFp4) {
         const Fp4Copy fc = fp4_copy(p.cache, r0, valid);
-        fp4_copy_pieces(fc, smem + L::kRawBase + (issued % L::kRawSlots) * kRawBytes, cq, lane);
+        fp4_copy_pieces<kRope>(fc, smem + L::kRawBase + (issued % L::kRawSlots) * kRawBytes, cq, lane);
       } else {
         const TileCopy tc = tile_copy(p.cache, r0, valid, smem + (issued % kRing) * kTileBytes);
 #pragma unroll
-        for (int n = 0; n < kDmaPerWave; ++n) tile_copy_piece(tc, cq, lane, n);
+        for (int n = 0; n < kDma; ++n) tile_copy_piece(tc, cq, lane, n);
       }
       ++issued;
       ic.next(p);
@@ -739,14 +756,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     if constexpr (kFp4) {
       if (issued < count) issue();
       if (issued == 3) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4DmaPerWave));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4Dma));
       } else if (issued == 2) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4DmaPerWave));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4Dma));
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
-      fp4_decode_part(smem + L::kRawBase, smem, cq, lane, 0);
-      fp4_decode_part(smem + L::kRawBase, smem, cq, lane, 1);
+      fp4_decode_part<kRope>(smem + L::kRawBase, smem, cq, lane, 0);
+      fp4_decode_part<kRope>(smem + L::kRawBase, smem, cq, lane, 1);
     }
     lds_barrier();  // query rows staged
 
@@ -800,7 +817,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         // stores were issued after it).
         if (k < count) {
           if (issued > k + 1 && !stored) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerWave));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma));
           } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           }
@@ -811,9 +828,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         if (k + 1 < count) {
           const int ahead = stored ? 0 : issued - (k + 2);
           if (ahead >= 2) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4DmaPerWave));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFp4Dma));
           } else if (ahead == 1) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4DmaPerWave));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFp4Dma));
           } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           }
@@ -826,7 +843,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       // copies below.
       Fp4Part dp{};
       if (kFp4 && k + 1 < count) {
-        dp = fp4_load_part(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes, cq, lane, 0);
+        dp = fp4_load_part<kRope>(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes, cq, lane, 0);
       }
       // References of tile k-1's rows, read before the copies are issued so
       // that their latency is covered.
@@ -846,7 +863,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           // The decode bounds the FP4 step, so it issues ahead of the score
           // wave on the same SIMD.
           __builtin_amdgcn_s_setprio(3);
-          fp4_store_part(dp, smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
+          fp4_store_part<kRope>(dp, smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
           __builtin_amdgcn_s_setprio(0);
         }
       } else if (issued < count) {
@@ -1181,16 +1198,23 @@ __global__ void __launch_bounds__(kMUThreads) merge_up_kernel(AttnParams p, Proj
 hipError_t launch_attn_bf16(const AttnParams& p, bool fp4_latent, const ProjParams* up, hipStream_t s) {
   const int blocks = ((p.workgroups + 7) / 8) * 8 * p.groups;
   const bool lo = p.q_lat_lo != nullptr;
+  const bool rope = p.cache.rope != nullptr;
+  const dim3 grid(blocks), block(kThreads);
+  // (latent dtype, low part of q_lat, separate RoPE keys)
   if (fp4_latent) {
     if (lo) {
-      hipLaunchKernelGGL((attn_mfma_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+      if (rope) hipLaunchKernelGGL((attn_mfma_kernel<true, true, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_mfma_kernel<true, true, false>), grid, block, 0, s, p);
     } else {
-      hipLaunchKernelGGL((attn_mfma_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+      if (rope) hipLaunchKernelGGL((attn_mfma_kernel<true, false, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_mfma_kernel<true, false, false>), grid, block, 0, s, p);
     }
   } else if (lo) {
-    hipLaunchKernelGGL((attn_mfma_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, s, p);
+    if (rope) hipLaunchKernelGGL((attn_mfma_kernel<false, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<false, true, false>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, p);
+    if (rope) hipLaunchKernelGGL((attn_mfma_kernel<false, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<false, false, false>), grid, block, 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -48,10 +48,14 @@ bool deepseek_dims(const mla_dims* d) {
   return d->d_nope == 128 && d->d_rope == 64 && d->d_v == 128 && d->d_latent == 512;
 }
 
-int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t batch) {
-  if (c == nullptr || c->latent == nullptr || c->rope == nullptr) return MLA_ERR_INVALID_ARG;
+// A cache without a RoPE section (rope NULL, rope_stride 0: the rotation
+// lives in the latent's tail) is accepted only where `no_rope_ok`.
+int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t batch, bool no_rope_ok = false) {
+  if (c == nullptr || c->latent == nullptr) return MLA_ERR_INVALID_ARG;
+  const bool no_rope = c->rope == nullptr;
+  if (no_rope && (!no_rope_ok || c->rope_stride != 0)) return MLA_ERR_INVALID_ARG;
   if (!aligned16(c->latent) || !aligned16(c->rope)) return MLA_ERR_INVALID_ARG;
-  if (c->latent_stride <= 0 || c->rope_stride <= 0 || (c->latent_stride & 15) ||
+  if (c->latent_stride <= 0 || (!no_rope && c->rope_stride <= 0) || (c->latent_stride & 15) ||
       (c->rope_stride & 15)) {
     return MLA_ERR_INVALID_ARG;
   }
@@ -69,7 +73,7 @@ int check_cache(const mla_kv_cache* c, int32_t d_latent, int32_t d_rope, int32_t
     return MLA_ERR_UNSUPPORTED;
   }
   if (c->rope_dtype != MLA_F32 && c->rope_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
-  const int64_t rope_bytes = (int64_t)d_rope * (c->rope_dtype == MLA_F32 ? 4 : 2);
+  const int64_t rope_bytes = no_rope ? 0 : (int64_t)d_rope * (c->rope_dtype == MLA_F32 ? 4 : 2);
   if (c->latent_stride < lat_bytes || c->rope_stride < rope_bytes) return MLA_ERR_INVALID_ARG;
   // Tile loads address one 64-row page with 32-bit byte offsets.
   if (c->latent_stride > mla::kMaxRowStride || c->rope_stride > mla::kMaxRowStride ||
@@ -133,7 +137,8 @@ int check_attn(const mla_dims* dims, int32_t dtype, const mla_kv_cache* cache, i
   if (hq > 1024 || dims->q_len > 16) return MLA_ERR_UNSUPPORTED;
   if (dtype == MLA_F32) {
     if (dims->d_latent % 4 || dims->d_rope % 4 || dims->d_latent > 2048) return MLA_ERR_UNSUPPORTED;
-    if (cache != nullptr && (cache->latent_dtype != MLA_F32 || cache->rope_dtype != MLA_F32)) {
+    if (cache != nullptr && (cache->latent_dtype != MLA_F32 || cache->rope_dtype != MLA_F32 ||
+                             cache->rope == nullptr)) {
       return MLA_ERR_UNSUPPORTED;
     }
   } else if (dtype == MLA_BF16) {
@@ -267,9 +272,11 @@ int prepare_decode(const mla_dims* dims, int32_t dtype, const void* q_lat, const
                    const mla_decode_opts* opts, mla::AttnParams* out) {
   int st = check_attn(dims, dtype, cache, max_seq_len, opts);
   if (st) return st;
-  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
+  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch, dtype == MLA_BF16);
   if (st) return st;
-  if (q_lat == nullptr || q_pe == nullptr || seq_lens == nullptr || x_lat == nullptr) {
+  // q_pe goes with the cache's RoPE keys: given iff the cache has them.
+  if (q_lat == nullptr || (q_pe == nullptr) != (cache->rope == nullptr) || seq_lens == nullptr ||
+      x_lat == nullptr) {
     return MLA_ERR_INVALID_ARG;
   }
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(x_lat) || !aligned16(q_lat_lo)) {
@@ -445,10 +452,14 @@ int prepare_append(const mla_dims* dims, int32_t src_dtype, const void* c_kv_new
                    bool pe_optional = false) {
   int st = check_dims(dims);
   if (st) return st;
-  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch);
+  st = check_cache(cache, dims->d_latent, dims->d_rope, dims->batch, true);
   if (st) return st;
   if (c_kv_new == nullptr || seq_lens == nullptr) return MLA_ERR_INVALID_ARG;
-  if (k_pe_new == nullptr && !pe_optional) return MLA_ERR_INVALID_ARG;
+  if (cache->rope == nullptr) {
+    if (k_pe_new != nullptr) return MLA_ERR_INVALID_ARG;  // no RoPE section to store it in
+  } else if (k_pe_new == nullptr && !pe_optional) {
+    return MLA_ERR_INVALID_ARG;
+  }
   if (!aligned16(c_kv_new) || !aligned16(k_pe_new)) return MLA_ERR_INVALID_ARG;
   if (src_dtype != MLA_F32 && src_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   if (cache->latent_dtype == MLA_FP4_E2M1_E4M3X16) {
@@ -494,6 +505,7 @@ MLA_API int mla_rope_append(const mla_dims* dims, int32_t src_dtype, const void*
   mla::AppendParams p{};
   const int st = prepare_append(dims, src_dtype, c_kv_new, k_pe_new, cache, seq_lens, &p, tail);
   if (st) return st;
+  if (!tail && cache->rope == nullptr) return MLA_ERR_INVALID_ARG;  // rotated keys need a RoPE section
   if (cos_sin == nullptr || n_pos <= 0 || !aligned16(cos_sin)) return MLA_ERR_INVALID_ARG;
   if (q_pe != nullptr && !aligned16(q_pe)) return MLA_ERR_INVALID_ARG;
   if (dims->d_rope % 2 || dims->d_rope > dims->d_latent) return MLA_ERR_UNSUPPORTED;
@@ -585,7 +597,7 @@ MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const voi
 MLA_API int mla_dequant_rows(const mla_kv_cache* cache, int32_t d_latent, const int32_t* rows,
                              int32_t n, float* out, void* stream) {
   if (d_latent <= 0 || n < 0) return MLA_ERR_INVALID_ARG;
-  int st = check_cache(cache, d_latent, 1, 0);
+  int st = check_cache(cache, d_latent, 1, 0, true);
   if (st) return st;
   if (rows == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
   return hip_status(mla::launch_dequant_rows(view_of(cache), cache->latent_dtype, d_latent, rows, n,

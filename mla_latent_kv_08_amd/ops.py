@@ -62,10 +62,12 @@ class LatentCache:
 
     Rows are physical cache rows; strides are in bytes. Build one with
     `combined` ([latent | rope] rows, the CacheCompressed layout), `fp4`
-    ([codes | scales | rope] rows) or `separate`.
+    ([codes | scales | rope] rows, or [codes | scales] without RoPE keys) or
+    `latent_only` (bf16 latent rows whose tail carries the rotation: no RoPE
+    section, rope None).
     """
     latent: torch.Tensor
-    rope: torch.Tensor
+    rope: Optional[torch.Tensor]
     latent_dtype: int
     rope_dtype: int
     latent_stride: int
@@ -94,7 +96,7 @@ class LatentCache:
             latent=_ptr(self.latent).value + self.latent_offset,
             latent_scale=(_ptr(self.latent_scale).value + self.scale_offset
                           if self.latent_scale is not None else None),
-            rope=_ptr(self.rope).value + self.rope_offset,
+            rope=_ptr(self.rope).value + self.rope_offset if self.rope is not None else None,
             latent_stride=self.latent_stride,
             scale_stride=self.scale_stride,
             rope_stride=self.rope_stride,
@@ -117,12 +119,26 @@ class LatentCache:
                            rope_offset=d_latent * es, page_table=page_table)
 
     @staticmethod
+    def latent_only(buf: torch.Tensor, d_latent: int, capacity: int,
+                    page_table: Optional[torch.Tensor] = None) -> "LatentCache":
+        """buf: [n_rows, d_latent] bf16 latent rows, no RoPE section (the DeepSeek-V4.1-Flash layout: the
+        rotation is applied to the latent's last d_rope dims)."""
+        code = _code(buf)
+        row = buf.shape[1] * buf.element_size()
+        return LatentCache(buf, None, code, code, row, 0, buf.shape[0], capacity, page_table=page_table)
+
+    @staticmethod
     def fp4(buf: torch.Tensor, d_latent: int, capacity: int,
-            page_table: Optional[torch.Tensor] = None) -> "LatentCache":
-        """buf: uint8 [n_rows, d_latent/2 + d_latent/16 + 2*d_rope]: codes | E4M3 scales | bf16 rope."""
+            page_table: Optional[torch.Tensor] = None, rope: bool = True) -> "LatentCache":
+        """buf: uint8 [n_rows, d_latent/2 + d_latent/16 + 2*d_rope]: codes | E4M3 scales | bf16 rope; with
+        rope=False, [n_rows, d_latent/2 + d_latent/16]: codes | scales (288 B for 512 dims)."""
         if buf.dtype != torch.uint8:
             raise TypeError("FP4 cache buffer must be uint8")
         row = buf.shape[1]
+        if not rope:
+            return LatentCache(buf, None, MLA_FP4_E2M1_E4M3X16, MLA_BF16, row, 0, buf.shape[0], capacity,
+                               latent_scale=buf, scale_offset=d_latent // 2, scale_stride=row,
+                               page_table=page_table)
         return LatentCache(buf, buf, MLA_FP4_E2M1_E4M3X16, MLA_BF16, row, row, buf.shape[0], capacity,
                            rope_offset=d_latent // 2 + d_latent // 16, latent_scale=buf,
                            scale_offset=d_latent // 2, scale_stride=row, page_table=page_table)
@@ -156,15 +172,16 @@ def mla_decode_workspace_size(batch: int, heads: int, q_len: int, dtype: int, ma
     return int(out.value)
 
 
-def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
+def mla_decode_attn(q_lat: torch.Tensor, q_pe: Optional[torch.Tensor], cache: LatentCache,
                     seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
                     x_lat: torch.Tensor, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, workgroups: int = 0,
                     d_nope: int = 128, d_v: int = 128, q_lat_lo: Optional[torch.Tensor] = None,
-                    stream=None) -> None:
-    """Absorbed attention over the latent cache; see mla_decode_attn in include/mla.h."""
+                    stream=None, d_rope: int = 64) -> None:
+    """Absorbed attention over the latent cache; see mla_decode_attn in include/mla.h. q_pe is None
+    exactly when the cache has no RoPE section (then d_rope only fills the dims)."""
     B, H, Q, Ckv = q_lat.shape
-    Dr = q_pe.shape[-1]
+    Dr = q_pe.shape[-1] if q_pe is not None else d_rope
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     if lse is not None and lse.dtype != torch.float32:
@@ -183,15 +200,15 @@ def mla_decode_attn(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
         "mla_decode_attn")
 
 
-def mla_decode_attn_noalloc(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
+def mla_decode_attn_noalloc(q_lat: torch.Tensor, q_pe: Optional[torch.Tensor], cache: LatentCache,
                             seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
                             x_lat: torch.Tensor, lse: Optional[torch.Tensor] = None, workgroups: int = 0,
                             d_nope: int = 128, d_v: int = 128, q_lat_lo: Optional[torch.Tensor] = None,
-                            stream=None) -> None:
+                            stream=None, d_rope: int = 64) -> None:
     """mla_decode_attn with the library's own scratch instead of a workspace; see
     mla_decode_attn_noalloc in include/mla.h."""
     B, H, Q, Ckv = q_lat.shape
-    Dr = q_pe.shape[-1]
+    Dr = q_pe.shape[-1] if q_pe is not None else d_rope
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     if lse is not None and lse.dtype != torch.float32:
@@ -238,14 +255,14 @@ def mla_prefill_attn(q_nope: torch.Tensor, q_pe: torch.Tensor, cache: LatentCach
         "mla_prefill_attn")
 
 
-def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: torch.Tensor, cache: LatentCache,
+def mla_decode_attn_up(q_lat: torch.Tensor, q_pe: Optional[torch.Tensor], cache: LatentCache,
                        seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
                        x_lat: torch.Tensor, lse: Optional[torch.Tensor], wkv_b: torch.Tensor, out: torch.Tensor,
                        workspace: Optional[torch.Tensor] = None, workgroups: int = 0,
-                       q_lat_lo: Optional[torch.Tensor] = None, stream=None) -> None:
+                       q_lat_lo: Optional[torch.Tensor] = None, stream=None, d_rope: int = 64) -> None:
     """mla_decode_attn then mla_up_proj_v on its x; see mla_decode_attn_up in include/mla.h."""
     B, H, Q, Ckv = q_lat.shape
-    Dr = q_pe.shape[-1]
+    Dr = q_pe.shape[-1] if q_pe is not None else d_rope
     Vd = out.shape[-1]
     d_nope = wkv_b.shape[1] - Vd
     if seq_lens.dtype != torch.int32:
@@ -276,11 +293,12 @@ def mla_up_proj_v(x_lat: torch.Tensor, wkv_b: torch.Tensor, out: torch.Tensor, s
                                          _ptr(out), _stream(stream)), "mla_up_proj_v")
 
 
-def mla_cache_append(c_kv_new: torch.Tensor, k_pe_new: torch.Tensor, cache: LatentCache,
-                     seq_lens: torch.Tensor, stream=None) -> None:
-    """Store the new tokens [B, Qn, Ckv] / [B, Qn, Dr] at positions len-Qn .. len-1."""
+def mla_cache_append(c_kv_new: torch.Tensor, k_pe_new: Optional[torch.Tensor], cache: LatentCache,
+                     seq_lens: torch.Tensor, stream=None, d_rope: int = 64) -> None:
+    """Store the new tokens [B, Qn, Ckv] / [B, Qn, Dr] at positions len-Qn .. len-1 (k_pe_new None for a
+    cache without a RoPE section; d_rope then only fills the dims)."""
     B, Qn, Ckv = c_kv_new.shape
-    Dr = k_pe_new.shape[-1]
+    Dr = k_pe_new.shape[-1] if k_pe_new is not None else d_rope
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     d = _dims(B, 1, Qn, 128, Dr, 128, Ckv)

@@ -226,6 +226,37 @@ def test_prefill_attn_validation(lib):
     assert call(ws=P + 8, ws_bytes=1 << 40) == E.MLA_ERR_WORKSPACE
 
 
+def test_rope_less_cache_validation(lib):
+    """A cache without a RoPE section (rope NULL, rope_stride 0) is taken by the bf16 / FP4 decode (with q_pe
+    NULL), by the append without k_pe and by the latent-tail RoPE append; everything else rejects it."""
+    E = _lib
+    byref = ctypes.byref
+    c = _cache(rope=None, rope_stride=0, latent_stride=1024)
+    d = _dims()
+    # decode: q_pe must be NULL exactly when the cache has no RoPE keys (checked before any device query)
+    assert lib.mla_decode_attn(byref(d), E.MLA_BF16, P, None, P, byref(c), P, 4096, 0.07, P, P, P, 1 << 30, None,
+                               None) == E.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_attn(byref(d), E.MLA_BF16, P, None, None, byref(_cache()), P, 4096, 0.07, P, P, P,
+                               1 << 30, None, None) == E.MLA_ERR_INVALID_ARG
+    cf = _cache(rope=None, rope_stride=0, latent_stride=2048, latent_dtype=E.MLA_F32, rope_dtype=E.MLA_F32)
+    assert lib.mla_decode_attn(byref(d), E.MLA_F32, P, None, None, byref(cf), P, 4096, 0.07, P, P, P, 1 << 30,
+                               None, None) == E.MLA_ERR_UNSUPPORTED
+    # a NULL rope with a nonzero stride is malformed
+    bad = _cache(rope=None, rope_stride=128, latent_stride=1024)
+    assert lib.mla_decode_attn(byref(d), E.MLA_BF16, P, None, None, byref(bad), P, 4096, 0.07, P, P, P, 1 << 30,
+                               None, None) == E.MLA_ERR_INVALID_ARG
+    # appends: no k_pe to store; the rotated-key append needs a RoPE section
+    assert lib.mla_cache_append(byref(d), E.MLA_BF16, P, P, byref(c), P, None) == E.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(byref(_dims(batch=0)), E.MLA_BF16, P, None, byref(c), P, None) == E.MLA_OK
+    assert lib.mla_rope_append(byref(d), E.MLA_BF16, P, None, None, P, 64, E.MLA_ROPE_HALVES, byref(c), P,
+                               None) == E.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_append(byref(_dims(batch=0)), E.MLA_BF16, P, None, None, P, 64,
+                               E.MLA_ROPE_HALVES | E.MLA_ROPE_LATENT_TAIL, byref(c), P, None) == E.MLA_OK
+    # prefill needs the RoPE keys
+    assert lib.mla_prefill_attn(byref(_dims(q_len=4)), E.MLA_BF16, P, P, byref(c), P, P, 0.1, P, None, None, 0,
+                                None) == E.MLA_ERR_INVALID_ARG
+
+
 def test_prefill_workspace_size(lib):
     """B * H * ceil(capacity / 32) tiles of 16 KiB (K [32][128] and V^T [128][32], bf16) from Q = 256 on;
     0 below (the fused path needs none)."""

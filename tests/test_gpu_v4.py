@@ -1,9 +1,11 @@
 """GPU parity of the DeepSeek-V4.1-Flash form of latent attention against the
 fp64 reference oracle/v4_ref.py, through the C ABI: mla_rope_append in
-latent-tail mode (the cache and the query rows), mla_decode_attn with an
-all-zero q_pe, then mla_sink_inverse_rope (sink column and inverse rotation
-of x's tail); and of the grouped output projection that follows it
-(mla_grouped_out_proj against v4_ref.grouped_out_proj)."""
+latent-tail mode (the cache and the query rows), mla_decode_attn, then
+mla_sink_inverse_rope (sink column and inverse rotation of x's tail); on the
+form's own rows (one 512-wide latent, no RoPE section: 1024 B bf16, 288 B
+FP4) and on DeepSeek-V3 rows with an all-zero RoPE slot and q_pe; and of the
+grouped output projection that follows it (mla_grouped_out_proj against
+v4_ref.grouped_out_proj)."""
 import math
 
 import numpy as np
@@ -11,6 +13,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import fp4_ref as F
 from oracle import rope_ref as RR
 from oracle import v4_ref as V
 from tests import mla_testlib as T
@@ -28,11 +31,16 @@ def _inputs(B, H, Q, lens, dtype, seed):
     return q, lat, sinks
 
 
-def _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups=0):
+def _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups=0, own_rows=False):
     B, H = q.shape[0], q.shape[1]
     cap = max(64, -(-max(lens) // 64) * 64)
-    buf = torch.zeros(B * cap, CKV + DR, dtype=dtype, device="cuda")
-    cache = o.LatentCache.combined(buf, CKV, cap)
+    if own_rows:
+        # The form's own rows: the 512-wide latent alone, no RoPE section.
+        buf = torch.full((B * cap, CKV), float("nan"), dtype=dtype, device="cuda")
+        cache = o.LatentCache.latent_only(buf, CKV, cap)
+    else:
+        buf = torch.zeros(B * cap, CKV + DR, dtype=dtype, device="cuda")
+        cache = o.LatentCache.combined(buf, CKV, cap)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     n = max(lens)
     hist = torch.zeros(B, n, CKV, dtype=dtype)
@@ -48,7 +56,7 @@ def _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups=0):
     o.mla_rope_append(new.cuda(), None, cache, sl, tab, style=style, q_pe=qg, latent_tail=True)
     x = torch.empty(B, H, Q, CKV, dtype=dtype, device="cuda")
     lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
-    zero_pe = torch.zeros(B, H, Q, DR, dtype=dtype, device="cuda")
+    zero_pe = None if own_rows else torch.zeros(B, H, Q, DR, dtype=dtype, device="cuda")
     scale = 1.0 / math.sqrt(CKV)
     o.mla_decode_attn(qg, zero_pe, cache, sl, n, scale, x, lse, workgroups=workgroups)
     o.mla_sink_inverse_rope(x, lse, sl, sinks.cuda(), tab, style)
@@ -57,16 +65,18 @@ def _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups=0):
 
 
 @pytest.mark.parametrize("style", [RR.INTERLEAVED, RR.HALVES])
-@pytest.mark.parametrize("dtype,Q,workgroups", [(torch.bfloat16, 1, 0), (torch.bfloat16, 2, 7),
-                                                (torch.float32, 2, 0)])
-def test_v4_form_against_oracle(style, dtype, Q, workgroups):
+@pytest.mark.parametrize("dtype,Q,workgroups,own_rows", [(torch.bfloat16, 1, 0, False), (torch.bfloat16, 2, 7, False),
+                                                         (torch.float32, 2, 0, False), (torch.bfloat16, 1, 0, True),
+                                                         (torch.bfloat16, 2, 5, True)])
+def test_v4_form_against_oracle(style, dtype, Q, workgroups, own_rows):
     o = T.ops()
     B, H = 3, 64  # the V4.1-Flash form has 64 query heads over one latent
     lens = [300, 2, 129]
     q, lat, sinks = _inputs(B, H, Q, lens, dtype, seed=31 + Q)
     table = W.rope_table(512, DR)
-    T.say(f"[case] v4 form style={style} dtype={dtype} Q={Q} lens={lens} workgroups={workgroups}")
-    x, lse, scale, _ = _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups)
+    T.say(f"[case] v4 form style={style} dtype={dtype} Q={Q} lens={lens} workgroups={workgroups} "
+          f"own_rows={own_rows}")
+    x, lse, scale, _ = _run_v4(o, q, lat, lens, sinks, table, style, dtype, Q, workgroups, own_rows)
     ref = V.decode_v4(q.double().numpy(), [r.double().numpy() for r in lat], lens, table.double().numpy(), style,
                       scale, sinks.double().numpy(), r=DR)
     tol = T.TOL["f32" if dtype == torch.float32 else "bf16"]
@@ -103,6 +113,51 @@ def test_v4_fp4_tail_quantises_the_rotated_latent():
         torch.cuda.synchronize()
         assert torch.equal(a.cpu(), bref.cpu()), f"style {style}"
         assert torch.all(f32[:, CKV:] == 0)
+
+
+@pytest.mark.parametrize("Q,paged,workgroups", [(1, False, 0), (2, True, 0), (2, False, 9)])
+def test_fp4_288_byte_rows_against_oracle(Q, paged, workgroups):
+    # Attention over the form's FP4 entry (codes | scales, 288 B, no RoPE
+    # section): the rows go in through mla_cache_append (the codec pinned bit
+    # for bit elsewhere); the oracle quantises the same fp32 rows with its own
+    # codec, and with an identity rotation table decode_v4 is plain latent
+    # attention over the dequantised rows.
+    o = T.ops()
+    B, H = 3, 64
+    lens = [300, 33, 129]
+    g = torch.Generator().manual_seed(40 + Q)
+    q = torch.randn(B, H, Q, CKV, generator=g).to(torch.bfloat16)
+    lat = [torch.randn(n, CKV, generator=g) for n in lens]
+    n = max(lens)
+    cap = -(-n // 64) * 64
+    row = o.LatentCache.fp4_row_bytes(CKV, 0)
+    assert row == 288
+    pt = None
+    if paged:
+        pages = cap // 64
+        perm = torch.randperm(B * pages, generator=g).to(torch.int32)
+        pt = perm.reshape(B, pages).cuda()
+    buf = torch.full((B * cap, row), 0xFF, dtype=torch.uint8, device="cuda")
+    cache = o.LatentCache.fp4(buf, CKV, cap, page_table=pt, rope=False)
+    hist = torch.zeros(B, n, CKV)
+    for b, rows in enumerate(lat):
+        hist[b, n - len(rows):] = rows
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o.mla_cache_append(hist.cuda(), None, cache, sl)
+    x = torch.empty(B, H, Q, CKV, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(CKV)
+    T.say(f"[case] v4 fp4 288-byte rows Q={Q} paged={paged} workgroups={workgroups}")
+    o.mla_decode_attn(q.cuda(), None, cache, sl, n, scale, x, lse, workgroups=workgroups)
+    torch.cuda.synchronize()
+    keys = []
+    for rows in lat:
+        codes, scs = F.quantize_rows_fast(rows.numpy())
+        keys.append(F.dequantize_rows(codes, scs))
+    ident = np.concatenate([np.ones((n, DR // 2)), np.zeros((n, DR // 2))], axis=1)
+    ref = V.decode_v4(q.double().numpy(), keys, lens, ident, RR.HALVES, scale, None, r=DR)
+    T.assert_close(T.to64(x), ref["x"], T.TOL["bf16"], "x")
+    T.assert_lse_close(T.to64(lse), ref["lse"], T.TOL["bf16"])
 
 
 def test_sink_inverse_rope_positions_outside_table_and_no_sink():
