@@ -83,9 +83,10 @@ def _counter_values(run_dir: str, counter: str) -> dict:
     return values
 
 
-def summarize_counters(fetch_dir: str, write_dir: str):
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str = WORKLOAD):
     """Scale FETCH_SIZE / WRITE_SIZE of the attention call by what the same counters
-    read for the calibration copy, and store the HBM bytes per launch."""
+    read for the calibration copy, and store the HBM bytes per launch (per workload:
+    profiles/attn_decode_<workload>_traffic.json)."""
     fetch = _counter_values(fetch_dir, "FETCH_SIZE")
     write = _counter_values(write_dir, "WRITE_SIZE")
 
@@ -104,12 +105,14 @@ def summarize_counters(fetch_dir: str, write_dir: str):
     copy_kib = COPY_BYTES / 1024.0
     f_factor = copy_kib / max(values(fetch, "copyBuffer"))
     w_factor = copy_kib / max(values(write, "copyBuffer"))
-    # bf16 latent (first template argument false), with or without the low part of q_lat
-    attn_f = pick(fetch, "attn_mfma_kernel<false") * 1024.0 * f_factor
-    attn_w = pick(write, "attn_mfma_kernel<false") * 1024.0 * w_factor
+    # the attention kernel of the workload's latent dtype (first template argument: FP4)
+    key = "attn_mfma_kernel<true" if workload == "mtp_fp4" else "attn_mfma_kernel<false"
+    attn_f = pick(fetch, key) * 1024.0 * f_factor
+    attn_w = pick(write, key) * 1024.0 * w_factor
     comb_f = pick(fetch, "attn_combine_kernel") * 1024.0 * f_factor
     comb_w = pick(write, "attn_combine_kernel") * 1024.0 * w_factor
     rec = {
+        "workload": workload,
         "kernel_source_hash": kernel_source_hash(),
         "hbm_bytes_per_launch": attn_f + attn_w + comb_f + comb_w,
         "attention_kernel": {"fetch_bytes": attn_f, "write_bytes": attn_w},
@@ -117,7 +120,9 @@ def summarize_counters(fetch_dir: str, write_dir: str):
         "fetch_scale": f_factor, "write_scale": w_factor,
         "calibration": f"one {COPY_BYTES} B device-to-device copy in the same process",
     }
-    with open(TRAFFIC_PATH, "w") as fh:
+    path = TRAFFIC_PATH if workload == WORKLOAD else os.path.join(ROOT, "profiles",
+                                                                 f"attn_decode_{workload}_traffic.json")
+    with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
@@ -496,10 +501,11 @@ def main():
                     help="first run one device-to-device copy of COPY_BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--calibrate-copy run into the traffic record under profiles/, then exit")
+                         "--calibrate-copy run (of --workload, else the headline) into the traffic "
+                         "record under profiles/, then exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, workload=args.workload or WORKLOAD)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
@@ -518,6 +524,13 @@ def main():
         return
     if args.workload:
         torch.cuda.set_device(dev)
+        if args.calibrate_copy:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         rec = measure_other_workloads(dev, torch.cuda.current_stream(dev), max(1, args.steps), lo=not args.no_lo,
                                       names=(args.workload,))
         print(json.dumps({"workload": args.workload, **rec[args.workload]}))

@@ -10,7 +10,9 @@
 //   online softmax over t per row r (scaled, causal limit per row)
 //   O^T[c, r] += sum_t C^T[c, t] P^T[t, r]        c over the 512 latent
 //
-// Both contractions run on bf16 matrix ops with fp32 accumulation. The eight
+// Both contractions run on bf16 matrix ops with fp32 accumulation (over an
+// FP4 latent on fp16 ones: its decoded values are exact in fp16, and the
+// query is rounded once to fp16 per row after a power-of-two scaling). The eight
 // waves of a workgroup are two per SIMD, one of each role on every SIMD, so
 // the matrix work and the softmax arithmetic are spread evenly:
 //   score waves 0..3   query rows 16w .. 16w+15 of the group over the whole
@@ -31,7 +33,7 @@
 // Tiles of 32 tokens (half a cache page) live in a ring of four LDS buffers:
 // the P.V tile, the score tile and two tiles in flight. bf16 rows are copied
 // straight into LDS by buffer loads with an LDS destination; a raw FP4 tile
-// is copied into LDS three tiles ahead and decoded to bf16 in LDS one step
+// is copied into LDS three tiles ahead and decoded to fp16 in LDS one step
 // before the score waves need it.
 // Latent row t holds its 16-byte chunk c at slot c ^ swz(t), which keeps the
 // score reads (16 tokens, one chunk each) and the transposed P.V reads (4
@@ -46,6 +48,8 @@
 // significant bits, so that the rounding that matters is x's own; lse_s fp32)
 // and merged by the combine kernel in fp32:
 //   lse = log sum_s exp(lse_s),  x = sum_s exp(lse_s - lse) x_s.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mla {
@@ -277,14 +281,15 @@ __device__ __forceinline__ void tile_copy_piece(const TileCopy& tc, int d, int l
   }
 }
 
-// FP4 tiles. P.V wave d (of four) copies and decodes tokens 8d .. 8d+7 of
-// each tile, so it only ever reads raw bytes its own copies wrote and needs
-// no barrier between copy and decode. Its four buffer-to-LDS loads per tile:
-// the codes of tokens 8d .. 8d+3 and 8d+4 .. 8d+7 (lane i: token i / 16,
-// 16-byte chunk i % 16), their RoPE keys (lane i: token i / 8, chunk i % 8)
-// and their scales (lanes 0..15: token i / 2, half i % 2). The descriptors
-// span exactly the tile's `valid` rows, so later rows read as zero (code 0
-// times scale 0).
+// FP4 tiles. P.V wave d (of four) copies tokens 8d .. 8d+7 of each tile and
+// waits for its copies before a step barrier; the score wave of the same
+// index decodes them after that barrier (the P.V wave decodes tile 0 itself,
+// from its own copies, before the first barrier). Its four buffer-to-LDS
+// loads per tile (three without RoPE keys): the codes of tokens 8d .. 8d+3
+// and 8d+4 .. 8d+7 (lane i: token i / 16, 16-byte chunk i % 16), their RoPE
+// keys (lane i: token i / 8, chunk i % 8) and their scales (lanes 0..15:
+// token i / 2, half i % 2). The descriptors span exactly the tile's `valid`
+// rows, so later rows read as zero (code 0 times scale 0).
 struct Fp4Copy {
   int32x4_t codes, scales, rope;
   uint32_t cs, ss, rs;
@@ -357,15 +362,16 @@ __device__ __forceinline__ void fp4_store_part(const Fp4Part& f, uint8_t* dst, i
   const int t = 8 * d + (u >> 4);
   const int j = u & 15;
   const float2 sv = e4m3_pair(f.sc);
+  const half2v s0 = {(_Float16)sv.x, (_Float16)sv.x}, s1 = {(_Float16)sv.y, (_Float16)sv.y};
   uint8_t* row = dst + t * kLatRowBytes;
   const int fz = swz(t);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int qd = (r + (j >> 2)) & 3;
-    const float s = (qd & 2) ? sv.y : sv.x;
+    const half2v s2 = (qd & 2) ? s1 : s0;
     const uint32_t wd = f.w[r];
-    *reinterpret_cast<uint4*>(row + (((4 * j + qd) ^ fz) << 4)) =
-        make_uint4(fp4_pair<0>(wd, s), fp4_pair<1>(wd, s), fp4_pair<2>(wd, s), fp4_pair<3>(wd, s));
+    *reinterpret_cast<uint4*>(row + (((4 * j + qd) ^ fz) << 4)) = make_uint4(
+        fp4_pair_f16<0>(wd, s2), fp4_pair_f16<1>(wd, s2), fp4_pair_f16<2>(wd, s2), fp4_pair_f16<3>(wd, s2));
   }
   if (kRope && lane < 32) {
     const int c = lane + 32 * h;
@@ -534,6 +540,51 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       load_lo(b);
     };
+    // FP4 latent: the decoded tiles hold fp16 (each E2M1 code times its E4M3
+    // scale is exact in fp16), so the latent score runs on fp16 matrix ops.
+    // The row's query (q_lat, plus q_lat_lo when given, summed in fp32) is
+    // scaled by the power of two 2^-e that brings its largest element into
+    // [2^14, 2^15) and rounded once to fp16 (11 significant bits); q_pe gets
+    // the same power of two and stays bf16 against the bf16 RoPE keys. The
+    // row's scores are then 2^-e times the true ones, and its softmax scale
+    // is c * 2^e.
+    half8 qf[kFp4 ? 16 : 1];
+    float c_row = p.scale_log2;
+    auto make_qf = [&]() {
+      if constexpr (kFp4) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < (kRope ? 18 : 16); ++ks) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float v = (float)qh[ks][j];
+            if (kLo && ks < 16) v += (float)ql[ks][j];
+            amax = fmaxf(amax, fabsf(v));
+          }
+        }
+        amax = xor32_max(xor16_max(amax));
+        const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;  // floor(log2(amax)), amax normal
+        const int e = amax > 0.0f ? min(100, max(-100, ex - 14)) : 0;
+        const float down = __uint_as_float((uint32_t)(127 - e) << 23);
+        c_row = p.scale_log2 * __uint_as_float((uint32_t)(127 + e) << 23);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float v = (float)qh[ks][j];
+            if (kLo) v += (float)ql[ks][j];
+            qf[ks][j] = (_Float16)(v * down);
+          }
+        }
+        if constexpr (kRope) {
+#pragma unroll
+          for (int ks = 16; ks < 18; ++ks) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qh[ks][j] = (__bf16)((float)qh[ks][j] * down);
+          }
+        }
+      }
+    };
     if (rows_on) load_lo(cur.b);
     {
       // Score wave w copies latent rows 16w .. 16w+15 and RoPE chunks 2w,
@@ -570,21 +621,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           qh[16 + ks] = *reinterpret_cast<const bf16x8*>(smem + L::kQRopeBase + (4 * ks + g4) * 1024 + rl * 16);
         }
       }
+      make_qf();
     }
     float m = -INFINITY, l = 0.0f;
     for (int k = 0; k <= count; ++k) {
       lds_barrier();  // step k
-      // FP4: this wave decodes the second half of P.V wave `wave`'s tokens of
-      // tile k+1 (its raw bytes landed before this step's barrier); the raw
-      // bytes are read after S, decoded at the end of the step.
+      // FP4: this wave decodes P.V wave `wave`'s tokens of tile k+1 (their raw
+      // bytes landed before this step's barrier); the raw bytes are read after
+      // S, decoded at the end of the step.
       const bool dec = kFp4 && k + 1 < count;
       constexpr int kSlots = kFp4 ? L::kRawSlots : 1;
       const uint8_t* const dec_raw = smem + L::kRawBase + ((k + 1) % kSlots) * kRawBytes;
-      Fp4Part dp{};
+      Fp4Part dp{}, dq{};
       if (rows_on && k < count) {
         if (k == 0 || sc.tile == 0) {
           // New segment (sequence sc.b).
-          if (k > 0) load_q(sc.b);
+          if (k > 0) {
+            load_q(sc.b);
+            make_qf();
+          }
           m = -INFINITY;
           l = 0.0f;
         }
@@ -617,7 +672,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           for (int f = 0; f < kF; ++f) {
             const int ks = f >> 1, th = f & 1;
             const bf16x8 a = ka[f % kAhead];
-            if constexpr (kLo) {
+            if constexpr (kFp4) {
+              if (ks < 16) {
+                acc[th][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), qf[ks],
+                                                                         acc[th][ks & 1], 0, 0, 0);
+              } else {
+                acc[th][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], acc[th][ks & 1], 0, 0, 0);
+              }
+            } else if constexpr (kLo) {
               acc[th][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], acc[th][0], 0, 0, 0);
               if (ks < 16) acc[th][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], acc[th][1], 0, 0, 0);
             } else {
@@ -630,7 +692,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           // Keep the reads kAhead fragments ahead of the matrix ops (the
           // scheduler would otherwise pull each read down to its first use):
           // kAhead reads, then per fragment its matrix ops and the next read.
-          constexpr int kMf = kLo ? 2 : 1;  // matrix ops per latent fragment
+          constexpr int kMf = kLo && !kFp4 ? 2 : 1;  // matrix ops per latent fragment
           __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
           for (int f = 0; f < 32; ++f) {
@@ -644,13 +706,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (dec) dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
+        if (dec) {
+          dq = fp4_load_part<kRope>(dec_raw, wave, lane, 0);
+          dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
+        }
 
         // ---- scale, causal limit, row max over the tile ----
         // Lane holds row rl, tokens tok0 + 16*th + i (i < 4). Raw scores; with
         // a positive scale and no masking the scale enters through the max
         // and one fused multiply-add per exponent.
-        const float c = p.scale_log2;
+        const float c = c_row;
         const int tok0 = sc.tile * kTile + 4 * g4;
         const bool whole_tile = c > 0.0f && (sc.tile + 1) * kTile <= sc.L - p.Q + 1;
         const float sc_c = whole_tile ? c : 1.0f;
@@ -676,14 +741,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         m = m_new;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         float rs = 0.0f;
-        bf16x4 pk[2];
+        // Probabilities in bf16 (fp16 over an FP4 latent, whose P.V runs on
+        // fp16 matrix ops; p <= 2^8 fits either).
+        typedef typename std::conditional<kFp4, _Float16, __bf16>::type PT;
+        typedef PT ptx4 __attribute__((ext_vector_type(4)));
+        ptx4 pk[2];
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[th][i], sc_c, -m_use));
             rs += e;
-            pk[th][i] = (__bf16)e;
+            pk[th][i] = (PT)e;
           }
         }
         l = l * alpha + xor32_sum(xor16_sum(rs));
@@ -694,16 +763,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         uint8_t* ps = ptiles + (k & 1) * kPSlotBytes + rb * 2048 + 8 * (g4 & 1) +
                       (16 * (wave & 1) + l16 + 32 * (g4 >> 1)) * 16;
 #pragma unroll
-        for (int th = 0; th < 2; ++th) *reinterpret_cast<bf16x4*>(ps + th * 1024) = pk[th];
+        for (int th = 0; th < 2; ++th) *reinterpret_cast<ptx4*>(ps + th * 1024) = pk[th];
         if (g4 == 0) {
           Meta* mt = metas + (k & 1);
           mt->m[rl] = m;
           mt->l[rl] = l;
         }
       } else if (dec) {
+        dq = fp4_load_part<kRope>(dec_raw, wave, lane, 0);
         dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
       }
-      if (dec) fp4_store_part<kRope>(dp, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
+      if (dec) {
+        fp4_store_part<kRope>(dq, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 0);
+        fp4_store_part<kRope>(dp, smem + ((k + 1) % kRing) * kTileBytes, wave, lane, 1);
+      }
       if (k < count) sc.next(p);
     }
   } else {
@@ -738,8 +811,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       const int64_t r0 = tile_row0(p.cache, ic.b, ic.tile, bad);
       const int valid = bad ? 1 : min(kTile, ic.L - ic.tile * kTile);
       if constexpr (kFp4) {
-        const Fp4Copy fc = fp4_copy(p.cache, r0, valid);
-        fp4_copy_pieces<kRope>(fc, smem + L::kRawBase + (issued % L::kRawSlots) * kRawBytes, cq, lane);
+        fp4_copy_pieces<kRope>(fp4_copy(p.cache, r0, valid), smem + L::kRawBase + (issued % L::kRawSlots) * kRawBytes,
+                               cq, lane);
       } else {
         const TileCopy tc = tile_copy(p.cache, r0, valid, smem + (issued % kRing) * kTileBytes);
 #pragma unroll
@@ -778,19 +851,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
     // Scale of O (log2 domain) for rows lane % 32 of each row block: the
     // reference it was last moved to in the segment.
     float oref[2] = {-INFINITY, -INFINITY};
-    // P.V of 16 tokens (k-step kk) of tile kt. All V fragments of the half
-    // are requested before its first matrix op, so the reads overlap each
-    // other instead of one LDS round trip per channel block. Before the
-    // first half, O moves up to the tile's reference of each row (r0, r1:
-    // row blocks 0 and 1); within a segment the reference never falls.
-    auto pv_half = [&](int kt, int kk, float r0, float r1) {
+    // P.V of 16 tokens (k-step kk) of tile kt, in two parts: pv_read requests
+    // the half's transposed V fragments and its probabilities, pv_mma (after
+    // the other work of the step has covered the reads' latency) moves O up
+    // to the tile's reference of each row before the first half (r0, r1: row
+    // blocks 0 and 1; within a segment the reference never falls) and issues
+    // the matrix ops.
+    struct PvFrags {
+      bf16x8 a[4];
+      bf16x8 p0, p1;
+    };
+    auto pv_read = [&](int kt, int kk) {
+      PvFrags f;
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
-      bf16x8 a[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
-      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(ps);
-      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+      for (int cb = 0; cb < 4; ++cb) f.a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
+      f.p0 = *reinterpret_cast<const bf16x8*>(ps);
+      f.p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
+      return f;
+    };
+    auto pv_mma = [&](const PvFrags& f, int kk, float r0, float r1) {
       if (kk == 0) {
         const bool up0 = r0 > oref[0], up1 = r1 > oref[1];
         if (__any(up0 || up1)) {
@@ -807,8 +888,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb], p0, o[cb], 0, 0, 0);
-        o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb], p1, o[4 + cb], 0, 0, 0);
+        if constexpr (kFp4) {
+          const half8 ah = __builtin_bit_cast(half8, f.a[cb]);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, __builtin_bit_cast(half8, f.p0), o[cb], 0, 0, 0);
+          o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, __builtin_bit_cast(half8, f.p1), o[4 + cb], 0, 0, 0);
+        } else {
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[cb], f.p0, o[cb], 0, 0, 0);
+          o[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[cb], f.p1, o[4 + cb], 0, 0, 0);
+        }
       }
     };
     for (int k = 0; k <= count; ++k) {
@@ -838,34 +925,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       }
       stored = false;
       lds_barrier();  // step k
-      // FP4: the raw bytes of the first half of this wave's tokens of tile k+1
-      // are read first, so that their latency is covered by the reads and
-      // copies below.
-      Fp4Part dp{};
-      if (kFp4 && k + 1 < count) {
-        dp = fp4_load_part<kRope>(smem + L::kRawBase + ((k + 1) % L::kRawSlots) * kRawBytes, cq, lane, 0);
-      }
-      // References of tile k-1's rows, read before the copies are issued so
-      // that their latency is covered.
+      // The first half of tile k-1's V fragments and probabilities, and its
+      // rows' references, are requested before the copies are issued (and,
+      // FP4, the decode is done), which cover their latency; the second half
+      // follows just before the first half's matrix ops.
       float ref[2];
+      PvFrags pf[2];
       if (k > 0) {
+        if constexpr (kFp4) pf[0] = pv_read(k - 1, 0);
         const Meta* mt = metas + ((k + 1) & 1);
         ref[0] = mt->m[lane & 31];
         ref[1] = mt->m[32 + (lane & 31)];
       }
       if constexpr (kFp4) {
-        // Raw tile k+3 goes to the slot tile k left (decoded in step k-1);
-        // then the first half of this wave's tokens of tile k+1 is decoded
-        // into the buffer tile k-2 left (the score wave of the same index
-        // decodes the other half at the end of its step).
+        // Raw tile k+3 goes to the slot tile k left (decoded in step k-1).
+        // The score wave of the same index decodes this wave's tokens of tile
+        // k+1 into the buffer tile k-2 left, at the end of its step: the P.V
+        // chain (copies and matrix ops) sets the FP4 step, the score wave
+        // waits at the barrier otherwise.
         if (issued < count) issue();
-        if (k + 1 < count) {
-          // The decode bounds the FP4 step, so it issues ahead of the score
-          // wave on the same SIMD.
-          __builtin_amdgcn_s_setprio(3);
-          fp4_store_part<kRope>(dp, smem + ((k + 1) % kRing) * kTileBytes, cq, lane, 0);
-          __builtin_amdgcn_s_setprio(0);
-        }
       } else if (issued < count) {
         // Tile k+2 goes to the buffer tile k-2 left at the end of step k-1.
         issue();
@@ -881,8 +959,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       // ahead of the score wave sharing the SIMD (FP4, whose score chain
       // sets the step, keeps them behind it).
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(2);
-      pv_half(kt, 0, ref[0], ref[1]);
-      pv_half(kt, 1, ref[0], ref[1]);
+      if constexpr (!kFp4) pf[0] = pv_read(kt, 0);
+      pf[1] = pv_read(kt, 1);
+      pv_mma(pf[0], 0, ref[0], ref[1]);
+      pv_mma(pf[1], 1, ref[0], ref[1]);
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(0);
 
       const int nt = tiles_of(pc.L);

@@ -9,6 +9,7 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -99,6 +100,19 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float s) {
   const float lo = r[0] * s;
   const float hi = r[1] * s;
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two codes (byte e of w) times scale s as two fp16 (s2 = {s, s} in fp16):
+// E2M1 values at scale 1 straight to fp16, then one packed fp16 multiply.
+// Every E4M3 value is an fp16 number, and every product of an E2M1 value
+// (2 significant bits, |v| <= 6) and an E4M3 scale (4 bits, 2^-9 .. 448)
+// has at most 5 significant bits and lies in [2^-10, 2688], inside fp16's
+// normal range: the product is exact.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+template <int e>
+__device__ __forceinline__ uint32_t fp4_pair_f16(uint32_t w, half2v s2) {
+  const half2v v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, e) * s2;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Values of E4M3 ("FN") scale bytes: subnormal m * 2^-9, normal
