@@ -226,11 +226,16 @@ def setup_attn_case(w, dev, copies: int, lo: bool = True):
             if L:
                 c[b, max_len - L:] = inp.seq_latent(b)
                 r[b, max_len - L:] = inp.seq_rope(b)
-        ops.mla_cache_append(c.to(dev), r.to(dev), first, seq_lens)
-        del c, r
+        c, r = c.to(dev), r.to(dev)
+        ops.mla_cache_append(c, r, first, seq_lens)
         caches.append(first)
+        # Further copies written by the same append (a device-to-device copy of
+        # the cache would be mistaken for the counter-calibration copy).
         for _ in range(copies - 1):
-            caches.append(ops.LatentCache.fp4(buf.clone(), w.Ckv, pl.capacity, page_table=pt))
+            more = ops.LatentCache.fp4(torch.full_like(buf, 0xFF), w.Ckv, pl.capacity, page_table=pt)
+            ops.mla_cache_append(c, r, more, seq_lens)
+            caches.append(more)
+        del c, r
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     q_lat = torch.empty(w.B, w.H, w.Q, w.Ckv, dtype=dt, device=dev)
     q_lo = torch.empty_like(q_lat) if (lo and w.dtype != "f32") else None
