@@ -255,7 +255,8 @@ def setup_attn_case(w, dev, copies: int, lo: bool = True):
 OTHER_WORKLOADS = {"tiny_f32": 1, "ragged_paged_bf16": 1, "long_splitkv_bf16": 1, "mtp_fp4": 2}
 
 
-def measure_other_workloads(dev, stream, reps: int, lo: bool = True, names=None) -> dict:
+def measure_other_workloads(dev, stream, reps: int, lo=None, names=None) -> dict:
+    """The attention call alone on each named workload; `lo` None takes the workload's own q_lat_lo setting."""
     import torch
     import workloads as W
     from mla_latent_kv_08_amd import ops
@@ -265,7 +266,7 @@ def measure_other_workloads(dev, stream, reps: int, lo: bool = True, names=None)
             continue
         w = W.WORKLOADS[name]
         print(f"bench: workload {name}", file=sys.stderr, flush=True)
-        case = setup_attn_case(w, dev, copies, lo)
+        case = setup_attn_case(w, dev, copies, w.q_lat_lo if lo is None else lo)
         inputs_sha = case["inputs_sha256"]
 
         def call(i, case=case, w=w):
@@ -485,8 +486,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (>= 3 defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workgroups", type=int, default=0)
-    ap.add_argument("--no-lo", action="store_true",
-                    help="scores against q_lat alone (rounded to bf16), without its low part q_lat_lo")
+    ap.add_argument("--lo", choices=("auto", "on", "off"), default="auto",
+                    help="pass the query's low part q_lat_lo to the scores: auto = as each workload is "
+                         "configured (spiked long context and FP4: on; headline and ragged: off)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step (and the timed attention calls) from captured HIP "
                          "graphs instead of launching the calls one by one")
@@ -509,6 +511,7 @@ def main():
                          "--calibrate-copy run (of --workload, else the headline) into the traffic "
                          "record under profiles/, then exit")
     args = ap.parse_args()
+    lo_flag = {"auto": None, "on": True, "off": False}[args.lo]
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, workload=args.workload or WORKLOAD)
         return
@@ -536,7 +539,7 @@ def main():
             dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        rec = measure_other_workloads(dev, torch.cuda.current_stream(dev), max(1, args.steps), lo=not args.no_lo,
+        rec = measure_other_workloads(dev, torch.cuda.current_stream(dev), max(1, args.steps), lo=lo_flag,
                                       names=(args.workload,))
         print(json.dumps({"workload": args.workload, **rec[args.workload]}))
         return
@@ -566,7 +569,8 @@ def main():
     c_new = inp.latent[last].reshape(B, 1, w.Ckv).contiguous().to(dev)
     r_new = inp.rope[last].reshape(B, 1, w.Dr).contiguous().to(dev)
     q_lat = torch.empty(B, H, Q, w.Ckv, dtype=torch.bfloat16, device=dev)
-    q_lo = None if args.no_lo else torch.empty_like(q_lat)
+    use_lo = w.q_lat_lo if lo_flag is None else lo_flag
+    q_lo = torch.empty_like(q_lat) if use_lo else None
     x = torch.empty_like(q_lat)
     lse = torch.empty(B, H, Q, dtype=torch.float32, device=dev)
     out = torch.empty(B, H, Q, w.Vd, dtype=torch.bfloat16, device=dev)
@@ -724,7 +728,7 @@ def main():
     # The projections against their own weight-bandwidth roofline (bf16 weights
     # read once, activations in and out once).
     wt = H * w.Dn * w.Ckv * 2
-    proj_bytes = {"append_absorb": wt + B * H * Q * (w.Dn + (1 if args.no_lo else 2) * w.Ckv) * 2
+    proj_bytes = {"append_absorb": wt + B * H * Q * (w.Dn + (2 if use_lo else 1) * w.Ckv) * 2
                   + 2 * B * Q * (w.Ckv + w.Dr) * 2,
                   "up_proj": H * w.Vd * w.Ckv * 2 + B * H * Q * (w.Ckv + w.Vd) * 2}
     attn_s = attn_avg_ms / 1e3
@@ -741,7 +745,7 @@ def main():
             calls[k].update({"alg_bytes": proj_bytes[k], "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS})
     others, context = None, None
     if not args.headline_only:
-        others = measure_other_workloads(dev, stream, max(10, args.steps), lo=not args.no_lo)
+        others = measure_other_workloads(dev, stream, max(10, args.steps), lo=lo_flag)
         others["v4_form_bf16"] = measure_v4_form(dev, stream, max(10, args.steps))
         others["prefill_bf16"] = measure_prefill(dev, stream, 20)
         context = gpu_context(dev)
@@ -769,8 +773,8 @@ def main():
                                 else ", append fused into the absorption launch")
                              + (", attention and up-projection as two calls" if args.separate_up
                                 else ", split merge fused with the up-projection"),
-                   "scores": ("q_lat (bf16) only" if args.no_lo
-                              else "q_lat + q_lat_lo (bf16 high and low parts of the fp32 absorption)"),
+                   "scores": ("q_lat + q_lat_lo (bf16 high and low parts of the fp32 absorption)" if use_lo
+                              else "q_lat (bf16, the absorption rounded once)"),
                    "inputs_sha256": inp.sha256()},
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,

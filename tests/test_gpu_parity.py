@@ -197,13 +197,14 @@ def _samples(B, H, n, seed):
     return pairs
 
 
-def _full_sampled(name, n, tol=None, workgroups=0):
+def _full_sampled(name, n, tol=None, workgroups=0, lo=None):
     w = W.WORKLOADS[name]
+    lo = w.q_lat_lo if lo is None else lo  # default: the launch bench.py times
     T.say(f"[case] full {name}: generating inputs")
     inp = W.generate(w)
     g = T.GpuCase(inp, poison=True)
-    T.say(f"[case] full {name}: running GPU path (the launch bench.py times)")
-    res = g.run(workgroups)
+    T.say(f"[case] full {name}: running GPU path, q_lat_lo={lo}")
+    res = g.run(workgroups, lo=lo)
     for k in ("x", "out"):
         assert torch.isfinite(res[k].float()).all(), k
     for b, h in _samples(w.B, w.H, n, seed=zlib.crc32(name.encode())):
@@ -212,12 +213,14 @@ def _full_sampled(name, n, tol=None, workgroups=0):
         T.compare(res, ref, w, heads=[h], batch=[b], tol=tol)
 
 
-def test_full_dsv3_bf16_sampled():
-    _full_sampled("dsv3_bf16", 16)
+@pytest.mark.parametrize("lo", [False, True])
+def test_full_dsv3_bf16_sampled(lo):
+    _full_sampled("dsv3_bf16", 16, lo=lo)
 
 
-def test_full_ragged_paged_bf16_sampled():
-    _full_sampled("ragged_paged_bf16", 8)
+@pytest.mark.parametrize("lo", [False, True])
+def test_full_ragged_paged_bf16_sampled(lo):
+    _full_sampled("ragged_paged_bf16", 8, lo=lo)
 
 
 def test_full_long_splitkv_bf16_sampled():

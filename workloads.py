@@ -47,6 +47,11 @@ class Workload:
     paged: bool = False  # 64-token pages dealt from a shuffled shared pool
     spike_frac: float = 0.0  # fraction of tokens per sequence whose latent is scaled
     spike_mult: float = 1.0
+    # Run configuration, not data: whether the timed launch passes the query's
+    # low part (q_lat_lo) to the scores. Spiked logits need it to stay within
+    # the bf16 bar; over an FP4 latent it only sharpens the query's one
+    # rounding to fp16, at no matrix-op cost.
+    q_lat_lo: bool = False
 
     @property
     def softmax_scale(self) -> float:
@@ -68,9 +73,9 @@ WORKLOADS = {
                                   paged=True),
     "long_splitkv_bf16": Workload("long_splitkv_bf16", B=4, H=128, Q=1, Dn=128, Dr=64, Vd=128,
                                   Ckv=512, dtype="bf16", seed=3, lk=131072,
-                                  spike_frac=0.01, spike_mult=8.0),
+                                  spike_frac=0.01, spike_mult=8.0, q_lat_lo=True),
     "mtp_fp4": Workload("mtp_fp4", B=128, H=128, Q=2, Dn=128, Dr=64, Vd=128, Ckv=512,
-                        dtype="fp4", seed=4, lk=8192),
+                        dtype="fp4", seed=4, lk=8192, q_lat_lo=True),
 }
 WORKLOAD_ORDER = ["tiny_f32", "dsv3_bf16", "ragged_paged_bf16", "long_splitkv_bf16", "mtp_fp4"]
 
