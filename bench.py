@@ -484,6 +484,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (>= 3 defeats the MALL)")
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps, so that the timed steps run at "
+                         "steady clocks (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workgroups", type=int, default=0)
     ap.add_argument("--lo", choices=("auto", "on", "off"), default="auto",
@@ -638,6 +641,18 @@ def main():
         else:
             step_graphs[i % ncopy].replay()
 
+    # Clock settling: the GPU's clocks ramp up over the first tens of
+    # milliseconds of sustained load, and a few warmup steps take well under a
+    # millisecond. A fixed period of the same step, untimed and before the
+    # warmup steps, lets the timed steps run at steady clocks whatever the
+    # warmup count.
+    settle_steps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        for _ in range(64):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -758,6 +773,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settle_steps,
+                   "why": "untimed steps before the warmup steps: the clocks ramp over the first tens of ms"},
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
