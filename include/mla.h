@@ -439,11 +439,13 @@ MLA_API int mla_append_absorb(const mla_dims* dims, int32_t src_dtype, const voi
 
 /*
  * mla_dequant_rows -- inspection aid: the latent of `n` physical cache rows
- * (device int32 rows[n]) as fp32 [n, Ckv]. An FP4 row is decoded by the
- * device functions the attention kernel decodes its tiles with (the hardware
- * E2M1 conversion at scale 1, one fp32 multiply by the E4M3 scale, the
- * product kept as bf16, which holds it exactly; a NaN scale gives NaN); bf16
- * and fp32 rows are widened. A row index outside [0, num_rows) gives NaN.
+ * (device int32 rows[n]) as fp32 [n, Ckv]. An FP4 row is decoded exactly:
+ * the hardware E2M1 conversion at scale 1 times the E4M3 scale (itself from
+ * the hardware FP8 conversion), in fp32 and kept as bf16, which holds every
+ * such product exactly; a NaN scale gives NaN. (The attention kernel decodes
+ * its tiles with the same conversions into fp16, which also holds every
+ * product exactly, so both give the same values.) bf16 and fp32 rows are
+ * widened. A row index outside [0, num_rows) gives NaN.
  * Lets a caller check the stored cache bit for bit (DeepSeek-V4.1-Flash
  * course page, block 4A, profiling checklist: check the FP4 dequant and the
  * scale's channel order).

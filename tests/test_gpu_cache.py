@@ -47,7 +47,8 @@ def test_fp4_append_bytes_bit_exact(paged):
     assert np.array_equal(buf[rows, :256], codes_ref)
     assert np.array_equal(buf[rows, 256:288], scales_ref)
     assert np.array_equal(buf[rows, 288:416].view(np.int16), rope.view(torch.int16).numpy())
-    # Decoded values, through fp4_pair / e4m3_value (the attention kernel's tile decode).
+    # Decoded values, through mla_dequant_rows (fp4_pair / e4m3_value; the
+    # attention kernel's own fp16 tile decode is pinned separately, below).
     out = torch.empty(n_tok, 512, dtype=torch.float32, device="cuda")
     T.ops().mla_dequant_rows(g.cache, torch.from_numpy(rows.astype(np.int32)).cuda(), out)
     torch.cuda.synchronize()
