@@ -269,7 +269,10 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
 //
 // Workspace: per (b, h) Lt = ceil(capacity / 32) tiles of 16 KiB each, tile
 // j holding K[32 tokens][128] (token-major) then V^T[128][32] (value-major),
-// bf16, tokens 32j .. 32j+31; rows past the sequence's length are zero.
+// bf16, tokens 32j .. 32j+31; rows past the sequence's length are zero. The
+// columns of V^T run in the order the score fragments of the flash-attention
+// kernel hold their tokens: within each group of 16, tokens 4..7 and 8..11
+// trade places (column 16g + 8a + 4b + c holds token 16g + 8b + 4a + c).
 // ---------------------------------------------------------------------------
 constexpr int kKvTilesPerBlock = 8;  // tiles (of 32 tokens) per block of the decompression
 constexpr int kWsTileBytes = 2 * kPfT * 128 * 2;
@@ -283,9 +286,13 @@ struct KvLds {
 
 // First physical row of tile `t0 / 32` of sequence b, or -1 for a page index
 // outside the cache (the same whole-page rule as the fused kernel).
+// The page index is read through the constant address space (a scalar load:
+// the index is uniform), so it does not wait behind the block's outstanding
+// vector loads.
 __device__ __forceinline__ int64_t pf_tile_base(const CacheView& c, int b, int t0) {
   if (c.page_size == 0) return (int64_t)b * c.capacity + t0;
-  const int page = c.page_table[(int64_t)b * c.pt_stride + t0 / kPageTokens];
+  const int page = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(c.page_table))[(int64_t)b * c.pt_stride + t0 / kPageTokens];
   const int64_t p0 = (int64_t)page * kPageTokens;
   if (page < 0 || p0 + kPageTokens > c.num_rows) return -1;
   return p0 + t0 % kPageTokens;
@@ -350,8 +357,8 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p)
       for (int i = 0; i < 16; ++i) s.k[(8 * (i >> 2) + 4 * hi + (i & 3)) * kKsPitch + n] = to_bf16(acc[i]);
     } else {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 8 * i4 + 4 * hi]) =
+      for (int i4 = 0; i4 < 4; ++i4) {  // tokens 8 i4 + 4 hi .. +3, at their permuted columns
+        *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 16 * (i4 >> 1) + 8 * hi + 4 * (i4 & 1)]) =
             make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
       }
     }
@@ -364,45 +371,56 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p)
   }
 }
 
-// Row reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15), on the
-// VALU: swap within pairs, within quads, mirror within half-rows, mirror
-// within the row; every lane ends with the row's result.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+// Lanes l and l ^ 32 combine a value; both get the same result, operands in
+// the same order (v_permlane32_swap instead of an LDS permute).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
-  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0xB1>(x);
-  x += dpp_f<0x4E>(x);
-  x += dpp_f<0x141>(x);
-  return x + dpp_f<0x140>(x);
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-constexpr int kFaQ = 128;  // queries per flash-attention block (16 per wave)
+constexpr int kFaWaves = 4;                 // waves per flash-attention block
+constexpr int kFaQ = 32 * kFaWaves;         // queries per block (32 per wave)
+constexpr int kFaThreads = 64 * kFaWaves;
+static_assert(kFaThreads == 256 && kPfT == 32, "a tile is two K, two V^T and one RoPE piece per thread");
+// The reference maximum of a query moves only when a tile's maximum passes it
+// by more than this many binary orders of magnitude, so P <= 2^8.
+constexpr float kLazyRescaleLog2 = 8.0f;
+// s_waitcnt immediate: no vector-memory operation outstanding (lgkm and exp
+// counters left alone).
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 struct FaLds {
   uint16_t k[2][kPfT * kKPitch];   // [token][128 decompressed | 64 RoPE | pad]
-  uint16_t vt[2][128 * kVPitch];   // [value dim][token]
-  uint16_t p[8][16 * kPPitch];
+  uint16_t vt[2][128 * kVPitch];   // [value dim][token, in the stored column order]
   int bad;
 };
 
-// Block of 128 queries of one (b, h), 512 threads; every wave takes 16
-// queries: S = [q_nope | q_pe] . [K | k_pe]^T (16x16x32 matrix ops, query
-// fragments in registers), scale, causal limit, online softmax, O += P V.
+// Block of kFaQ queries of one (b, h); wave w takes queries q0 + 32w .. +31,
+// lanes l and l + 32 both holding query l % 32.
+//   S^T = [K | k_pe] . [q_nope | q_pe]^T for 32 tokens x 32 queries with
+//   v_mfma_f32_32x32x16_bf16: A = key rows from LDS, B = the wave's query
+//   fragments, held in registers. Lane l gets 16 of the tile's tokens for its
+//   query and lane l ^ 32 the other 16, so a query's maximum is 15 maxima and
+//   one lane swap, and its running sum stays per lane until the end.
+//   Online softmax (log2 domain, c = softmax scale * log2 e) with a lazy
+//   rescale: the reference maximum m moves only when a tile's maximum passes
+//   it by more than 8 / c, so P = 2^(c s - c m) <= 256, and O and the sums are
+//   rescaled (wave-wide) only then.
+//   O^T += V^T P^T (v_mfma_f32_32x32x16_bf16, A = V^T rows from LDS): P^T in
+//   bf16 is the B operand as it stands in the score registers, V^T's columns
+//   being stored in that token order.
 // All threads move the next tile into the other LDS buffer (prefetched into
-// registers one tile ahead), so one barrier per tile suffices. Blocks are
-// dealt so that the query tiles of a (b, h) run on one XCD and share its L2,
-// heaviest (last) query tiles first.
-__global__ void __launch_bounds__(kPfThreads) prefill_fa_kernel(PrefillParams p) {
+// registers a tile ahead), so one barrier per tile suffices; a wave whose
+// queries see none of a tile skips its arithmetic. Blocks are dealt so that
+// the query tiles of a (b, h) run on one XCD and share its L2, heaviest (last)
+// query tiles first.
+__global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) FaLds s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
   const int nqt = (p.Q + kFaQ - 1) / kFaQ;
   const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
   const int unit = xcd + 8 * (r / nqt);
@@ -416,133 +434,159 @@ __global__ void __launch_bounds__(kPfThreads) prefill_fa_kernel(PrefillParams p)
   const int pos_max = len - Q + min(q0 + kFaQ - 1, Q - 1);
   const int n_tiles = pos_max < 0 ? 0 : min(pos_max / kPfT + 1, (len + kPfT - 1) / kPfT);
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(p.kv_ws) + ((int64_t)b * H + h) * p.Lt * kWsTileBytes;
-  const int l16 = lane & 15, g4 = lane >> 4;
 
-  // Query fragments (A operand): query q0 + 16w + l%16, dims 32ks + 8(l/16) .. +7.
-  bf16x8 qa[6];
+  // This lane's query sees positions 0 .. lim (lim = -1: none). The wave needs
+  // tiles 0 .. w_tiles - 1, and a tile ending at or before full_lim needs no
+  // mask (every query of the wave exists and sees all of it).
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + l32;
+  const int lim = qi < Q ? len - Q + qi : -1;
+  const int w_last = len - Q + min(qw + 31, Q - 1);
+  const int w_tiles = (qw >= Q || w_last < 0) ? 0 : min(w_last / kPfT + 1, n_tiles);
+  const int full_lim = qw + 31 < Q ? len - Q + qw : -1;
+
+  // Query fragments (B operand): query qi, dims 16ks + 8(l/32) .. +7 of
+  // [q_nope | q_pe].
+  bf16x8 qb[12];
   {
-    const int qi = min(q0 + 16 * wave + l16, Q - 1);
-    const int64_t row = ((int64_t)b * H + h) * Q + qi;
-    const uint16_t* qn = reinterpret_cast<const uint16_t*>(p.q_nope) + row * 128 + 8 * g4;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_pe) + row * 64 + 8 * g4;
+    const int64_t row = ((int64_t)b * H + h) * Q + min(qi, Q - 1);
+    const uint16_t* qn = reinterpret_cast<const uint16_t*>(p.q_nope) + row * 128 + 8 * hi;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q_pe) + row * 64 + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = *reinterpret_cast<const bf16x8*>(qn + 32 * ks);
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qn + 16 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qa[4 + ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+    for (int ks = 0; ks < 4; ++ks) qb[8 + ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
   }
   if (tid == 0) s.bad = 0;
 
-  // Tile moves: thread tid carries K row tid / 16 chunk tid % 16, V^T row
-  // tid / 4 chunk tid % 4 and, for tid < 256, RoPE row tid / 8 chunk tid % 8.
-  struct Tile {
-    uint4 k, v, r;
-    int bad;
-  };
+  // Tile moves, prefetched into registers: thread tid carries K rows tid / 16
+  // and 16 + tid / 16 (chunk tid % 16), V^T rows tid / 4 and 64 + tid / 4
+  // (chunk tid % 4) and RoPE row tid / 8 (chunk tid % 8).
+  uint4 nk0, nk1, nv0, nv1, nr;
+  int nbad = 0;
+  const int kof = (tid >> 4) * 256 + (tid & 15) * 16, vof = kPfT * 256 + (tid >> 2) * 64 + (tid & 3) * 16;
   auto load = [&](int tile) {
-    Tile t;
-    const uint8_t* wt = ws + (int64_t)tile * kWsTileBytes;
-    t.k = *reinterpret_cast<const uint4*>(wt + (tid >> 4) * 256 + (tid & 15) * 16);
-    t.v = *reinterpret_cast<const uint4*>(wt + kPfT * 256 + (tid >> 2) * 64 + (tid & 3) * 16);
     const int t0 = tile * kPfT;
     const int64_t base = pf_tile_base(c, b, t0);
-    t.bad = base < 0 ? 1 : 0;
-    const int rr = (tid >> 3) & 31;
-    t.r = make_uint4(0, 0, 0, 0);
-    if (tid < 256 && base >= 0 && t0 + rr < len) {
-      t.r = *reinterpret_cast<const uint4*>(c.rope + (base + rr) * c.rope_stride + (tid & 7) * 16);
+    const uint8_t* wt = ws + (int64_t)tile * kWsTileBytes;
+    nk0 = *reinterpret_cast<const uint4*>(wt + kof);
+    nk1 = *reinterpret_cast<const uint4*>(wt + kof + 16 * 256);
+    nv0 = *reinterpret_cast<const uint4*>(wt + vof);
+    nv1 = *reinterpret_cast<const uint4*>(wt + vof + 64 * 64);
+    nbad = base < 0 ? 1 : 0;
+    nr = make_uint4(0, 0, 0, 0);
+    if (base >= 0 && t0 + (tid >> 3) < len) {
+      nr = *reinterpret_cast<const uint4*>(c.rope + (base + (tid >> 3)) * c.rope_stride + (tid & 7) * 16);
     }
-    return t;
   };
-  auto store = [&](const Tile& t, int buf) {
-    *reinterpret_cast<uint4*>(&s.k[buf][(tid >> 4) * kKPitch + (tid & 15) * 8]) = t.k;
-    *reinterpret_cast<uint4*>(&s.vt[buf][(tid >> 2) * kVPitch + (tid & 3) * 8]) = t.v;
-    if (tid < 256) *reinterpret_cast<uint4*>(&s.k[buf][(tid >> 3) * kKPitch + 128 + (tid & 7) * 8]) = t.r;
-    if (t.bad) s.bad = 1;
+  uint16_t* const ks0 = &s.k[0][(tid >> 4) * kKPitch + (tid & 15) * 8];
+  uint16_t* const vs0 = &s.vt[0][(tid >> 2) * kVPitch + (tid & 3) * 8];
+  uint16_t* const rs0 = &s.k[0][(tid >> 3) * kKPitch + 128 + (tid & 7) * 8];
+  auto store = [&](int buf) {
+    *reinterpret_cast<uint4*>(ks0 + buf * kPfT * kKPitch) = nk0;
+    *reinterpret_cast<uint4*>(ks0 + buf * kPfT * kKPitch + 16 * kKPitch) = nk1;
+    *reinterpret_cast<uint4*>(vs0 + buf * 128 * kVPitch) = nv0;
+    *reinterpret_cast<uint4*>(vs0 + buf * 128 * kVPitch + 64 * kVPitch) = nv1;
+    *reinterpret_cast<uint4*>(rs0 + buf * kPfT * kKPitch) = nr;
+    if (nbad) s.bad = 1;
   };
 
-  float m[4], l[4];
-  floatx4 o[8];
+  const float cs = p.scale_log2;
+  const float thr = kLazyRescaleLog2 / cs;
+  float m = -INFINITY, mc = 0.0f, lsum = 0.0f;  // reference maximum, c m (0 while m = -inf), sum
+  floatx16 o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-  }
-#pragma unroll
-  for (int vb = 0; vb < 8; ++vb) o[vb] = floatx4{};
-  Tile nx{};
+  for (int db = 0; db < 4; ++db) o[db] = floatx16{};
   __syncthreads();  // the flag is cleared before any store can set it
-  if (n_tiles > 0) store(load(0), 0);
-  if (n_tiles > 1) nx = load(1);
+  if (n_tiles > 0) {
+    load(0);
+    store(0);
+  }
+  // The query fragments have arrived (they did on the path above): without
+  // this the compiler would wait for them inside the tile loop, behind the
+  // prefetch of the tile after next.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  if (n_tiles > 1) load(1);
   __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * kPfT;
     const int buf = tile & 1;
     // Tile+1 goes to the buffer tile-1 left (its readers passed the last
     // barrier); tile+2 is requested.
-    if (tile + 1 < n_tiles) store(nx, buf ^ 1);
-    if (tile + 2 < n_tiles) nx = load(tile + 2);
-    floatx4 sc[2] = {floatx4{}, floatx4{}};
+    if (tile + 1 < n_tiles) store(buf ^ 1);
+    if (tile + 2 < n_tiles) load(tile + 2);
+    if (tile < w_tiles) {
+      floatx16 st = floatx16{};
+      const uint16_t* kr = &s.k[buf][l32 * kKPitch + 8 * hi];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const uint16_t* kr = &s.k[buf][(16 * tb + l16) * kKPitch + 8 * g4];
-#pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], *reinterpret_cast<const bf16x8*>(kr + 32 * ks),
-                                                         sc[tb], 0, 0, 0);
+      for (int ks = 0; ks < 12; ++ks) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qb[ks], st, 0,
+                                                     0, 0);
       }
-    }
-    // S lane l: token t0 + 16tb + l%16, queries q0 + 16w + 4(l/16) + i.
-    float pr[2][4];
+      // st[i]: token t0 + 8(i/4) + 4(l/32) + i%4 for query qi.
+      if (t0 + kPfT - 1 > full_lim) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qg = q0 + 16 * wave + 4 * g4 + i;
-      const int pos = len - Q + qg;
-      float x[2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int t = t0 + 16 * tb + l16;
-        x[tb] = (qg < Q && t <= pos && t < len) ? sc[tb][i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          if (t0 + 8 * (i >> 2) + 4 * hi + (i & 3) > lim) st[i] = -INFINITY;
+        }
       }
-      const float mx = row16_max(fmaxf(x[0], x[1]));
-      const float m_new = fmaxf(m[i], mx);
-      const float alpha = m_new == m[i] ? 1.0f : __builtin_amdgcn_exp2f(m[i] - m_new);
-      const float mu = m_new == -INFINITY ? 0.0f : m_new;
-      pr[0][i] = __builtin_amdgcn_exp2f(x[0] - mu);
-      pr[1][i] = __builtin_amdgcn_exp2f(x[1] - mu);
-      l[i] = l[i] * alpha + row16_sum(pr[0][i] + pr[1][i]);
-      m[i] = m_new;
+      float mx = st[0];
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb) o[vb][i] *= alpha;
-    }
-    // P to this wave's LDS rows [query 4(l/16)+i][token 16tb + l%16], read
-    // back as the A operand (query l%16, tokens 8(l/16) .. +7).
-    uint16_t* pw = s.p[wave];
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
+      mx = pair_max(mx);
+      const bool need = mx > m + thr;
+      if (__any(need)) {
+        const float m_new = need ? mx : m;
+        const float alpha = need ? __builtin_amdgcn_exp2f((m - m_new) * cs) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) pw[(4 * g4 + i) * kPPitch + 16 * tb + l16] = to_bf16(pr[tb][i]);
-    }
-    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pw[l16 * kPPitch + 8 * g4]);
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+        lsum *= alpha;
+        m = m_new;
+        mc = m == -INFINITY ? 0.0f : m * cs;
+      }
+      bf16x8 pb[2];
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb) {
-      const bf16x8 vbk = *reinterpret_cast<const bf16x8*>(&s.vt[buf][(16 * vb + l16) * kVPitch + 8 * g4]);
-      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbk, o[vb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, -mc));
+        lsum += pv;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 va =
+              *reinterpret_cast<const bf16x8*>(&s.vt[buf][(32 * db + l32) * kVPitch + 16 * kk + 8 * hi]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[db], 0, 0, 0);
+        }
+      }
     }
     __syncthreads();
   }
   const bool bad = s.bad != 0;
   const float nanv = __uint_as_float(0x7fc00000u);
+  const float lt = pair_sum(lsum);
+  if (qi < Q) {
+    const int64_t row = ((int64_t)b * H + h) * Q + qi;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + row * 128 + 4 * hi;
+    // o[db][4a + e]: value dim 32db + 8a + 4(l/32) + e.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qg = q0 + 16 * wave + 4 * g4 + i;
-    if (qg >= Q) continue;
-    const int64_t row = ((int64_t)b * H + h) * Q + qg;
-    const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + row * 128;
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb) orow[16 * vb + l16] = to_bf16(bad ? nanv : o[vb][i] * inv);
-    if (p.lse != nullptr && l16 == 0) {
-      p.lse[row] = bad ? nanv : (l[i] > 0.0f ? (m[i] + __log2f(l[i])) * kLn2 : -INFINITY);
+      for (int a = 0; a < 4; ++a) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bad ? nanv : o[db][4 * a + e] * inv;
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * a) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+    if (p.lse != nullptr && hi == 0) {
+      p.lse[row] = bad ? nanv : (lt > 0.0f ? (mc + __log2f(lt)) * kLn2 : -INFINITY);
     }
   }
 }
@@ -563,7 +607,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
     const int64_t units = ((int64_t)p.B * p.H + 7) / 8 * 8;
     const int64_t blocks = units * ((p.Q + kFaQ - 1) / kFaQ);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(prefill_fa_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, s, p);
+    hipLaunchKernelGGL(prefill_fa_kernel, dim3((unsigned)blocks), dim3(kFaThreads), 0, s, p);
     return hipGetLastError();
   }
   const int qt = (p.Q + kPfQ - 1) / kPfQ;
