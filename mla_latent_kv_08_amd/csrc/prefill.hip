@@ -394,8 +394,8 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 struct FaLds {
-  uint16_t k[2][kPfT * kKPitch];   // [token][128 decompressed | 64 RoPE | pad]
-  uint16_t vt[2][128 * kVPitch];   // [value dim][token, in the stored column order]
+  uint16_t k[3][kPfT * kKPitch];   // [token][128 decompressed | 64 RoPE | pad]
+  uint16_t vt[3][128 * kVPitch];   // [value dim][token, in the stored column order]
   int bad;
 };
 
@@ -413,11 +413,12 @@ struct FaLds {
 //   O^T += V^T P^T (v_mfma_f32_32x32x16_bf16, A = V^T rows from LDS): P^T in
 //   bf16 is the B operand as it stands in the score registers, V^T's columns
 //   being stored in that token order.
-// All threads move the next tile into the other LDS buffer (prefetched into
-// registers a tile ahead), so one barrier per tile suffices; a wave whose
-// queries see none of a tile skips its arithmetic. Blocks are dealt so that
-// the query tiles of a (b, h) run on one XCD and share its L2, heaviest (last)
-// query tiles first.
+// Tiles pass through a ring of three LDS buffers, moved by all threads
+// (prefetched into registers a tile ahead), with one barrier per tile: the
+// matrix ops of S^T for the next tile are issued next to the exponentials of
+// the current one. A wave whose queries see none of a tile skips its
+// arithmetic. Blocks are dealt so that the query tiles of a (b, h) run on one
+// XCD and share its L2, heaviest (last) query tiles first.
 __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) FaLds s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5, l32 = lane & 31;
@@ -497,6 +498,44 @@ __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p)
   floatx16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = floatx16{};
+  // S^T of the tile in LDS buffer bi: st[i] is token t0 + 8(i/4) + 4(l/32) + i%4
+  // of that tile for query qi.
+  auto score = [&](int bi) {
+    floatx16 acc = floatx16{};
+    const uint16_t* kr = &s.k[bi][l32 * kKPitch + 8 * hi];
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qb[ks], acc, 0, 0,
+                                                    0);
+    }
+    return acc;
+  };
+  // Probabilities of st (bf16 P^T fragments) and their sum; then O^T += V^T P^T
+  // from LDS buffer bi.
+  auto prob_pv = [&](const floatx16& st, int bi) {
+    bf16x8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, -mc));
+      lsum += pv;
+      pb[i >> 3][i & 7] = (__bf16)pv;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.vt[bi][(32 * db + l32) * kVPitch + 16 * kk + 8 * hi]);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Software pipeline over a ring of three tile buffers: step k applies the
+  // mask, maximum and rescale to S^T(k) (formed in step k-1), moves tile k+1
+  // into the buffer tile k-2 left and requests tile k+2, passes the step's
+  // one barrier, then issues the matrix ops of S^T(k+1) next to the
+  // exponentials of tile k, and O^T += V^T P^T(k).
+  floatx16 st = floatx16{};
   __syncthreads();  // the flag is cleared before any store can set it
   if (n_tiles > 0) {
     load(0);
@@ -508,22 +547,12 @@ __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p)
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   if (n_tiles > 1) load(1);
   __syncthreads();
+  if (w_tiles > 0) st = score(0);
+  int bc = 0;  // buffer of tile k
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * kPfT;
-    const int buf = tile & 1;
-    // Tile+1 goes to the buffer tile-1 left (its readers passed the last
-    // barrier); tile+2 is requested.
-    if (tile + 1 < n_tiles) store(buf ^ 1);
-    if (tile + 2 < n_tiles) load(tile + 2);
+    const int bn = bc == 2 ? 0 : bc + 1;  // buffer of tile k+1 (held tile k-2)
     if (tile < w_tiles) {
-      floatx16 st = floatx16{};
-      const uint16_t* kr = &s.k[buf][l32 * kKPitch + 8 * hi];
-#pragma unroll
-      for (int ks = 0; ks < 12; ++ks) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qb[ks], st, 0,
-                                                     0, 0);
-      }
-      // st[i]: token t0 + 8(i/4) + 4(l/32) + i%4 for query qi.
       if (t0 + kPfT - 1 > full_lim) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -547,24 +576,18 @@ __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p)
         m = m_new;
         mc = m == -INFINITY ? 0.0f : m * cs;
       }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, -mc));
-        lsum += pv;
-        pb[i >> 3][i & 7] = (__bf16)pv;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(&s.vt[buf][(32 * db + l32) * kVPitch + 16 * kk + 8 * hi]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], o[db], 0, 0, 0);
-        }
-      }
     }
+    if (tile + 1 < n_tiles) store(bn);
+    if (tile + 2 < n_tiles) load(tile + 2);
     __syncthreads();
+    if (tile + 1 < w_tiles) {
+      const floatx16 sn = score(bn);
+      prob_pv(st, bc);
+      st = sn;
+    } else if (tile < w_tiles) {
+      prob_pv(st, bc);
+    }
+    bc = bn;
   }
   const bool bad = s.bad != 0;
   const float nanv = __uint_as_float(0x7fc00000u);
