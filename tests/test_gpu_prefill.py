@@ -6,8 +6,9 @@ V formed once into a workspace, then flash attention; Q >= 256).
 
 Cases span several query tiles with a ragged last one, several 32-token
 chunks with a ragged tail, sequences shorter than Q (leading queries that see
-nothing: out 0, lse -inf), Q = 1, the paged layout and the contiguous one; and, at the two sizes bench.py
-times, in the launch configuration it times, sampled (sequence, head) pairs."""
+nothing: out 0, lse -inf), Q = 1, the paged layout and the contiguous one; planted logit jumps that
+move the running maximum mid-sequence, on both paths; and, at the two sizes bench.py times, in the launch
+configuration it times, sampled (sequence, head) pairs."""
 import math
 
 import numpy as np
@@ -93,6 +94,41 @@ def test_prefill_two_kernel_against_oracle(B, H, Q, lens, paged):
     out_f, lse_f = _run(inp, case=case)
     T.assert_close(T.to64(out), T.to64(out_f), T.TOL["bf16"], "two-kernel vs fused")
     T.assert_lse_close(T.to64(lse), T.to64(lse_f), T.TOL["bf16"])
+
+
+# Planted logit jumps (log2 domain) through the RoPE stream: every query's
+# q_pe carries a * u (u a unit vector) and the RoPE keys of chosen tokens carry
+# lam * u on top of their noise, so those tokens' logits sit about
+# scale * log2(e) * a * lam above the rest. Jumps of more than 2^8 at a token
+# a query reaches mid-sequence make the flash-attention kernel move its
+# reference maximum and rescale O (and the fused kernel its running max);
+# levels up to 2^120 leave the earlier weights to underflow. Inputs are
+# bf16-exact, so the fp64 oracle sees exactly the values the kernels read.
+JUMPS = [(100, 600, 12.0), (250, 600, 40.0), (301, 302, 60.0), (330, 331, 9.0), (420, 600, 120.0)]
+
+
+@pytest.mark.parametrize("two", [True, False])
+def test_prefill_planted_score_jumps(two):
+    w = W.reduced(W.WORKLOADS["dsv3_bf16"], 1, [600], seed=31).with_(H=3, Q=300)
+    inp = W.generate(w)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(w.Dr)
+    u /= np.linalg.norm(u)
+    a = 4.0
+    per_unit = w.softmax_scale * math.log2(math.e) * a
+    q_pe = a * u + 0.05 * rng.standard_normal((w.B, w.H, w.Q, w.Dr))
+    lam = np.zeros(600)
+    for t0, t1, level in JUMPS:
+        lam[t0:t1] = level / per_unit
+    rope = inp.rope.float().numpy() * 0.3 + lam[:, None] * u[None, :]
+    inp.q_pe = torch.from_numpy(q_pe.astype(np.float32)).to(inp.q_pe.dtype)
+    inp.rope = torch.from_numpy(rope.astype(np.float32)).to(inp.rope.dtype)
+    T.say(f"[case] prefill planted jumps B=1 H=3 Q=300 len=600 two_kernel={two}")
+    case = T.GpuCase(inp, poison=True)
+    out, lse = _run(inp, two_kernel=two, case=case)
+    ref = T.oracle(inp)
+    T.assert_close(T.to64(out), ref["out"], T.TOL["bf16"], "out")
+    T.assert_lse_close(T.to64(lse), ref["lse"], T.TOL["bf16"])
 
 
 def test_prefill_two_kernel_bad_page_gives_nan():
