@@ -17,7 +17,9 @@
 //      rows from LDS, B = its weight fragments;
 //   3. waves 0..3 each take 16 queries: S = [q_nope | q_pe] . [K | k_pe]^T over
 //      192 dims (v_mfma_f32_16x16x32_bf16), scale, causal limit, online softmax
-//      (fp32 running max and sum per query), P in bf16 through LDS, O += P V.
+//      (fp32 reference max and sum per query, row reductions by DPP, the
+//      reference moved only on a jump past 2^8), P in bf16 through LDS,
+//      O += P V.
 // Query j of a sequence with `len` cached tokens (the Q new ones included) sees
 // positions 0 .. len - Q + j. A query that sees nothing gets out = 0 and
 // lse = -inf; a page index outside the cache makes the block's outputs NaN.
@@ -35,6 +37,9 @@ constexpr int kKPitch = 200;    // key row pitch: 128 decompressed + 64 RoPE + p
 constexpr int kVPitch = 40;     // transposed value row pitch: 32 tokens + pad
 constexpr int kPPitch = 40;     // probability row pitch: 32 tokens + pad
 constexpr float kLn2 = 0.69314718055994530942f;
+// The reference maximum of a query moves only when a tile's maximum passes it
+// by more than this many binary orders of magnitude, so P <= 2^8.
+constexpr float kLazyRescaleLog2 = 8.0f;
 
 struct PrefillLds {
   uint16_t q[kPfQ * kKPitch];
@@ -46,6 +51,26 @@ struct PrefillLds {
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)f32_to_bf16_bits(v); }
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15) on the VALU:
+// swap within pairs, within quads, mirror within half-rows, mirror within the
+// row; every lane ends with the row's result.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));      // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));      // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));     // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x + dpp_f<0x140>(x);
+}
 
 __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) PrefillLds s;
@@ -193,7 +218,11 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
         }
       }
       // S lane l: token t0 + 16tb + l%16, queries q0 + 16w + 4(l/16) + i.
-      float pr[2][4];
+      // Online softmax with a lazy rescale: a row's reference maximum moves
+      // only when the tile's maximum passes it by more than 2^8, so P <= 2^8
+      // and O is rescaled (wave-wide) only then.
+      float pr[2][4], alpha[4];
+      bool moved = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qg = q0 + 16 * wave + 4 * g4 + i;
@@ -204,11 +233,10 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
           const int t = t0 + 16 * tb + l16;
           x[tb] = (qg < Q && t <= pos && t < len) ? sc[tb][i] * p.scale_log2 : -INFINITY;
         }
-        float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 16));
-        const float m_new = fmaxf(m[i], mx);
-        const float alpha = m_new == m[i] ? 1.0f : __builtin_amdgcn_exp2f(m[i] - m_new);
+        const float mx = row16_max(fmaxf(x[0], x[1]));
+        const float m_new = mx > m[i] + kLazyRescaleLog2 ? mx : m[i];
+        alpha[i] = m_new == m[i] ? 1.0f : __builtin_amdgcn_exp2f(m[i] - m_new);
+        moved |= m_new != m[i];
         const float mu = m_new == -INFINITY ? 0.0f : m_new;
         float rs = 0.0f;
 #pragma unroll
@@ -216,12 +244,15 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
           pr[tb][i] = __builtin_amdgcn_exp2f(x[tb] - mu);
           rs += pr[tb][i];
         }
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) rs += __shfl_xor(rs, d, 16);
-        l[i] = l[i] * alpha + rs;
+        l[i] = l[i] * alpha[i] + row16_sum(rs);
         m[i] = m_new;
+      }
+      if (__any(moved)) {
 #pragma unroll
-        for (int vb = 0; vb < 8; ++vb) o[vb][i] *= alpha;
+        for (int vb = 0; vb < 8; ++vb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[vb][i] *= alpha[i];
+        }
       }
       // P to this wave's LDS rows [query 4(l/16)+i][token 16tb + l%16], then
       // read back as the A operand (query l%16, tokens 8(l/16) .. +7).
@@ -229,7 +260,9 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) pw[(4 * g4 + i) * kPPitch + 16 * tb + l16] = to_bf16(pr[tb][i]);
+        for (int tb = 0; tb < 2; ++tb) {
+          pw[(4 * g4 + i) * kPPitch + 16 * tb + l16] = __builtin_bit_cast(uint16_t, (__bf16)pr[tb][i]);
+        }
       }
       const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pw[l16 * kPPitch + 8 * g4]);
 #pragma unroll
@@ -386,9 +419,6 @@ constexpr int kFaWaves = 4;                 // waves per flash-attention block
 constexpr int kFaQ = 32 * kFaWaves;         // queries per block (32 per wave)
 constexpr int kFaThreads = 64 * kFaWaves;
 static_assert(kFaThreads == 256 && kPfT == 32, "a tile is two K, two V^T and one RoPE piece per thread");
-// The reference maximum of a query moves only when a tile's maximum passes it
-// by more than this many binary orders of magnitude, so P <= 2^8.
-constexpr float kLazyRescaleLog2 = 8.0f;
 // s_waitcnt immediate: no vector-memory operation outstanding (lgkm and exp
 // counters left alone).
 constexpr int kVmcntZero = (7 << 4) | (15 << 8);
