@@ -51,6 +51,11 @@ struct PrefillLds {
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)f32_to_bf16_bits(v); }
+// Two values to a bf16 pair by the hardware conversion (round to nearest even,
+// as f32_to_bf16_bits for every finite value).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
 
 // Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15) on the VALU:
 // swap within pairs, within quads, mirror within half-rows, mirror within the
@@ -176,26 +181,41 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
     __syncthreads();
     // ---- 2. decompress: D[token][n] = sum_k C[token][k] W[n][k] for this wave's 32 rows n ----
     {
+      // K (waves 0..3) is formed transposed, D = W C^T, so that a lane holds
+      // runs of 4 dims of one token (8-byte stores into the token-major key
+      // rows); V (waves 4..7) as D = C W^T, runs of 4 tokens of one dim for
+      // the value-major V^T. The operand layouts are the same either way.
       floatx16 acc = floatx16{};
       const uint16_t* a = &s.c[buf][(lane & 31) * kCPitch + 8 * hi];
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0,
-                                                      0, 0);
-        // Keep the LDS reads within groups of 8 k-steps: hoisting all of them
-        // would need another 128 registers.
-        if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-      }
-      // D lane l: column n = 32(w%4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
-      const int n = 32 * (wave & 3) + (lane & 31);
       if (wave < 4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s.k[buf][(8 * (i >> 2) + 4 * hi + (i & 3)) * kKPitch + n] = to_bf16(acc[i]);
+        for (int ks = 0; ks < 32; ++ks) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], *reinterpret_cast<const bf16x8*>(a + 16 * ks), acc, 0,
+                                                        0, 0);
+          // Keep the LDS reads within groups of 8 k-steps: hoisting all of
+          // them would need another 128 registers.
+          if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        // D lane l: token l%32, dims 32w + 8(i/4) + 4(l/32) + i%4.
+        uint16_t* kd = &s.k[buf][(lane & 31) * kKPitch + 32 * wave + 4 * hi];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          *reinterpret_cast<uint2*>(kd + 8 * a4) =
+              make_uint2(bf16_pair(acc[4 * a4], acc[4 * a4 + 1]), bf16_pair(acc[4 * a4 + 2], acc[4 * a4 + 3]));
+        }
       } else {
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0,
+                                                        0, 0);
+          if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        // D lane l: dim n = 32(w-4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
+        const int n = 32 * (wave & 3) + (lane & 31);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 8 * i4 + 4 * hi]) =
-              make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+              make_uint2(bf16_pair(acc[4 * i4], acc[4 * i4 + 1]), bf16_pair(acc[4 * i4 + 2], acc[4 * i4 + 3]));
         }
       }
     }
@@ -375,24 +395,37 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p)
     for (int j = 0; j < 4; ++j) *reinterpret_cast<bf16x8*>(&s.c[(r0 + 8 * j) * kCPitch + cc * 8]) = v[j];
     if (tile + 1 < tile1) load(tile + 1, v);
     __syncthreads();
+    // K transposed (D = W C^T: runs of 4 dims of one token per lane), V as
+    // D = C W^T (runs of 4 tokens of one dim), as in the fused kernel.
     floatx16 acc = floatx16{};
     const uint16_t* a = &s.c[(lane & 31) * kCPitch + 8 * hi];
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0, 0,
-                                                    0);
-      if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-    }
-    // D lane l: column n = 32(w%4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
-    const int n = 32 * (wave & 3) + (lane & 31);
     if (wave < 4) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s.k[(8 * (i >> 2) + 4 * hi + (i & 3)) * kKsPitch + n] = to_bf16(acc[i]);
+      for (int ks = 0; ks < 32; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], *reinterpret_cast<const bf16x8*>(a + 16 * ks), acc, 0, 0,
+                                                      0);
+        if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+      // D lane l: token l%32, dims 32w + 8(i/4) + 4(l/32) + i%4.
+      uint16_t* kd = &s.k[(lane & 31) * kKsPitch + 32 * wave + 4 * hi];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        *reinterpret_cast<uint2*>(kd + 8 * a4) =
+            make_uint2(bf16_pair(acc[4 * a4], acc[4 * a4 + 1]), bf16_pair(acc[4 * a4 + 2], acc[4 * a4 + 3]));
+      }
     } else {
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a + 16 * ks), wf[ks], acc, 0, 0,
+                                                      0);
+        if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+      // D lane l: dim n = 32(w-4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
+      const int n = 32 * (wave & 3) + (lane & 31);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {  // tokens 8 i4 + 4 hi .. +3, at their permuted columns
         *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 16 * (i4 >> 1) + 8 * hi + 4 * (i4 & 1)]) =
-            make_uint2(pack_bf16x2(acc[4 * i4], acc[4 * i4 + 1]), pack_bf16x2(acc[4 * i4 + 2], acc[4 * i4 + 3]));
+            make_uint2(bf16_pair(acc[4 * i4], acc[4 * i4 + 1]), bf16_pair(acc[4 * i4 + 2], acc[4 * i4 + 3]));
       }
     }
     __syncthreads();
