@@ -15,11 +15,11 @@
 //   2. every wave forms its 32 x 32 slice of K (token-major) or V (stored
 //      transposed, value-major) with v_mfma_f32_32x32x16_bf16, A = the latent
 //      rows from LDS, B = its weight fragments;
-//   3. waves 0..3 each take 16 queries: S = [q_nope | q_pe] . [K | k_pe]^T over
-//      192 dims (v_mfma_f32_16x16x32_bf16), scale, causal limit, online softmax
-//      (fp32 reference max and sum per query, row reductions by DPP, the
-//      reference moved only on a jump past 2^8), P in bf16 through LDS,
-//      O += P V.
+//   3. waves 0..3 each take 16 queries: S^T = [K | k_pe] . [q_nope | q_pe]^T
+//      over 192 dims (v_mfma_f32_16x16x32_bf16), scale, causal limit, online
+//      softmax (fp32 reference max per query, moved only on a jump past 2^8;
+//      sums per lane), and O^T += V^T P^T with P^T in bf16 straight from the
+//      score registers (V^T's columns are stored in their token order).
 // Query j of a sequence with `len` cached tokens (the Q new ones included) sees
 // positions 0 .. len - Q + j. A query that sees nothing gets out = 0 and
 // lse = -inf; a page index outside the cache makes the block's outputs NaN.
@@ -35,7 +35,6 @@ static_assert(kPageTokens % kPfT == 0, "a tile never crosses a page");
 constexpr int kCPitch = 520;    // latent row pitch in LDS (bf16)
 constexpr int kKPitch = 200;    // key row pitch: 128 decompressed + 64 RoPE + pad
 constexpr int kVPitch = 40;     // transposed value row pitch: 32 tokens + pad
-constexpr int kPPitch = 40;     // probability row pitch: 32 tokens + pad
 constexpr float kLn2 = 0.69314718055994530942f;
 // The reference maximum of a query moves only when a tile's maximum passes it
 // by more than this many binary orders of magnitude, so P <= 2^8.
@@ -46,7 +45,6 @@ struct PrefillLds {
   uint16_t c[2][kPfT * kCPitch];
   uint16_t k[2][kPfT * kKPitch];
   uint16_t vt[128 * kVPitch];
-  uint16_t p[4][16 * kPPitch];
   int bad;
 };
 
@@ -57,24 +55,25 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15) on the VALU:
-// swap within pairs, within quads, mirror within half-rows, mirror within the
-// row; every lane ends with the row's result.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+// Lanes l and l ^ 16 (or l ^ 32) combine a value; both get the same result,
+// operands in the same order (v_permlane16_swap / v_permlane32_swap instead
+// of an LDS permute). Two of them combine the four lanes l % 16 + 16g of a
+// column of the 16 x 16 result layouts.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(x));      // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f<0x4E>(x));      // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0x141>(x));     // row_half_mirror
-  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0xB1>(x);
-  x += dpp_f<0x4E>(x);
-  x += dpp_f<0x141>(x);
-  return x + dpp_f<0x140>(x);
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
@@ -108,14 +107,14 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   }
   const int l16 = lane & 15, g4 = lane >> 4;
   if (tid == 0) s.bad = 0;
-  // Rows of this lane in the 16 x 16 result layouts: queries 4*(l/16) + i.
-  float m[4], l[4];
+  // Attention waves 0..3: lane l takes query qg = q0 + 16w + l%16 (in every
+  // 16 x 16 result layout below the query is the column), which sees
+  // positions 0 .. lim (lim = -1: none). Its reference maximum, its sum (per
+  // lane; the four lanes of a query are added at the end) and O^T columns.
+  const int qg = q0 + 16 * wave + l16;
+  const int lim = qg < Q ? len - Q + qg : -1;
+  float m = -INFINITY, lsum = 0.0f;
   floatx4 o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-  }
 #pragma unroll
   for (int vb = 0; vb < 8; ++vb) o[vb] = floatx4{};
 
@@ -211,10 +210,14 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
           if ((ks & 7) == 7) __builtin_amdgcn_sched_barrier(0);
         }
         // D lane l: dim n = 32(w-4) + l%32, tokens 8(i/4) + 4(l/32) + i%4.
+        // V^T's columns run in the order the attention waves hold their
+        // probabilities: column 8g + j is token 4g + j for j < 4 and token
+        // 16 + 4g + j - 4 otherwise, so tokens 8 i4 + 4 hi .. +3 go to column
+        // 8 (2 (i4 % 2) + hi) + 4 (i4 / 2).
         const int n = 32 * (wave & 3) + (lane & 31);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 8 * i4 + 4 * hi]) =
+          *reinterpret_cast<uint2*>(&s.vt[n * kVPitch + 8 * (2 * (i4 & 1) + hi) + 4 * (i4 >> 1)]) =
               make_uint2(bf16_pair(acc[4 * i4], acc[4 * i4 + 1]), bf16_pair(acc[4 * i4 + 2], acc[4 * i4 + 3]));
         }
       }
@@ -224,71 +227,63 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
     if (wave >= 4) {
       if (tile + 1 < n_tiles) fetch(t0 + kPfT, buf ^ 1);
     } else {
+      // S^T = [K | k_pe] . [q_nope | q_pe]^T for the tile's two 16-token
+      // halves tb (A = key rows, B = query rows, both from LDS: token or
+      // query l%16, dims 32ks + 8(l/16) .. +7).
       floatx4 sc[2] = {floatx4{}, floatx4{}};
-      // A lane l: query q0 + 16w + l%16, dims 32ks + 8(l/16) .. +7.
       const uint16_t* qr = &s.q[(16 * wave + l16) * kKPitch + 8 * g4];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const uint16_t* kr = &s.k[buf][(16 * tb + l16) * kKPitch + 8 * g4];
 #pragma unroll
         for (int ks = 0; ks < 6; ++ks) {
-          sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qr + 32 * ks),
-                                                           *reinterpret_cast<const bf16x8*>(kr + 32 * ks), sc[tb], 0,
+          sc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(kr + 32 * ks),
+                                                           *reinterpret_cast<const bf16x8*>(qr + 32 * ks), sc[tb], 0,
                                                            0, 0);
         }
       }
-      // S lane l: token t0 + 16tb + l%16, queries q0 + 16w + 4(l/16) + i.
-      // Online softmax with a lazy rescale: a row's reference maximum moves
-      // only when the tile's maximum passes it by more than 2^8, so P <= 2^8
-      // and O is rescaled (wave-wide) only then.
-      float pr[2][4], alpha[4];
-      bool moved = false;
+      // sc[tb][i]: token t0 + 16tb + 4(l/16) + i for query qg. Online softmax
+      // with a lazy rescale: the reference maximum moves only when the tile's
+      // maximum passes it by more than 2^8, so P <= 2^8, and O is rescaled
+      // (wave-wide) only then. The query's maximum over its four lanes by two
+      // lane swaps.
+      float x[2][4];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qg = q0 + 16 * wave + 4 * g4 + i;
-        const int pos = len - Q + qg;
-        float x[2];
+      for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int t = t0 + 16 * tb + l16;
-          x[tb] = (qg < Q && t <= pos && t < len) ? sc[tb][i] * p.scale_log2 : -INFINITY;
-        }
-        const float mx = row16_max(fmaxf(x[0], x[1]));
-        const float m_new = mx > m[i] + kLazyRescaleLog2 ? mx : m[i];
-        alpha[i] = m_new == m[i] ? 1.0f : __builtin_amdgcn_exp2f(m[i] - m_new);
-        moved |= m_new != m[i];
-        const float mu = m_new == -INFINITY ? 0.0f : m_new;
-        float rs = 0.0f;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          pr[tb][i] = __builtin_amdgcn_exp2f(x[tb] - mu);
-          rs += pr[tb][i];
-        }
-        l[i] = l[i] * alpha[i] + row16_sum(rs);
-        m[i] = m_new;
-      }
-      if (__any(moved)) {
-#pragma unroll
-        for (int vb = 0; vb < 8; ++vb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[vb][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) {
+          x[tb][i] = t0 + 16 * tb + 4 * g4 + i <= lim ? sc[tb][i] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, x[tb][i]);
         }
       }
-      // P to this wave's LDS rows [query 4(l/16)+i][token 16tb + l%16], then
-      // read back as the A operand (query l%16, tokens 8(l/16) .. +7).
-      uint16_t* pw = s.p[wave];
+      mx = xor32_max(xor16_max(mx));
+      const float m_new = mx > m + kLazyRescaleLog2 ? mx : m;
+      if (__any(m_new != m)) {
+        const float alpha = m_new == m ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int vb = 0; vb < 8; ++vb) o[vb] *= alpha;
+        lsum *= alpha;
+      }
+      m = m_new;
+      const float mu = m == -INFINITY ? 0.0f : m;
+      // P^T is the B operand of O^T += V^T P^T as it stands: lane l holds
+      // k-steps 8(l/16) .. +7 = tokens 4(l/16) + 0..3 and 16 + 4(l/16) + 0..3,
+      // the order of V^T's columns.
+      bf16x8 pb;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          pw[(4 * g4 + i) * kPPitch + 16 * tb + l16] = __builtin_bit_cast(uint16_t, (__bf16)pr[tb][i]);
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(x[tb][i] - mu);
+          lsum += pv;
+          pb[4 * tb + i] = (__bf16)pv;
         }
       }
-      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pw[l16 * kPPitch + 8 * g4]);
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb) {
-        const bf16x8 vbk = *reinterpret_cast<const bf16x8*>(&s.vt[(16 * vb + l16) * kVPitch + 8 * g4]);
-        o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vbk, o[vb], 0, 0, 0);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.vt[(16 * vb + l16) * kVPitch + 8 * g4]);
+        o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[vb], 0, 0, 0);
       }
     }
   }
@@ -296,17 +291,21 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillParams p) {
   if (wave < 4) {
     const bool bad = s.bad != 0;
     const float nanv = __uint_as_float(0x7fc00000u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qg = q0 + 16 * wave + 4 * g4 + i;
-      if (qg >= Q) continue;
+    const float lt = xor32_sum(xor16_sum(lsum));
+    if (qg < Q) {
       const int64_t row = ((int64_t)b * H + h) * Q + qg;
-      const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + row * 128;
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      // o[vb][i]: value dim 16vb + 4(l/16) + i of query qg.
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + row * 128 + 4 * g4;
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb) orow[16 * vb + l16] = to_bf16(bad ? nanv : o[vb][i] * inv);
-      if (p.lse != nullptr && l16 == 0) {
-        p.lse[row] = bad ? nanv : (l[i] > 0.0f ? (m[i] + __log2f(l[i])) * kLn2 : -INFINITY);
+      for (int vb = 0; vb < 8; ++vb) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = bad ? nanv : o[vb][i] * inv;
+        *reinterpret_cast<uint2*>(orow + 16 * vb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+      if (p.lse != nullptr && g4 == 0) {
+        p.lse[row] = bad ? nanv : (lt > 0.0f ? (m + __log2f(lt)) * kLn2 : -INFINITY);
       }
     }
   }
@@ -435,17 +434,6 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p)
     *reinterpret_cast<uint4*>(wt + kPfT * 256 + (tid >> 2) * 64 + (tid & 3) * 16) =
         *reinterpret_cast<const uint4*>(&s.vt[(tid >> 2) * kVPitch + (tid & 3) * 8]);
   }
-}
-
-// Lanes l and l ^ 32 combine a value; both get the same result, operands in
-// the same order (v_permlane32_swap instead of an LDS permute).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 constexpr int kFaWaves = 4;                 // waves per flash-attention block
@@ -625,7 +613,7 @@ __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p)
       float mx = st[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
-      mx = pair_max(mx);
+      mx = xor32_max(mx);
       const bool need = mx > m + thr;
       if (__any(need)) {
         const float m_new = need ? mx : m;
@@ -654,7 +642,7 @@ __global__ void __launch_bounds__(kFaThreads) prefill_fa_kernel(PrefillParams p)
   }
   const bool bad = s.bad != 0;
   const float nanv = __uint_as_float(0x7fc00000u);
-  const float lt = pair_sum(lsum);
+  const float lt = xor32_sum(lsum);
   if (qi < Q) {
     const int64_t row = ((int64_t)b * H + h) * Q + qi;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
