@@ -13,8 +13,9 @@
 // of 32 cached tokens:
 //   1. the latent rows go to LDS; the RoPE keys go straight to the key tile;
 //   2. every wave forms its 32 x 32 slice of K (token-major) or V (stored
-//      transposed, value-major) with v_mfma_f32_32x32x16_bf16, A = the latent
-//      rows from LDS, B = its weight fragments;
+//      transposed, value-major) with v_mfma_f32_32x32x16_bf16 from the latent
+//      rows in LDS and its weight fragments (K as W C^T, so that a lane holds
+//      runs of dims of one token; V as C W^T, runs of tokens of one dim);
 //   3. waves 0..3 each take 16 queries: S^T = [K | k_pe] . [q_nope | q_pe]^T
 //      over 192 dims (v_mfma_f32_16x16x32_bf16), scale, causal limit, online
 //      softmax (fp32 reference max per query, moved only on a jump past 2^8;
