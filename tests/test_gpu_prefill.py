@@ -181,8 +181,8 @@ def test_prefill_bad_page_gives_nan_and_rejects_fp32():
                            w.softmax_scale, out.float())
 
 
-@pytest.mark.parametrize("B,Q,L,heads,batch,two", [(8, 64, 4096, [0, 77], [0, 5], False),
-                                                   (1, 4096, 4096, [3, 100], [0], True)])
+@pytest.mark.parametrize("B,Q,L,heads,batch,two", [(8, 64, 4096, [0, 31, 77, 127], [0, 3, 5, 7], False),
+                                                   (1, 4096, 4096, [0, 3, 17, 41, 64, 88, 100, 127], [0], True)])
 def test_prefill_full_size_sampled(B, Q, L, heads, batch, two):
     # The two prefill shapes bench.py times (H = 128), in the same launch
     # configuration (chunked: fused; full: two kernels); the oracle evaluates
