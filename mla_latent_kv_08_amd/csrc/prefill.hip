@@ -40,6 +40,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // The reference maximum of a query moves only when a tile's maximum passes it
 // by more than this many binary orders of magnitude, so P <= 2^8.
 constexpr float kLazyRescaleLog2 = 8.0f;
+// s_waitcnt immediate: no vector-memory operation outstanding (lgkm and exp
+// counters left alone).
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 struct PrefillLds {
   uint16_t q[kPfQ * kKPitch];
@@ -389,6 +392,10 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kv_kernel(PrefillParams p)
   };
   bf16x8 v[4];
   load(tile0, v);
+  // The weight fragments and the first tile have arrived: without this the
+  // compiler carries their pending state into the loop and, at the top of
+  // each step, waits for the previous step's stores along with the tile.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   for (int tile = tile0; tile < tile1; ++tile) {
     __syncthreads();  // the previous tile's readers and copies are done
 #pragma unroll
@@ -441,9 +448,6 @@ constexpr int kFaWaves = 4;                 // waves per flash-attention block
 constexpr int kFaQ = 32 * kFaWaves;         // queries per block (32 per wave)
 constexpr int kFaThreads = 64 * kFaWaves;
 static_assert(kFaThreads == 256 && kPfT == 32, "a tile is two K, two V^T and one RoPE piece per thread");
-// s_waitcnt immediate: no vector-memory operation outstanding (lgkm and exp
-// counters left alone).
-constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 struct FaLds {
   uint16_t k[3][kPfT * kKPitch];   // [token][128 decompressed | 64 RoPE | pad]
