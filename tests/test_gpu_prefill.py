@@ -75,6 +75,7 @@ CASES_TWO = [
     (2, 2, 257, (600, 257), True),
     (2, 2, 400, (100, 450), False),
     (1, 1, 256, (256,), True),
+    (1, 2, 300, (2000,), True),  # a long history before the new tokens
 ]
 
 
