@@ -1100,16 +1100,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
 //     attention kernel; xq is read back only if `need_x`.
 // The run plan (each sequence's first tile in run order) was left by the
 // attention kernel.
+// What the merge of sequence b reads before its partials: its length and the
+// run plan's entries for it and for the end. The three reads leave together
+// (the empty statement makes the compiler fetch both pointers first). With a
+// sequence per lane group (kScalarEnd), the end entry, the same for every
+// row, is a scalar read, so that no vector wait is needed to move it to a
+// scalar register.
+struct MergeMeta {
+  int len_raw, cum_b, total_tiles;
+};
+template <bool kScalarEnd>
+__device__ __forceinline__ MergeMeta merge_meta(const AttnParams& p, int b) {
+  asm volatile("" : : "s"(p.plan), "s"(p.seq_lens));
+  MergeMeta mm;
+  mm.len_raw = load_ro(p.seq_lens, b);
+  mm.cum_b = p.plan[b];
+  mm.total_tiles = kScalarEnd ? load_ro(p.plan, p.B) : p.plan[p.B];
+  return mm;
+}
+
 template <int L>
-__device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, int j, bool need_x,
-                                          uint4 xq[64 / L]) {
+__device__ __forceinline__ void merge_row(const AttnParams& p, const MergeMeta& mm, int b, int row, int j,
+                                          bool need_x, uint4 xq[64 / L]) {
   constexpr int kC = 64 / L;  // 16-byte chunks per lane
   const int g = row / kRowsPerGroup;
   const int row_local = row % kRowsPerGroup;
   const int64_t grow = (int64_t)b * p.HQ + row;
   uint16_t* xo = reinterpret_cast<uint16_t*>(p.x_lat) + grow * p.Ckv;
   const int c0 = 8 * j;
-  const int nb = tiles_of(seq_len(p, b));
+  // The run plan is read together with the length (it is written for every
+  // sequence, empty ones included), so the partials' addresses are known
+  // after one round trip instead of two. (The empty statement keeps the
+  // reads ahead of the branch.)
+  asm volatile("" : : "v"(mm.len_raw), "v"(mm.cum_b), "v"(mm.total_tiles));
+  const int cum_b = mm.cum_b, total_tiles = mm.total_tiles;
+  const int nb = tiles_of(clamp_len(mm.len_raw, p.cache.capacity));
   if (nb == 0) {
 #pragma unroll
     for (int k = 0; k < kC; ++k) {
@@ -1119,8 +1144,6 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, int b, int row, i
     if (p.lse != nullptr && j == 0) p.lse[grow] = -INFINITY;
     return;
   }
-  const int cum_b = p.plan[b];
-  const int total_tiles = p.plan[p.B];
   const int per = (total_tiles + p.workgroups - 1) / p.workgroups;
   const int i_first = cum_b / per;
   const int i_last = (cum_b + nb - 1) / per;
@@ -1215,14 +1238,17 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(AttnParam
   const int row = (blockIdx.y >> 2) * kRowsPerGroup + (blockIdx.y & 3) * 16 + (threadIdx.x >> 4);
   if (row >= p.HQ) return;
   uint4 xq[4];
-  merge_row<16>(p, blockIdx.x, row, threadIdx.x & 15, false, xq);
+  merge_row<16>(p, merge_meta<false>(p, blockIdx.x), blockIdx.x, row, threadIdx.x & 15, false, xq);
 }
 
 // The merge and the up-projection out[b,h,q,:] = W_UV[h] x[b,h,q,:] in one
 // launch. Block (h, y) takes query rows 16y .. 16y+15 of head h (rows ordered
-// m = b * Q + q). Wave w first requests its W_UV slice (value columns
-// 16w .. 16w+15, all 512 latent channels: 64 registers a lane), so that
-// those loads are in flight during the merge; the merged (or whole) x rows,
+// m = b * Q + q). Each row's first merge reads (length, run plan) leave
+// first; then wave w requests its W_UV slice (value columns 16w .. 16w+15,
+// all 512 latent channels: 64 registers a lane), which stays in flight
+// during the merge (vector loads complete in issue order, so a wait for the
+// merge reads issued after the slice would wait for the slice too, and the
+// merge's two round trips would queue behind it); the merged (or whole) x rows,
 // 32 lanes a row, go to x_lat and to LDS as bf16; then the wave forms out^T
 // for its 16 columns by v_mfma_f32_16x16x32_bf16 (A = the W_UV slice,
 // B = the x rows from LDS) with fp32 accumulation.
@@ -1238,15 +1264,22 @@ __global__ void __launch_bounds__(kMUThreads) merge_up_kernel(AttnParams p, Proj
   // A lane l: W_UV row 16w + l % 16, channels 32ks + 8(l / 16) .. +7.
   const uint16_t* wv = reinterpret_cast<const uint16_t*>(u.w) +
                        ((int64_t)h * (u.Dn + u.Vd) + u.Dn + 16 * wave + (lane & 15)) * u.Ckv + 8 * quad;
+  const int r = tid >> 5;
+  const int mr = m0 + r;  // this thread's merge row
+  const MergeMeta mm = merge_meta<true>(p, min(mr, M - 1) / p.Q);
+  __builtin_amdgcn_sched_barrier(0);
   bf16x8 a[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wv + 32 * ks);
+  __builtin_amdgcn_sched_barrier(0);
+  // (The merge reads are used here, after the slice's loads, so that the
+  // compiler keeps them ahead of the slice instead of sinking them into the
+  // merge's branch; the wait here leaves the slice in flight.)
+  asm volatile("" : : "v"(mm.len_raw), "v"(mm.cum_b), "v"(mm.total_tiles));
   {
-    const int r = tid >> 5;
-    const int m = m0 + r;
     uint4 xq[2];
-    if (m < M) {
-      merge_row<32>(p, m / p.Q, h * p.Q + m % p.Q, tid & 31, true, xq);
+    if (mr < M) {
+      merge_row<32>(p, mm, mr / p.Q, h * p.Q + mr % p.Q, tid & 31, true, xq);
     } else {
       xq[0] = xq[1] = make_uint4(0, 0, 0, 0);
     }
