@@ -226,8 +226,11 @@ def replay(B, H, Q, lens, fp4=False, paged=False, page_table=None, num_rows=None
                     part_lse.check(part_lse.lo + (prow0 + r) * 4, 4, "partial lse")
                 first = False
                 seg_lo = 0
-    # merge: each split sequence's partial rows
+    # merge: every sequence's run-plan entries (read with its length, empty
+    # sequences included), then each split sequence's partial rows
     for b in range(B):
+        plan.check(plan.lo + 4 * b, 4, "merge plan read")
+        plan.check(plan.lo + 4 * B, 4, "merge plan end read")
         nb = ntiles[b]
         if nb == 0:
             continue
