@@ -406,20 +406,6 @@ __device__ __forceinline__ float xor16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max(a, b) as the median of (a, b, +inf): one instruction, where fmaxf
-// adds a NaN-quieting step per operand. With a NaN operand the result may
-// be the other operand; a NaN score still turns its probability and the
-// row sum into NaN.
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
-__device__ __forceinline__ float xor32_max2(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_max2(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 template <bool kFp4, bool kLo, bool kRope>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
   using L = Lds<kFp4>;
@@ -741,9 +727,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
             for (int i = 0; i < 4; ++i) s[th][i] = tok0 + kHalf * th + i < vis ? s[th][i] * c : -INFINITY;
           }
         }
-        float mx = max2(max2(max2(s[0][0], s[0][1]), max2(s[0][2], s[0][3])),
-                        max2(max2(s[1][0], s[1][1]), max2(s[1][2], s[1][3])));
-        mx = xor32_max2(xor16_max2(mx));
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = xor32_max(xor16_max(mx));
         if (whole_tile) mx *= c;
 
         // ---- online softmax in the log2 domain ----
@@ -754,25 +740,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
         const float alpha = m_new == m ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        float rs = 0.0f;
         // Probabilities in bf16 (fp16 over an FP4 latent, whose P.V runs on
         // fp16 matrix ops; p <= 2^8 fits either).
         typedef typename std::conditional<kFp4, _Float16, __bf16>::type PT;
         typedef PT ptx4 __attribute__((ext_vector_type(4)));
         ptx4 pk[2];
-        float e8[8];
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            e8[4 * th + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[th][i], sc_c, -m_use));
-            pk[th][i] = (PT)e8[4 * th + i];
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[th][i], sc_c, -m_use));
+            rs += e;
+            pk[th][i] = (PT)e;
           }
         }
-        // The row sum stays a per-lane partial (the lanes of a row share
-        // alpha); it is summed over the row's lanes only at the segment's
-        // last tile, the one whose sum the P.V waves read.
-        l = l * alpha + (((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7])));
-        const bool seg_last = sc.tile == tiles_of(sc.L) - 1 || k == count - 1;
+        l = l * alpha + xor32_sum(xor16_sum(rs));
         // Probabilities in the P.V B-operand layout [rb][kk][lane]: k-step
         // kk = th covers that half's tokens; lane L holds row L % 32 of the
         // block, tokens 8 * (L / 32) .. +7, so this lane's 4 tokens go to lane
@@ -781,12 +764,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
                       (16 * (wave & 1) + l16 + 32 * (g4 >> 1)) * 16;
 #pragma unroll
         for (int th = 0; th < 2; ++th) *reinterpret_cast<ptx4*>(ps + th * 1024) = pk[th];
-        Meta* mt = metas + (k & 1);
-        if (seg_last) {
-          const float l_row = xor32_sum(xor16_sum(l));
-          if (g4 == 0) mt->l[rl] = l_row;
+        if (g4 == 0) {
+          Meta* mt = metas + (k & 1);
+          mt->m[rl] = m;
+          mt->l[rl] = l;
         }
-        if (g4 == 0) mt->m[rl] = m;
       } else if (dec) {
         dq = fp4_load_part<kRope>(dec_raw, wave, lane, 0);
         dp = fp4_load_part<kRope>(dec_raw, wave, lane, 1);
@@ -883,14 +865,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       PvFrags f;
       const uint8_t* tb = smem + (kt % kRing) * kTileBytes + 16384 * kk;
       const uint8_t* ps = ptiles + (kt & 1) * kPSlotBytes + kk * 1024 + lane * 16;
-      // LDS reads return in issue order: the probabilities first, then the
-      // V fragments in the order the matrix ops take them, so each matrix op
-      // waits only for the reads it uses.
-      f.p0 = *reinterpret_cast<const bf16x8*>(ps);
-      f.p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) f.a[cb] = join(tr_read(tb + tr_off[0][cb]), tr_read(tb + tr_off[1][cb]));
+      f.p0 = *reinterpret_cast<const bf16x8*>(ps);
+      f.p1 = *reinterpret_cast<const bf16x8*>(ps + 2048);
       return f;
     };
     auto pv_mma = [&](const PvFrags& f, int kk, float r0, float r1) {
@@ -982,11 +960,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnParams p) {
       // sets the step, keeps them behind it).
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(2);
       if constexpr (!kFp4) pf[0] = pv_read(kt, 0);
-      // The halves' reads stay in order (first half, then second), so the
-      // first half's matrix ops start once its own fragments have landed.
-      __builtin_amdgcn_sched_barrier(0);
       pf[1] = pv_read(kt, 1);
-      __builtin_amdgcn_sched_barrier(0);
       pv_mma(pf[0], 0, ref[0], ref[1]);
       pv_mma(pf[1], 1, ref[0], ref[1]);
       if constexpr (!kFp4) __builtin_amdgcn_s_setprio(0);
