@@ -66,3 +66,33 @@ def test_noalloc_rejects_oversized_workspace():
     assert e.value.status == _lib.MLA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.count_nonzero(x.float()) == 0  # nothing was enqueued
+
+
+def test_noalloc_full_headline_equals_workspace():
+    # The launch bench.py times (B=32, H=128, 4096 tokens each, default split):
+    # its workspace fits the library's scratch, and the scratch call gives the
+    # workspace call's bits; then a smaller reduced call on the same scratch.
+    o = T.ops()
+    w = W.WORKLOADS["dsv3_bf16"]
+    T.say(f"[case] noalloc full {w.name}")
+    inp = W.generate(w)
+    g = T.GpuCase(inp)
+    need = o.mla_decode_workspace_size(w.B, w.H, w.Q, o.MLA_BF16, g.max_len)
+    assert need <= _lib.MLA_NOALLOC_SCRATCH_BYTES
+    q_lat = torch.empty(w.B, w.H, w.Q, w.Ckv, dtype=torch.bfloat16, device="cuda")
+    o.mla_absorb_q(g.q_nope, g.wkv_b, q_lat)
+    res = []
+    for noalloc in (False, True):
+        x = torch.full((w.B, w.H, w.Q, w.Ckv), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((w.B, w.H, w.Q), float("nan"), dtype=torch.float32, device="cuda")
+        call = o.mla_decode_attn_noalloc if noalloc else o.mla_decode_attn
+        call(q_lat, g.q_pe, g.cache, g.seq_lens, g.max_len, w.softmax_scale, x, lse)
+        torch.cuda.synchronize()
+        res.append((x, lse))
+    (x0, l0), (x1, l1) = res
+    assert torch.isfinite(x1.float()).all()
+    assert torch.equal(x0.view(torch.int16), x1.view(torch.int16)), "x differs from the workspace call"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "lse differs from the workspace call"
+    del g, q_lat, res, x0, x1
+    torch.cuda.empty_cache()
+    _both([300, 65], 0)
