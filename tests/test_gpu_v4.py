@@ -160,6 +160,60 @@ def test_fp4_288_byte_rows_against_oracle(Q, paged, workgroups):
     T.assert_lse_close(T.to64(lse), ref["lse"], T.TOL["bf16"])
 
 
+def _v4_samples(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = [(0, 0), (B - 1, H - 1)]
+    while len(pairs) < n:
+        p = (int(rng.integers(0, B)), int(rng.integers(0, H)))
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_v4_full_size_sampled(fp4):
+    # The size and launch the benchmark times for the form (B=32, 64 heads,
+    # 4096 tokens each, Q=1, the form's own rows, default split): bf16 rows
+    # through the whole chain (latent-tail RoPE append, attention, sink and
+    # inverse rotation); 288-byte FP4 rows through the plain append and the
+    # attention, against decode_v4 over the oracle codec's rows with an
+    # identity rotation. Eight (sequence, head) pairs against the fp64 oracle.
+    o = T.ops()
+    B, H, Q, L = 32, 64, 1, 4096
+    lens = [L] * B
+    q, lat, sinks = _inputs(B, H, Q, lens, torch.float32 if fp4 else torch.bfloat16, seed=77)
+    q = q.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(CKV)
+    T.say(f"[case] v4 full size fp4={fp4}")
+    if not fp4:
+        table = W.rope_table(L, DR)
+        x, lse, scale, _ = _run_v4(o, q, lat, lens, sinks, table, RR.INTERLEAVED, torch.bfloat16, Q, 0, True)
+    else:
+        row = o.LatentCache.fp4_row_bytes(CKV, 0)
+        buf = torch.full((B * L, row), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = o.LatentCache.fp4(buf, CKV, L, rope=False)
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        o.mla_cache_append(torch.stack(lat).cuda(), None, cache, sl)
+        x = torch.empty(B, H, Q, CKV, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, H, Q, dtype=torch.float32, device="cuda")
+        o.mla_decode_attn(q.cuda(), None, cache, sl, L, scale, x, lse)
+        torch.cuda.synchronize()
+    assert torch.isfinite(x.float()).all()
+    xs, ls = T.to64(x), T.to64(lse)
+    for b, h in _v4_samples(B, H, 8, seed=123 + int(fp4)):
+        T.say(f"  sample b={b} h={h}")
+        qs = q[b:b + 1, h:h + 1].double().numpy()
+        if not fp4:
+            ref = V.decode_v4(qs, [lat[b].double().numpy()], [L], W.rope_table(L, DR).double().numpy(),
+                              RR.INTERLEAVED, scale, sinks[h:h + 1].double().numpy(), r=DR)
+        else:
+            codes, scs = F.quantize_rows_fast(lat[b].numpy())
+            ident = np.concatenate([np.ones((L, DR // 2)), np.zeros((L, DR // 2))], axis=1)
+            ref = V.decode_v4(qs, [F.dequantize_rows(codes, scs)], [L], ident, RR.HALVES, scale, None, r=DR)
+        T.assert_close(xs[b:b + 1, h:h + 1], ref["x"], T.TOL["bf16"], f"x b={b} h={h}")
+        T.assert_lse_close(ls[b:b + 1, h:h + 1], ref["lse"], T.TOL["bf16"])
+
+
 def test_sink_inverse_rope_positions_outside_table_and_no_sink():
     o = T.ops()
     B, H, Q = 2, 4, 2
