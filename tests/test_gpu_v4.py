@@ -235,7 +235,7 @@ def test_sink_inverse_rope_positions_outside_table_and_no_sink():
     T.assert_close(xr[0, :, 1], ref, 1e-2, "tail turned back")
 
 
-@pytest.mark.parametrize("B,H,Q,G,N", [(3, 64, 2, 8, 1024), (20, 16, 2, 4, 64)])
+@pytest.mark.parametrize("B,H,Q,G,N", [(3, 64, 2, 8, 1024), (20, 16, 2, 4, 64), (32, 64, 1, 8, 1024)])
 def test_grouped_out_proj_against_oracle(B, H, Q, G, N):
     o = T.ops()
     g = torch.Generator().manual_seed(B * 100 + H)
